@@ -1,0 +1,262 @@
+"""Plain float64 oracle functions (test infrastructure only; see package doc).
+
+Layouts are token-major (NHWC): activations [B,H,W,C]; a patch is the row band
+[row0, row0+rows) of that, [B,rows,W,C]; token t = row*W + col; head h owns
+channels [h*D, (h+1)*D).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+
+def _f64(a) -> np.ndarray:
+    return np.asarray(a, dtype=np.float64)
+
+
+# ------------------------------------------------------------------ bf16 storage
+def bf16_round(a) -> np.ndarray:
+    """Round to the nearest bf16 value (ties to even), returned as float64.
+
+    A bf16 value is a float32 whose low 16 mantissa bits are zero.  The value
+    is first rounded to float32 (nearest-even), then its float32 bit pattern u
+    is rounded at bit 16: add 0x7FFF plus the lowest kept bit, drop 16 bits.
+    Used where a bf16 configuration stores a layer output (reading R6)."""
+    f = np.ascontiguousarray(np.asarray(a, dtype=np.float64).astype(np.float32))
+    u = f.view(np.uint32).astype(np.uint64)
+    keep_lsb = (u >> np.uint64(16)) & np.uint64(1)
+    r = ((u + np.uint64(0x7FFF) + keep_lsb) >> np.uint64(16)) << np.uint64(16)
+    out = r.astype(np.uint32).view(np.float32).astype(np.float64)
+    return out.reshape(np.shape(a))
+
+
+# ------------------------------------------------------------------ a1: splice
+def splice(full, patch, row0: int) -> np.ndarray:
+    """Full-image buffer with rows [row0, row0+rows) replaced by the patch.
+
+    One device's local stand-in for gathering every patch's output and
+    concatenating along the height axis into the reused full-image buffer
+    (DistriFusion architecture article, communication section).  Exact: the
+    result holds the input values unchanged (returned as a new array of the
+    input dtype)."""
+    full = np.asarray(full)
+    patch = np.asarray(patch)
+    rows = patch.shape[1]
+    out = full.copy()
+    out[:, row0:row0 + rows] = patch
+    return out
+
+
+# ------------------------------------------------------------------ a2: GroupNorm
+def patch_sums(x_patch, G: int) -> np.ndarray:
+    """Raw group sums of a patch: [B,G,2] = (sum x, sum x^2) over the patch's
+    rows, all columns and the C/G channels of group g (reading R2)."""
+    x = _f64(x_patch)
+    B, R, W, C = x.shape
+    xg = x.reshape(B, R * W, G, C // G)
+    s1 = xg.sum(axis=(1, 3))
+    s2 = (xg * xg).sum(axis=(1, 3))
+    return np.stack([s1, s2], axis=-1)
+
+
+def groupnorm_stale(x_patch, stale_stats, gamma, beta, H: int, G: int, p: int, eps: float = 1e-5):
+    """GroupNorm of patch p with statistics of the spliced image (reading R2).
+
+    x_patch [B,R,W,C]; stale_stats [B,P,G,2] raw sums of each patch from the
+    previous step (slot p is ignored; may be None when P == 1); gamma, beta [C].
+    Group statistics: totals T_k = sum_{q != p} stale_stats[:, q, g, k] + the
+    fresh sums of x_patch; n = H*W*C/G; mean = T_1/n; var = max(T_2/n - mean^2,
+    0).  y = (x - mean)/sqrt(var + eps) * gamma_c + beta_c.
+    Returns (y [B,R,W,C] float64, fresh sums [B,G,2] float64).
+    Module: DistriGroupNorm (DistriFusion architecture article, normalisation
+    section); stale reuse: DistriFusion reading notes, Introduction fourth
+    paragraph."""
+    x = _f64(x_patch)
+    B, R, W, C = x.shape
+    cg = C // G
+    fresh = patch_sums(x, G)
+    total = fresh.copy()
+    if stale_stats is not None:
+        st = _f64(stale_stats)
+        P = st.shape[1]
+        for q in range(P):
+            if q != p:
+                total += st[:, q]
+    n = float(H * W * cg)
+    mean = total[..., 0] / n                           # [B,G]
+    var = np.maximum(total[..., 1] / n - mean * mean, 0.0)
+    rstd = 1.0 / np.sqrt(var + eps)
+    mean_c = np.repeat(mean, cg, axis=1)[:, None, None, :]   # [B,1,1,C]
+    rstd_c = np.repeat(rstd, cg, axis=1)[:, None, None, :]
+    y = (x - mean_c) * rstd_c * _f64(gamma) + _f64(beta)
+    return y, fresh
+
+
+# ------------------------------------------------------------------ a3: conv with halos
+def _halo_band(x_patch, stale_full, row0: int) -> np.ndarray:
+    """Rows [row0-1, row0+rows] of the spliced image, zero-padded by one at
+    every image border: [B, rows+2, W+2, Cin].  The interior rows are the fresh
+    patch; the two halo rows come from the stale image (reading R3: neighbours'
+    fresh rows of this step are never available)."""
+    x = _f64(x_patch)
+    B, R, W, Cin = x.shape
+    if stale_full is None:
+        S = x
+        H = R
+        if row0 != 0:
+            raise ValueError("stale image required for a partial band")
+    else:
+        S = splice(_f64(stale_full), x, row0)   # spliced image S_p (reading R1)
+        H = S.shape[1]
+    band = np.zeros((B, R + 2, W + 2, Cin))
+    for i in range(R + 2):
+        r = row0 - 1 + i
+        if 0 <= r < H:
+            band[:, i, 1:W + 1] = S[:, r]
+    return band
+
+
+def conv3x3_halo(x_patch, stale_full, weight, bias, row0: int) -> np.ndarray:
+    """3x3 conv (stride 1, zero pad 1) of the spliced image, output rows of the
+    patch only: y[b,i,w,o] = bias[o] + sum_{dy,dx in 0..2} sum_c
+    weight[o,dy,dx,c] * Spad[b, row0+i+dy, w+dx, c], where Spad is the spliced
+    image padded by one zero row/column on every side.
+    x_patch [B,R,W,Cin]; stale_full [B,H,W,Cin] (None when the patch is the
+    whole image); weight [Cout,3,3,Cin]; bias [Cout] or None.
+    Module: DistriConv2dPP (DistriFusion architecture article, conv section);
+    computing only the own region: DistriFusion reading notes, Introduction
+    fourth paragraph."""
+    band = _halo_band(x_patch, stale_full, row0)
+    B, R2, W2, Cin = band.shape
+    R, W = R2 - 2, W2 - 2
+    wt = _f64(weight)
+    Cout = wt.shape[0]
+    y = np.zeros((B, R, W, Cout))
+    for dy in range(3):
+        for dx in range(3):
+            tap = band[:, dy:dy + R, dx:dx + W, :]           # [B,R,W,Cin]
+            y += tap @ wt[:, dy, dx, :].T
+    if bias is not None:
+        y += _f64(bias)
+    return y
+
+
+def conv3x3_halo_sampled(x_patch, stale_full, weight, bias, row0: int, b_idx, i_idx, w_idx) -> np.ndarray:
+    """conv3x3_halo evaluated only at output positions (b, i, w) of the patch:
+    returns [n, Cout].  Same definition, one output pixel at a time."""
+    band = _halo_band(x_patch, stale_full, row0)
+    wt = _f64(weight)
+    Cout = wt.shape[0]
+    wflat = wt.reshape(Cout, -1)                               # (dy, dx, c) order
+    b_idx, i_idx, w_idx = (np.asarray(v, dtype=np.int64) for v in (b_idx, i_idx, w_idx))
+    out = np.empty((len(b_idx), Cout))
+    for n, (b, i, w) in enumerate(zip(b_idx, i_idx, w_idx)):
+        nb = band[b, i:i + 3, w:w + 3, :].reshape(-1)          # (dy, dx, c) order
+        out[n] = wflat @ nb
+    if bias is not None:
+        out += _f64(bias)
+    return out
+
+
+# ------------------------------------------------------------------ a4: displaced attention
+def self_attn_displaced(q, k, v, heads: int, scale: float | None = None, rows=None, block: int = 256) -> np.ndarray:
+    """Per batch b and head h: O = softmax(scale Q_h K_h^T) V_h over all keys.
+
+    q [B,Nq,heads*D] (the patch's queries); k, v [B,N,heads*D] (the spliced
+    full-image buffer: fresh own rows, stale elsewhere); scale defaults to
+    1/sqrt(D) (reading R4).  rows: optional (b_idx, q_idx) to evaluate only
+    those query tokens (returns [n, heads*D]); else returns [B,Nq,heads*D].
+    Queries are independent, so they are evaluated in groups of `block`.
+    Module: DistriSelfAttentionPP (DistriFusion architecture article,
+    attention section); global context from stale activations: DistriFusion
+    reading notes, Introduction fourth paragraph."""
+    q = _f64(q)
+    k = _f64(k)
+    v = _f64(v)
+    B, Nq, HD = q.shape
+    D = HD // heads
+    if scale is None:
+        scale = 1.0 / np.sqrt(D)
+    if rows is None:
+        b_idx = np.repeat(np.arange(B), Nq)
+        q_idx = np.tile(np.arange(Nq), B)
+    else:
+        b_idx, q_idx = (np.asarray(r, dtype=np.int64) for r in rows)
+    out = np.empty((len(b_idx), HD))
+    for b in np.unique(b_idx):
+        sel = np.nonzero(b_idx == b)[0]
+        for s0 in range(0, len(sel), block):
+            part = sel[s0:s0 + block]
+            qb = q[b, q_idx[part]]                                 # [n, HD]
+            for h in range(heads):
+                cs = slice(h * D, (h + 1) * D)
+                s = scale * (qb[:, cs] @ k[b, :, cs].T)            # [n, N]
+                s = s - s.max(axis=1, keepdims=True)
+                e = np.exp(s)
+                out[part, cs] = (e @ v[b, :, cs]) / e.sum(axis=1, keepdims=True)
+    if rows is None:
+        return out.reshape(B, Nq, HD)
+    return out
+
+
+# ------------------------------------------------------------------ a5: CFG combine
+def cfg_combine_relmae(eps_c, eps_u, guidance: float):
+    """Classifier-free guidance combine and the denoising discrepancy.
+
+    eps = eps_u + w (eps_c - eps_u);  rel = sum|eps_c - eps_u| / sum|eps_u|
+    (reading R5; 0/0 gives NaN, x/0 gives inf).  Branches: Hybridiff technical
+    summary section 2A; discrepancy: section 2B."""
+    c = _f64(eps_c)
+    u = _f64(eps_u)
+    d = c - u
+    eps = u + guidance * d
+    with np.errstate(divide="ignore", invalid="ignore"):
+        rel = np.float64(np.abs(d).sum()) / np.float64(np.abs(u).sum())
+    return eps, float(rel)
+
+
+# ------------------------------------------------------------------ chained block
+def _store(a, bf16: bool):
+    return bf16_round(a) if bf16 else _f64(a)
+
+
+def previous_step_state(x_stale, gamma, beta, weight, bias, P: int, G: int, eps: float, bf16: bool):
+    """The synchronous first step on the stale input (reading R6): every patch
+    sees fresh data, so each layer is the plain full-image layer.
+
+    Returns dict: stale_stats [B,P,G,2] raw sums of each patch of x_stale;
+    a1 = GN(x_stale) [B,H,W,C] (stored: bf16-rounded when bf16); a2 =
+    conv(a1) [B,H,W,C] (stored)."""
+    xs = _f64(x_stale)
+    B, H, W, C = xs.shape
+    R = H // P
+    stats = np.stack([patch_sums(xs[:, q * R:(q + 1) * R], G) for q in range(P)], axis=1)
+    a1, _ = groupnorm_stale(xs, None, gamma, beta, H, G, 0, eps)
+    a1 = _store(a1, bf16)
+    a2 = _store(conv3x3_halo(a1, None, weight, bias, 0), bf16)
+    return {"stale_stats": stats, "a1": a1, "a2": a2}
+
+
+def displaced_block(x_fresh, state, gamma, beta, weight, bias, P: int, p: int, G: int, heads: int,
+                    eps: float, bf16: bool, attn_rows=None):
+    """One device's share (patch p) of GN -> conv -> splice -> attention.
+
+    x_fresh [B,H,W,C]: this step's input (the patch's rows are used); state:
+    previous_step_state(...) of the stale input.  Identity projections: the
+    conv output of the patch is Q; K = V = the previous step's conv output with
+    the patch's rows replaced by the fresh conv output (reading R6).
+    Returns dict y1 (GN out), y2 (conv out), kv (spliced buffer), o
+    (attention out; only attn_rows=(b_idx, q_idx) when given), stats (fresh
+    sums)."""
+    xf = _f64(x_fresh)
+    B, H, W, C = xf.shape
+    R = H // P
+    r0 = p * R
+    x_p = xf[:, r0:r0 + R]
+    y1, fresh = groupnorm_stale(x_p, state["stale_stats"], gamma, beta, H, G, p, eps)
+    y1 = _store(y1, bf16)
+    y2 = _store(conv3x3_halo(y1, state["a1"], weight, bias, r0), bf16)
+    kv = splice(state["a2"], y2, r0)
+    q = y2.reshape(B, R * W, C)
+    kvt = kv.reshape(B, H * W, C)
+    o = self_attn_displaced(q, kvt, kvt, heads, rows=attn_rows)
+    return {"y1": y1, "y2": y2, "kv": kv, "o": o, "stats": fresh}
