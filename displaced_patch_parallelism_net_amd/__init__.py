@@ -1,0 +1,23 @@
+"""MI355X (gfx950) kernels for one device's share of a displaced-patch-parallel
+diffusion denoising step.
+
+The compute lives in libdpp.so (C ABI, include/dpp.h); `_lib` is its ctypes
+binding (same names as the C entry points) and `step` sequences the calls of
+one patch-layer step.  Importing the package fails if libdpp.so is missing.
+"""
+from ._lib import (  # noqa: F401
+    DPP_BF16,
+    DPP_F32,
+    DppError,
+    LIB_PATH,
+    dpp_cfg_combine_relmae,
+    dpp_cfg_combine_workspace_bytes,
+    dpp_conv3x3_halo,
+    dpp_groupnorm_stale,
+    dpp_groupnorm_stale_workspace_bytes,
+    dpp_self_attn_displaced,
+    dpp_self_attn_workspace_bytes,
+    dpp_splice_patch,
+    dpp_strerror,
+    dpp_version,
+)

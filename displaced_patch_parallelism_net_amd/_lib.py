@@ -1,0 +1,172 @@
+"""ctypes binding of libdpp (include/dpp.h).
+
+Argument marshalling only: each Python function has the name of the C entry
+point, takes device tensors instead of pointers, reads sizes from their shapes,
+passes the current HIP stream, and raises DppError on a non-zero status.  All
+computation happens in the library's HIP kernels.  Importing this module
+fails loudly when libdpp.so has not been built.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libdpp.so")
+
+DPP_BF16 = 0
+DPP_F32 = 1
+
+STATUS = {
+    0: "DPP_OK", -1: "DPP_ERR_NULL", -2: "DPP_ERR_SHAPE", -3: "DPP_ERR_DTYPE", -4: "DPP_ERR_ALIGN",
+    -5: "DPP_ERR_ALIAS", -6: "DPP_ERR_WORKSPACE", -7: "DPP_ERR_UNSUPPORTED", -8: "DPP_ERR_LAUNCH",
+}
+
+# Every symbol include/dpp.h declares: name -> (restype, argtypes)
+_vp, _i64, _i, _f, _sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+SIGNATURES = {
+    "dpp_strerror": (ctypes.c_char_p, [_i]),
+    "dpp_version": (_i, []),
+    "dpp_splice_patch": (_i, [_vp, _vp, _i64, _i64, _i64, _i64, _i64, _i64, _i, _vp]),
+    "dpp_groupnorm_stale_workspace_bytes": (_sz, [_i64, _i64, _i64, _i64, _i64]),
+    "dpp_groupnorm_stale": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _i64, _i64, _i64, _f,
+                                 _vp, _sz, _i, _vp]),
+    "dpp_conv3x3_halo": (_i, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _i64, _i64, _i, _vp]),
+    "dpp_self_attn_workspace_bytes": (_sz, [_i64, _i64, _i64, _i64, _i64, _i]),
+    "dpp_self_attn_displaced": (_i, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _i64, _i64, _i64, _f, _vp, _sz,
+                                     _i, _vp]),
+    "dpp_cfg_combine_workspace_bytes": (_sz, [_i64]),
+    "dpp_cfg_combine_relmae": (_i, [_vp, _vp, _vp, _vp, _i64, _f, _vp, _sz, _i, _vp]),
+}
+
+
+class DppError(RuntimeError):
+    def __init__(self, name: str, status: int):
+        self.status = status
+        super().__init__(f"{name} -> {status} ({STATUS.get(status, '?')})")
+
+
+def _load():
+    # PyTorch brings its own HIP runtime (libamdhip64.so.7 under torch/lib).
+    # Loading it first makes libdpp's libamdhip64.so.7 dependency resolve to
+    # that same runtime; otherwise the process would hold two HIP runtimes and
+    # torch's streams and allocations would be foreign to libdpp's launches.
+    import torch  # noqa: F401
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"libdpp.so not built at {LIB_PATH}: run `python -m displaced_patch_parallelism_net_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    for name, (res, args) in SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+LIB = _load()
+
+
+def _check(name, status):
+    if status != 0:
+        raise DppError(name, status)
+
+
+def _dtype(t):
+    import torch
+    if t.dtype == torch.bfloat16:
+        return DPP_BF16
+    if t.dtype == torch.float32:
+        return DPP_F32
+    raise TypeError(f"unsupported tensor dtype {t.dtype}")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    if isinstance(stream, int):
+        return ctypes.c_void_p(stream)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _contig(*ts):
+    for t in ts:
+        if t is not None and not t.is_contiguous():
+            raise ValueError("tensor must be contiguous")
+
+
+# ------------------------------------------------------------------ calls
+def dpp_splice_patch(full, patch, row0: int, stream=None):
+    _contig(full, patch)
+    B, H, W, C = full.shape
+    rows = patch.shape[1]
+    _check("dpp_splice_patch", LIB.dpp_splice_patch(_ptr(full), _ptr(patch), B, H, W, C, row0, rows, _dtype(full),
+                                                    _stream(stream)))
+
+
+def dpp_groupnorm_stale_workspace_bytes(B, rows, W, C, G) -> int:
+    return int(LIB.dpp_groupnorm_stale_workspace_bytes(B, rows, W, C, G))
+
+
+def dpp_groupnorm_stale(y, stats_out, x, stale_stats, gamma, beta, H: int, G: int, P: int, p: int, eps: float,
+                        workspace, stream=None):
+    _contig(y, stats_out, x, stale_stats, gamma, beta)
+    B, rows, W, C = x.shape
+    _check("dpp_groupnorm_stale",
+           LIB.dpp_groupnorm_stale(_ptr(y), _ptr(stats_out), _ptr(x), _ptr(stale_stats), _ptr(gamma), _ptr(beta), B, H,
+                                   W, C, G, P, p, rows, eps, _ptr(workspace),
+                                   0 if workspace is None else workspace.numel() * workspace.element_size(),
+                                   _dtype(x), _stream(stream)))
+
+
+def dpp_conv3x3_halo(y, x, stale_full, weight, bias, H: int, row0: int, stream=None):
+    _contig(y, x, stale_full, weight, bias)
+    B, rows, W, Cin = x.shape
+    Cout = weight.shape[0]
+    _check("dpp_conv3x3_halo",
+           LIB.dpp_conv3x3_halo(_ptr(y), _ptr(x), _ptr(stale_full), _ptr(weight), _ptr(bias), B, H, W, Cin, Cout, row0,
+                                rows, _dtype(x), _stream(stream)))
+
+
+def dpp_self_attn_workspace_bytes(B, n_q, n_kv, heads, head_dim, dtype) -> int:
+    return int(LIB.dpp_self_attn_workspace_bytes(B, n_q, n_kv, heads, head_dim, dtype))
+
+
+def dpp_self_attn_displaced(o, q, k, v, heads: int, head_dim: int = 64, scale: float = 0.0, workspace=None,
+                            stream=None):
+    """q [B,n_q,*], k/v [B,n_kv,*], o [B,n_q,*]; row strides from the tensors
+    (last dimension contiguous, batch stride = rows * row stride)."""
+    for t in (o, q, k, v):
+        if t.stride(2) != 1 or t.stride(0) != t.shape[1] * t.stride(1):
+            raise ValueError("attention tensors must be [B,N,ld] row-major with unit channel stride")
+    B, n_q = q.shape[0], q.shape[1]
+    n_kv = k.shape[1]
+    _check("dpp_self_attn_displaced",
+           LIB.dpp_self_attn_displaced(_ptr(o), _ptr(q), _ptr(k), _ptr(v), B, n_q, n_kv, heads, head_dim, q.stride(1),
+                                       k.stride(1), o.stride(1), scale, _ptr(workspace),
+                                       0 if workspace is None else workspace.numel() * workspace.element_size(),
+                                       _dtype(q), _stream(stream)))
+
+
+def dpp_cfg_combine_workspace_bytes(n) -> int:
+    return int(LIB.dpp_cfg_combine_workspace_bytes(n))
+
+
+def dpp_cfg_combine_relmae(eps, relmae, eps_c, eps_u, guidance: float, workspace=None, stream=None):
+    _contig(eps, eps_c, eps_u)
+    n = eps_c.numel()
+    _check("dpp_cfg_combine_relmae",
+           LIB.dpp_cfg_combine_relmae(_ptr(eps), _ptr(relmae), _ptr(eps_c), _ptr(eps_u), n, guidance, _ptr(workspace),
+                                      0 if workspace is None else workspace.numel() * workspace.element_size(),
+                                      _dtype(eps_c), _stream(stream)))
+
+
+def dpp_strerror(status: int) -> str:
+    return LIB.dpp_strerror(status).decode()
+
+
+def dpp_version() -> int:
+    return int(LIB.dpp_version())

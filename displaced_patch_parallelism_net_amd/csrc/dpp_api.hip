@@ -1,0 +1,183 @@
+// C ABI of libdpp: argument validation on the host, then the launch
+// sequence of each call on the caller's stream.  No call allocates, frees,
+// synchronises or keeps state.  Validation runs before any HIP call, so an
+// invalid call returns its error code without touching the device.
+#include "../../include/dpp.h"
+#include "dpp_common.h"
+
+namespace {
+
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+inline int esize_of(int dtype) { return dtype == DPP_BF16 ? 2 : 4; }
+
+// Byte ranges [lo, hi) overlap?
+inline bool overlap(const void* a, int64_t abytes, const void* b, int64_t bbytes) {
+  const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
+  return a0 < b0 + static_cast<uintptr_t>(bbytes) && b0 < a0 + static_cast<uintptr_t>(abytes);
+}
+
+inline int launch_status(hipError_t e) { return e == hipSuccess ? DPP_OK : DPP_ERR_LAUNCH; }
+
+inline bool bad_dtype(int dtype) { return dtype != DPP_BF16 && dtype != DPP_F32; }
+
+}  // namespace
+
+extern "C" {
+
+const char* dpp_strerror(int status) {
+  switch (status) {
+    case DPP_OK: return "DPP_OK";
+    case DPP_ERR_NULL: return "DPP_ERR_NULL: required pointer is NULL";
+    case DPP_ERR_SHAPE: return "DPP_ERR_SHAPE: invalid sizes";
+    case DPP_ERR_DTYPE: return "DPP_ERR_DTYPE: unknown dtype";
+    case DPP_ERR_ALIGN: return "DPP_ERR_ALIGN: pointer or stride not 16-byte aligned";
+    case DPP_ERR_ALIAS: return "DPP_ERR_ALIAS: output overlaps an input";
+    case DPP_ERR_WORKSPACE: return "DPP_ERR_WORKSPACE: workspace missing or too small";
+    case DPP_ERR_UNSUPPORTED: return "DPP_ERR_UNSUPPORTED: no kernel for this shape/dtype";
+    case DPP_ERR_LAUNCH: return "DPP_ERR_LAUNCH: kernel launch failed";
+    default: return "DPP: unknown status";
+  }
+}
+
+int dpp_version(void) { return DPP_VERSION; }
+
+// ------------------------------------------------------------------ a1
+int dpp_splice_patch(void* full, const void* patch, int64_t B, int64_t H, int64_t W, int64_t C, int64_t row0,
+                     int64_t rows, int dtype, void* stream) {
+  if (bad_dtype(dtype)) return DPP_ERR_DTYPE;
+  if (!full || !patch) return DPP_ERR_NULL;
+  if (B <= 0 || H <= 0 || W <= 0 || C <= 0 || rows <= 0 || row0 < 0 || row0 + rows > H) return DPP_ERR_SHAPE;
+  if (B > 65535) return DPP_ERR_UNSUPPORTED;
+  const int es = esize_of(dtype);
+  if (overlap(full, B * H * W * C * es, patch, B * rows * W * C * es)) return DPP_ERR_ALIAS;
+  return launch_status(dpp::launch_splice(full, patch, B, H, W, C, row0, rows, es, static_cast<hipStream_t>(stream)));
+}
+
+// ------------------------------------------------------------------ a2
+size_t dpp_groupnorm_stale_workspace_bytes(int64_t B, int64_t rows, int64_t W, int64_t C, int64_t G) {
+  if (B <= 0 || rows <= 0 || W <= 0 || C <= 0 || G <= 0 || C % G != 0 || C % 4 != 0) return 0;
+  return dpp::gn_workspace_bytes(B, rows, W, C, G);
+}
+
+int dpp_groupnorm_stale(void* y, float* stats_out, const void* x, const float* stale_stats, const float* gamma,
+                        const float* beta, int64_t B, int64_t H, int64_t W, int64_t C, int64_t G, int64_t P, int64_t p,
+                        int64_t rows, float eps, void* workspace, size_t workspace_bytes, int dtype, void* stream) {
+  if (bad_dtype(dtype)) return DPP_ERR_DTYPE;
+  if (!x || !stats_out) return DPP_ERR_NULL;
+  if (y && (!gamma || !beta)) return DPP_ERR_NULL;
+  if (y && P > 1 && !stale_stats) return DPP_ERR_NULL;
+  if (B <= 0 || H <= 0 || W <= 0 || C <= 0 || G <= 0 || P <= 0 || rows <= 0 || rows > H || p < 0 || p >= P ||
+      C % G != 0 || !(eps >= 0.f))
+    return DPP_ERR_SHAPE;
+  const int vec = dtype == DPP_BF16 ? 8 : 4;
+  if (C % vec != 0 || C / vec > 256 || G > 256 || B > 65535) return DPP_ERR_UNSUPPORTED;
+  if (!aligned16(x) || (y && !aligned16(y))) return DPP_ERR_ALIGN;
+  const int es = esize_of(dtype);
+  const int64_t act = B * rows * W * C * es;
+  const int64_t st = B * P * G * 2 * 4;
+  if (overlap(stats_out, st, x, act)) return DPP_ERR_ALIAS;
+  if (stale_stats && overlap(stats_out, st, stale_stats, st)) return DPP_ERR_ALIAS;
+  if (y && (overlap(y, act, x, act) || overlap(y, act, stats_out, st))) return DPP_ERR_ALIAS;
+  if (y && stale_stats && overlap(y, act, stale_stats, st)) return DPP_ERR_ALIAS;
+  const size_t need = dpp::gn_workspace_bytes(B, rows, W, C, G);
+  if (!workspace || workspace_bytes < need) return DPP_ERR_WORKSPACE;
+  if (overlap(workspace, static_cast<int64_t>(need), x, act) || overlap(workspace, static_cast<int64_t>(need), stats_out, st) ||
+      (y && overlap(workspace, static_cast<int64_t>(need), y, act)))
+    return DPP_ERR_ALIAS;
+  return launch_status(dpp::launch_groupnorm(y, stats_out, x, stale_stats, gamma, beta, B, H, W, C, G, P, p, rows, eps,
+                                             workspace, dtype == DPP_BF16, static_cast<hipStream_t>(stream)));
+}
+
+// ------------------------------------------------------------------ a3
+int dpp_conv3x3_halo(void* y, const void* x, const void* stale_full, const void* weight, const float* bias, int64_t B,
+                     int64_t H, int64_t W, int64_t Cin, int64_t Cout, int64_t row0, int64_t rows, int dtype,
+                     void* stream) {
+  if (bad_dtype(dtype)) return DPP_ERR_DTYPE;
+  if (!y || !x || !weight) return DPP_ERR_NULL;
+  if (B <= 0 || H <= 0 || W <= 0 || Cin <= 0 || Cout <= 0 || rows <= 0 || row0 < 0 || row0 + rows > H)
+    return DPP_ERR_SHAPE;
+  const bool needs_stale = row0 > 0 || row0 + rows < H;
+  if (needs_stale && !stale_full) return DPP_ERR_NULL;
+  if (B > 65535 || W > (1 << 24) || H > (1 << 24) || Cin > (1 << 20) || Cout > (1 << 20)) return DPP_ERR_UNSUPPORTED;
+  if (dtype == DPP_BF16) {
+    if (Cin % 64 != 0 || Cout % 16 != 0) return DPP_ERR_UNSUPPORTED;
+    if (!aligned16(x) || !aligned16(y) || !aligned16(weight) || (stale_full && !aligned16(stale_full)))
+      return DPP_ERR_ALIGN;
+  }
+  const int es = esize_of(dtype);
+  const int64_t ybytes = B * rows * W * Cout * es;
+  if (overlap(y, ybytes, x, B * rows * W * Cin * es) || overlap(y, ybytes, weight, Cout * 9 * Cin * es) ||
+      (stale_full && overlap(y, ybytes, stale_full, B * H * W * Cin * es)) || (bias && overlap(y, ybytes, bias, Cout * 4)))
+    return DPP_ERR_ALIAS;
+  return launch_status(dpp::launch_conv3x3(y, x, stale_full, weight, bias, B, H, W, Cin, Cout, row0, rows,
+                                           dtype == DPP_BF16, static_cast<hipStream_t>(stream)));
+}
+
+// ------------------------------------------------------------------ a4
+size_t dpp_self_attn_workspace_bytes(int64_t B, int64_t n_q, int64_t n_kv, int64_t heads, int64_t head_dim, int dtype) {
+  if (B <= 0 || n_q <= 0 || n_kv <= 0 || heads <= 0 || head_dim <= 0 || bad_dtype(dtype)) return 0;
+  return dpp::attn_workspace_bytes(B, n_q, n_kv, heads, head_dim, dtype == DPP_BF16);
+}
+
+int dpp_self_attn_displaced(void* o, const void* q, const void* k, const void* v, int64_t B, int64_t n_q, int64_t n_kv,
+                            int64_t heads, int64_t head_dim, int64_t ld_q, int64_t ld_kv, int64_t ld_o, float scale,
+                            void* workspace, size_t workspace_bytes, int dtype, void* stream) {
+  if (bad_dtype(dtype)) return DPP_ERR_DTYPE;
+  if (!o || !q || !k || !v) return DPP_ERR_NULL;
+  if (B <= 0 || n_q <= 0 || n_kv <= 0 || heads <= 0 || head_dim <= 0) return DPP_ERR_SHAPE;
+  const int64_t hd = heads * head_dim;
+  if (ld_q < hd || ld_kv < hd || ld_o < hd) return DPP_ERR_SHAPE;
+  if (B * heads > 65535 || n_q > (1LL << 30) || n_kv > (1LL << 30)) return DPP_ERR_UNSUPPORTED;
+  if (dtype == DPP_BF16) {
+    if (head_dim != 64) return DPP_ERR_UNSUPPORTED;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || ld_q % 8 || ld_kv % 8 || ld_o % 8)
+      return DPP_ERR_ALIGN;
+  } else if (head_dim != 16 && head_dim != 32 && head_dim != 64 && head_dim != 128) {
+    return DPP_ERR_UNSUPPORTED;
+  }
+  const int es = esize_of(dtype);
+  const int64_t obytes = B * n_q * ld_o * es;
+  const int64_t kvbytes = B * n_kv * ld_kv * es;
+  if (overlap(o, obytes, q, B * n_q * ld_q * es) || overlap(o, obytes, k, kvbytes) || overlap(o, obytes, v, kvbytes))
+    return DPP_ERR_ALIAS;
+  if (workspace && workspace_bytes > 0) {
+    const int64_t wb = static_cast<int64_t>(workspace_bytes);
+    if (overlap(workspace, wb, o, obytes) || overlap(workspace, wb, q, B * n_q * ld_q * es) ||
+        overlap(workspace, wb, k, kvbytes) || overlap(workspace, wb, v, kvbytes))
+      return DPP_ERR_ALIAS;
+  }
+  if (!(scale > 0.f)) scale = 1.0f / sqrtf(static_cast<float>(head_dim));
+  return launch_status(dpp::launch_attention(o, q, k, v, B, n_q, n_kv, heads, head_dim, ld_q, ld_kv, ld_o, scale,
+                                             workspace, workspace ? workspace_bytes : 0, dtype == DPP_BF16,
+                                             static_cast<hipStream_t>(stream)));
+}
+
+// ------------------------------------------------------------------ a5
+size_t dpp_cfg_combine_workspace_bytes(int64_t n) {
+  if (n <= 0) return 0;
+  return dpp::cfg_workspace_bytes(n);
+}
+
+int dpp_cfg_combine_relmae(void* eps, float* relmae, const void* eps_c, const void* eps_u, int64_t n, float guidance,
+                           void* workspace, size_t workspace_bytes, int dtype, void* stream) {
+  if (bad_dtype(dtype)) return DPP_ERR_DTYPE;
+  if (!eps || !eps_c || !eps_u) return DPP_ERR_NULL;
+  if (n <= 0) return DPP_ERR_SHAPE;
+  const int es = esize_of(dtype);
+  const int64_t nb = n * es;
+  if ((eps != eps_c && overlap(eps, nb, eps_c, nb)) || (eps != eps_u && overlap(eps, nb, eps_u, nb)))
+    return DPP_ERR_ALIAS;
+  if (relmae) {
+    const size_t need = dpp::cfg_workspace_bytes(n);
+    if (!workspace || workspace_bytes < need) return DPP_ERR_WORKSPACE;
+    const int64_t wb = static_cast<int64_t>(need);
+    if (overlap(workspace, wb, eps, nb) || overlap(workspace, wb, eps_c, nb) || overlap(workspace, wb, eps_u, nb) ||
+        overlap(relmae, 4, eps, nb) || overlap(relmae, 4, workspace, wb))
+      return DPP_ERR_ALIAS;
+  }
+  return launch_status(dpp::launch_cfg(eps, relmae, eps_c, eps_u, n, guidance, workspace, dtype == DPP_BF16,
+                                       static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,119 @@
+// Internal helpers shared by the libdpp kernels (gfx950 / CDNA4, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dpp {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int kWave = 64;
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint16_t h) {
+  return __uint_as_float(static_cast<uint32_t>(h) << 16);
+}
+
+// float32 -> bf16 with round-to-nearest-even (v_cvt_pk_bf16_f32 on gfx950).
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
+  __bf16 b = static_cast<__bf16>(f);
+  return __builtin_bit_cast(uint16_t, b);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  bf16x2 v;
+  v.x = static_cast<__bf16>(lo);
+  v.y = static_cast<__bf16>(hi);
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// 8 bf16 in a uint4 -> 8 floats.
+__device__ __forceinline__ void unpack8(const uint4& u, float* f) {
+  f[0] = __uint_as_float(u.x << 16);
+  f[1] = __uint_as_float(u.x & 0xffff0000u);
+  f[2] = __uint_as_float(u.y << 16);
+  f[3] = __uint_as_float(u.y & 0xffff0000u);
+  f[4] = __uint_as_float(u.z << 16);
+  f[5] = __uint_as_float(u.z & 0xffff0000u);
+  f[6] = __uint_as_float(u.w << 16);
+  f[7] = __uint_as_float(u.w & 0xffff0000u);
+}
+
+__device__ __forceinline__ uint4 pack8(const float* f) {
+  uint4 u;
+  u.x = pack_bf16x2(f[0], f[1]);
+  u.y = pack_bf16x2(f[2], f[3]);
+  u.z = pack_bf16x2(f[4], f[5]);
+  u.w = pack_bf16x2(f[6], f[7]);
+  return u;
+}
+
+// Element access for the two storage types.
+template <typename T> struct Elem;
+template <> struct Elem<float> {
+  static constexpr int kVec = 4;  // elements per 16-byte vector
+  __device__ static float load(const float* p, int64_t i) { return p[i]; }
+  __device__ static void store(float* p, int64_t i, float v) { p[i] = v; }
+  __device__ static void unpack(const uint4& u, float* f) {
+    f[0] = __uint_as_float(u.x); f[1] = __uint_as_float(u.y);
+    f[2] = __uint_as_float(u.z); f[3] = __uint_as_float(u.w);
+  }
+  __device__ static uint4 pack(const float* f) {
+    return make_uint4(__float_as_uint(f[0]), __float_as_uint(f[1]),
+                      __float_as_uint(f[2]), __float_as_uint(f[3]));
+  }
+};
+template <> struct Elem<uint16_t> {
+  static constexpr int kVec = 8;
+  __device__ static float load(const uint16_t* p, int64_t i) { return bf16_bits_to_f32(p[i]); }
+  __device__ static void store(uint16_t* p, int64_t i, float v) { p[i] = f32_to_bf16_bits(v); }
+  __device__ static void unpack(const uint4& u, float* f) { unpack8(u, f); }
+  __device__ static uint4 pack(const float* f) { return pack8(f); }
+};
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
+__device__ __forceinline__ double wave_sum_d(double v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
+inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+}  // namespace dpp
+
+// Launchers (host side, one per kernel family).  They assume validated
+// arguments and return the hipError_t of the launch.
+namespace dpp {
+hipError_t launch_splice(void* full, const void* patch, int64_t B, int64_t H, int64_t W, int64_t C,
+                         int64_t row0, int64_t rows, int esize, hipStream_t s);
+
+size_t gn_workspace_bytes(int64_t B, int64_t rows, int64_t W, int64_t C, int64_t G);
+hipError_t launch_groupnorm(void* y, float* stats_out, const void* x, const float* stale_stats,
+                            const float* gamma, const float* beta, int64_t B, int64_t H, int64_t W,
+                            int64_t C, int64_t G, int64_t P, int64_t p, int64_t rows, float eps,
+                            void* ws, bool bf16, hipStream_t s);
+
+hipError_t launch_conv3x3(void* y, const void* x, const void* stale_full, const void* weight,
+                          const float* bias, int64_t B, int64_t H, int64_t W, int64_t Cin,
+                          int64_t Cout, int64_t row0, int64_t rows, bool bf16, hipStream_t s);
+
+size_t attn_workspace_bytes(int64_t B, int64_t n_q, int64_t n_kv, int64_t heads, int64_t D, bool bf16);
+hipError_t launch_attention(void* o, const void* q, const void* k, const void* v, int64_t B,
+                            int64_t n_q, int64_t n_kv, int64_t heads, int64_t D, int64_t ld_q,
+                            int64_t ld_kv, int64_t ld_o, float scale, void* ws, size_t ws_bytes,
+                            bool bf16, hipStream_t s);
+
+size_t cfg_workspace_bytes(int64_t n);
+hipError_t launch_cfg(void* eps, float* relmae, const void* eps_c, const void* eps_u, int64_t n,
+                      float guidance, void* ws, bool bf16, hipStream_t s);
+}  // namespace dpp

@@ -1,0 +1,415 @@
+// a4 -- displaced self-attention: the patch's queries against all tokens of
+// the spliced full-image K/V buffer.
+//
+// DistriSelfAttentionPP (DistriFusion architecture article, attention
+// section); the K/V rows of other patches are the previous step's
+// (DistriFusion reading notes, Introduction, fourth paragraph).  Per batch b,
+// head h and query i: o = softmax(scale q k^T) v over every key.
+//
+// bf16 path (head_dim 64): one pass over the keys with an online softmax
+// (running max m, running sum l, rescaled output), all on MFMA
+// v_mfma_f32_32x32x16_bf16:
+//  * a workgroup owns 256 queries of one (b, h) and a range of keys; each of
+//    its four waves owns 64 queries (two 32-query blocks) whose Q fragments
+//    stay in registers for the whole pass;
+//  * K and V tiles of 64 keys are double-buffered in LDS; the next tile's
+//    global loads are issued before the current tile's math;
+//  * scores are computed transposed, S^T = K Q^T, so each lane holds the
+//    scores of one query: the row max needs one cross-lane exchange, the row
+//    sum stays lane-local until the end, and the rescale of O^T is per lane;
+//  * the accumulator layout of S^T is reused as the B operand of
+//    O^T = V^T P^T after conversion to bf16: within every 16 keys the MFMA's
+//    k index runs over the keys in the order 0-3, 8-11, 4-7, 12-15, so V is
+//    written to LDS transposed ([d][key]) in that order;
+//  * scores are scaled by scale*log2(e) and exponentiated with exp2.
+// When the workspace allows, the key range is split over several workgroups
+// (fills the GPU when there are few query tiles); a second kernel merges the
+// partial (m, l, O) triples.
+//
+// f32 path: one thread per query, scalar online softmax (small shapes).
+#include "dpp_common.h"
+
+namespace dpp {
+
+// ------------------------------------------------------------------ fp32 reference-style kernel
+template <int D>
+__global__ __launch_bounds__(64) void attn_f32_kernel(const float* __restrict__ q, const float* __restrict__ k,
+                                                      const float* __restrict__ v, float* __restrict__ o, int n_q,
+                                                      int n_kv, int heads, int64_t ld_q, int64_t ld_kv, int64_t ld_o,
+                                                      float scale) {
+  const int bh = blockIdx.y;
+  const int b = bh / heads, h = bh % heads;
+  const int i = blockIdx.x * 64 + threadIdx.x;
+  if (i >= n_q) return;
+  const float* qp = q + (static_cast<int64_t>(b) * n_q + i) * ld_q + h * D;
+  const float* kb = k + static_cast<int64_t>(b) * n_kv * ld_kv + h * D;
+  const float* vb = v + static_cast<int64_t>(b) * n_kv * ld_kv + h * D;
+  float qr[D], acc[D];
+#pragma unroll
+  for (int d = 0; d < D; ++d) { qr[d] = qp[d] * scale; acc[d] = 0.f; }
+  float m = -INFINITY, l = 0.f;
+  for (int j = 0; j < n_kv; ++j) {
+    const float* kr = kb + static_cast<int64_t>(j) * ld_kv;
+    float s = 0.f;
+#pragma unroll
+    for (int d = 0; d < D; ++d) s = fmaf(qr[d], kr[d], s);
+    const float mn = fmaxf(m, s);
+    const float alpha = expf(m - mn);
+    const float p = expf(s - mn);
+    l = l * alpha + p;
+    const float* vr = vb + static_cast<int64_t>(j) * ld_kv;
+#pragma unroll
+    for (int d = 0; d < D; ++d) acc[d] = fmaf(acc[d], alpha, p * vr[d]);
+    m = mn;
+  }
+  float* op = o + (static_cast<int64_t>(b) * n_q + i) * ld_o + h * D;
+  const float inv = 1.f / l;
+#pragma unroll
+  for (int d = 0; d < D; ++d) op[d] = acc[d] * inv;
+}
+
+// ------------------------------------------------------------------ bf16 MFMA flash kernel
+constexpr int kAttD = 64;
+constexpr int kAttKT = 64;                      // keys per tile
+constexpr int kAttWaves = 4;
+constexpr int kAttQW = 64;                      // queries per wave
+constexpr int kAttQT = kAttQW * kAttWaves;      // queries per workgroup
+constexpr int kAttThreads = kAttWaves * kWave;
+constexpr int kAttRow = 72;                     // padded LDS row (bf16): 144 bytes
+constexpr float kLog2e = 1.4426950408889634f;
+
+struct AttnArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  uint16_t* o;
+  float* o_part;   // [nsplit][B*heads][n_q][64] unnormalised, split mode only
+  float* ml_part;  // [nsplit][B*heads][n_q][2] (m, l), split mode only
+  int n_q, n_kv, heads;
+  int64_t ld_q, ld_kv, ld_o;
+  float c;          // scale * log2(e)
+  int keys_per_split;
+};
+
+// Position of key (0..15) inside its 16-key group in the MFMA k order.
+__device__ __forceinline__ int kperm16(int key) {
+  const int g = (key >> 3) & 1, a = (key >> 2) & 1;
+  return (key & ~15) | (a << 3) | (g << 2) | (key & 3);
+}
+
+__global__ __launch_bounds__(kAttThreads) void attn_bf16_kernel(AttnArgs a) {
+  __shared__ uint16_t Ks[2][kAttKT * kAttRow];
+  __shared__ uint16_t Vt[2][kAttD * kAttRow];
+
+  const int tid = threadIdx.x;
+  const int wave = tid / kWave, lane = tid % kWave;
+  const int g = lane >> 5, l32 = lane & 31;
+  const int bh = blockIdx.y;
+  const int b = bh / a.heads, h = bh % a.heads;
+  const int split = blockIdx.z;
+  const int k_begin = split * a.keys_per_split;
+  const int k_end = min(a.n_kv, k_begin + a.keys_per_split);
+  const int q0 = blockIdx.x * kAttQT + wave * kAttQW;
+
+  const uint16_t* qb = a.q + static_cast<int64_t>(b) * a.n_q * a.ld_q + h * kAttD;
+  const uint16_t* kb = a.k + static_cast<int64_t>(b) * a.n_kv * a.ld_kv + h * kAttD;
+  const uint16_t* vb = a.v + static_cast<int64_t>(b) * a.n_kv * a.ld_kv + h * kAttD;
+
+  // Q^T fragments (B operand of S^T = K Q^T): lane -> query l32, d = 16 ks + 8 g + 0..7
+  bf16x8 qf[2][4];
+#pragma unroll
+  for (int qb2 = 0; qb2 < 2; ++qb2) {
+    const int qi = q0 + qb2 * 32 + l32;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      uint4 u = make_uint4(0, 0, 0, 0);
+      if (qi < a.n_q) u = *reinterpret_cast<const uint4*>(qb + static_cast<int64_t>(qi) * a.ld_q + ks * 16 + g * 8);
+      qf[qb2][ks] = __builtin_bit_cast(bf16x8, u);
+    }
+  }
+
+  // Tile loader: thread -> key pair kp = tid / 8 (keys 2kp, 2kp+1), d vector dv = tid % 8.
+  const int kp = tid >> 3, dv = tid & 7;
+  uint4 kr0, kr1, vr0, vr1;
+  auto load_tile = [&](int t0) {
+    const int k0 = t0 + 2 * kp, k1 = k0 + 1;
+    const uint4 z = make_uint4(0, 0, 0, 0);
+    kr0 = (k0 < k_end) ? *reinterpret_cast<const uint4*>(kb + static_cast<int64_t>(k0) * a.ld_kv + dv * 8) : z;
+    kr1 = (k1 < k_end) ? *reinterpret_cast<const uint4*>(kb + static_cast<int64_t>(k1) * a.ld_kv + dv * 8) : z;
+    vr0 = (k0 < k_end) ? *reinterpret_cast<const uint4*>(vb + static_cast<int64_t>(k0) * a.ld_kv + dv * 8) : z;
+    vr1 = (k1 < k_end) ? *reinterpret_cast<const uint4*>(vb + static_cast<int64_t>(k1) * a.ld_kv + dv * 8) : z;
+  };
+  auto store_tile = [&](int buf) {
+    *reinterpret_cast<uint4*>(&Ks[buf][(2 * kp) * kAttRow + dv * 8]) = kr0;
+    *reinterpret_cast<uint4*>(&Ks[buf][(2 * kp + 1) * kAttRow + dv * 8]) = kr1;
+    // V^T: element (key, d) -> Vt[d][kperm16(key)]; keys 2kp, 2kp+1 stay adjacent.
+    const int pos = kperm16(2 * kp);
+    const uint32_t a0[4] = {vr0.x, vr0.y, vr0.z, vr0.w};
+    const uint32_t a1[4] = {vr1.x, vr1.y, vr1.z, vr1.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      // d = dv*8 + 2e (low halves) and dv*8 + 2e + 1 (high halves)
+      const uint32_t lo = (a0[e] & 0xffffu) | (a1[e] << 16);
+      const uint32_t hi = (a0[e] >> 16) | (a1[e] & 0xffff0000u);
+      *reinterpret_cast<uint32_t*>(&Vt[buf][(dv * 8 + 2 * e) * kAttRow + pos]) = lo;
+      *reinterpret_cast<uint32_t*>(&Vt[buf][(dv * 8 + 2 * e + 1) * kAttRow + pos]) = hi;
+    }
+  };
+
+  f32x16 O[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) O[i][j][r] = 0.f;
+  float m_run[2] = {-INFINITY, -INFINITY};
+  float l_run[2] = {0.f, 0.f};
+
+  const int ntiles = (k_end - k_begin + kAttKT - 1) / kAttKT;
+  load_tile(k_begin);
+  for (int it = 0; it < ntiles; ++it) {
+    const int buf = it & 1;
+    const int t0 = k_begin + it * kAttKT;
+    __syncthreads();  // readers of buffer `buf` (two tiles ago) are done
+    store_tile(buf);
+    __syncthreads();
+    if (it + 1 < ntiles) load_tile(t0 + kAttKT);
+
+    // ---- S^T = K Q^T for 2 key blocks x 2 query blocks
+    f32x16 S[2][2];
+#pragma unroll
+    for (int kb2 = 0; kb2 < 2; ++kb2) {
+#pragma unroll
+      for (int qb2 = 0; qb2 < 2; ++qb2)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) S[kb2][qb2][r] = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const bf16x8 kf = __builtin_bit_cast(
+            bf16x8, *reinterpret_cast<const uint4*>(&Ks[buf][(kb2 * 32 + l32) * kAttRow + ks * 16 + g * 8]));
+#pragma unroll
+        for (int qb2 = 0; qb2 < 2; ++qb2)
+          S[kb2][qb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[qb2][ks], S[kb2][qb2], 0, 0, 0);
+      }
+    }
+    // lane holds keys kb2*32 + 8*(r/4) + 4*g + r%4 of query l32
+    if (t0 + kAttKT > k_end) {
+#pragma unroll
+      for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = t0 + kb2 * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
+          if (key >= k_end) {
+            S[kb2][0][r] = -INFINITY;
+            S[kb2][1][r] = -INFINITY;
+          }
+        }
+    }
+
+    // ---- online softmax per query block, then O^T += V^T P^T
+    bf16x8 P[2][2][2];  // [qb][kb][t16]
+#pragma unroll
+    for (int qb2 = 0; qb2 < 2; ++qb2) {
+      float mx = S[0][qb2][0];
+#pragma unroll
+      for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, S[kb2][qb2][r]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+      const float m_new = fmaxf(m_run[qb2], mx * a.c);
+      const float alpha = __builtin_amdgcn_exp2f(m_run[qb2] - m_new);
+      m_run[qb2] = m_new;
+      float lsum = 0.f;
+#pragma unroll
+      for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+        for (int t16 = 0; t16 < 2; ++t16) {
+          float p[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            p[e] = __builtin_amdgcn_exp2f(fmaf(S[kb2][qb2][t16 * 8 + e], a.c, -m_new));
+            lsum += p[e];
+          }
+          uint4 u;
+          u.x = pack_bf16x2(p[0], p[1]);
+          u.y = pack_bf16x2(p[2], p[3]);
+          u.z = pack_bf16x2(p[4], p[5]);
+          u.w = pack_bf16x2(p[6], p[7]);
+          P[qb2][kb2][t16] = __builtin_bit_cast(bf16x8, u);
+        }
+      l_run[qb2] = fmaf(l_run[qb2], alpha, lsum);
+#pragma unroll
+      for (int db = 0; db < 2; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) O[qb2][db][r] *= alpha;
+    }
+#pragma unroll
+    for (int db = 0; db < 2; ++db)
+#pragma unroll
+      for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+        for (int t16 = 0; t16 < 2; ++t16) {
+          const bf16x8 vf = __builtin_bit_cast(
+              bf16x8,
+              *reinterpret_cast<const uint4*>(&Vt[buf][(db * 32 + l32) * kAttRow + kb2 * 32 + t16 * 16 + g * 8]));
+#pragma unroll
+          for (int qb2 = 0; qb2 < 2; ++qb2)
+            O[qb2][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, P[qb2][kb2][t16], O[qb2][db], 0, 0, 0);
+        }
+  }
+
+  // ---- epilogue: lane holds query l32, d = db*32 + 8*(r/4) + 4*g + r%4
+#pragma unroll
+  for (int qb2 = 0; qb2 < 2; ++qb2) {
+    const int qi = q0 + qb2 * 32 + l32;
+    const float l_tot = l_run[qb2] + __shfl_xor(l_run[qb2], 32, kWave);
+    if (qi >= a.n_q) continue;
+    if (a.o_part == nullptr) {
+      const float inv = 1.f / l_tot;
+      uint16_t* op = a.o + (static_cast<int64_t>(b) * a.n_q + qi) * a.ld_o + h * kAttD;
+#pragma unroll
+      for (int db = 0; db < 2; ++db)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const int d = db * 32 + 8 * r4 + 4 * g;
+          uint2 u;
+          u.x = pack_bf16x2(O[qb2][db][r4 * 4 + 0] * inv, O[qb2][db][r4 * 4 + 1] * inv);
+          u.y = pack_bf16x2(O[qb2][db][r4 * 4 + 2] * inv, O[qb2][db][r4 * 4 + 3] * inv);
+          *reinterpret_cast<uint2*>(op + d) = u;
+        }
+    } else {
+      const int64_t row = (static_cast<int64_t>(split) * gridDim.y + bh) * a.n_q + qi;
+      float* op = a.o_part + row * kAttD;
+#pragma unroll
+      for (int db = 0; db < 2; ++db)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const int d = db * 32 + 8 * r4 + 4 * g;
+          *reinterpret_cast<float4*>(op + d) =
+              make_float4(O[qb2][db][r4 * 4 + 0], O[qb2][db][r4 * 4 + 1], O[qb2][db][r4 * 4 + 2], O[qb2][db][r4 * 4 + 3]);
+        }
+      if (g == 0) {
+        a.ml_part[row * 2] = m_run[qb2];
+        a.ml_part[row * 2 + 1] = l_tot;
+      }
+    }
+  }
+}
+
+// Merge of key-range splits: thread per (b*heads, query, 4 channels).
+__global__ __launch_bounds__(256) void attn_merge_kernel(const float* __restrict__ o_part,
+                                                         const float* __restrict__ ml_part, uint16_t* __restrict__ o,
+                                                         int nsplit, int n_q, int heads, int64_t ld_o, int64_t rows) {
+  const int64_t idx = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (idx >= rows * 16) return;
+  const int64_t row = idx / 16;  // bh * n_q + qi
+  const int dq = static_cast<int>(idx % 16);
+  float M = -INFINITY;
+  for (int s = 0; s < nsplit; ++s) M = fmaxf(M, ml_part[(s * rows + row) * 2]);
+  float L = 0.f;
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int s = 0; s < nsplit; ++s) {
+    const float w = __builtin_amdgcn_exp2f(ml_part[(s * rows + row) * 2] - M);
+    L = fmaf(w, ml_part[(s * rows + row) * 2 + 1], L);
+    const float4 ov = *reinterpret_cast<const float4*>(o_part + (s * rows + row) * kAttD + dq * 4);
+    acc[0] = fmaf(w, ov.x, acc[0]);
+    acc[1] = fmaf(w, ov.y, acc[1]);
+    acc[2] = fmaf(w, ov.z, acc[2]);
+    acc[3] = fmaf(w, ov.w, acc[3]);
+  }
+  const float inv = 1.f / L;
+  const int64_t bh = row / n_q, qi = row % n_q;
+  const int64_t b = bh / heads, h = bh % heads;
+  uint16_t* op = o + (b * n_q + qi) * ld_o + h * kAttD + dq * 4;
+  uint2 u;
+  u.x = pack_bf16x2(acc[0] * inv, acc[1] * inv);
+  u.y = pack_bf16x2(acc[2] * inv, acc[3] * inv);
+  *reinterpret_cast<uint2*>(op) = u;
+}
+
+// Key-range split policy: depends on the shape only (so the workspace query
+// needs no device).  Aim for at least ~2 workgroups per CU of a 256-CU
+// MI355X while keeping >= 8 key tiles per split.
+struct AttnSplit {
+  int nsplit;
+  int keys_per_split;
+};
+static AttnSplit attn_split(int64_t B, int64_t n_q, int64_t n_kv, int64_t heads) {
+  const int64_t qtiles = ceil_div(n_q, kAttQT) * B * heads;
+  const int64_t ktiles = ceil_div(n_kv, kAttKT);
+  int64_t ns = 1;
+  const int64_t target = 512;
+  if (qtiles < target) ns = ceil_div(target, qtiles);
+  const int64_t max_ns = ktiles / 8 > 0 ? ktiles / 8 : 1;
+  if (ns > max_ns) ns = max_ns;
+  if (ns < 1) ns = 1;
+  int64_t kps = ceil_div(ktiles, ns) * kAttKT;
+  ns = ceil_div(n_kv, kps);
+  return AttnSplit{static_cast<int>(ns), static_cast<int>(kps)};
+}
+
+size_t attn_workspace_bytes(int64_t B, int64_t n_q, int64_t n_kv, int64_t heads, int64_t D, bool bf16) {
+  if (!bf16 || D != kAttD) return 0;
+  const AttnSplit sp = attn_split(B, n_q, n_kv, heads);
+  if (sp.nsplit <= 1) return 0;
+  const int64_t rows = static_cast<int64_t>(sp.nsplit) * B * heads * n_q;
+  return static_cast<size_t>(rows * (kAttD + 2)) * sizeof(float);
+}
+
+hipError_t launch_attention(void* o, const void* q, const void* k, const void* v, int64_t B, int64_t n_q, int64_t n_kv,
+                            int64_t heads, int64_t D, int64_t ld_q, int64_t ld_kv, int64_t ld_o, float scale, void* ws,
+                            size_t ws_bytes, bool bf16, hipStream_t s) {
+  if (!bf16) {
+    dim3 grid(static_cast<unsigned>(ceil_div(n_q, 64)), static_cast<unsigned>(B * heads));
+    auto* qq = static_cast<const float*>(q);
+    auto* kk = static_cast<const float*>(k);
+    auto* vv = static_cast<const float*>(v);
+    auto* oo = static_cast<float*>(o);
+    const int nq = static_cast<int>(n_q), nkv = static_cast<int>(n_kv), hh = static_cast<int>(heads);
+    switch (D) {
+      case 16: hipLaunchKernelGGL(attn_f32_kernel<16>, grid, dim3(64), 0, s, qq, kk, vv, oo, nq, nkv, hh, ld_q, ld_kv, ld_o, scale); break;
+      case 32: hipLaunchKernelGGL(attn_f32_kernel<32>, grid, dim3(64), 0, s, qq, kk, vv, oo, nq, nkv, hh, ld_q, ld_kv, ld_o, scale); break;
+      case 64: hipLaunchKernelGGL(attn_f32_kernel<64>, grid, dim3(64), 0, s, qq, kk, vv, oo, nq, nkv, hh, ld_q, ld_kv, ld_o, scale); break;
+      default: hipLaunchKernelGGL(attn_f32_kernel<128>, grid, dim3(64), 0, s, qq, kk, vv, oo, nq, nkv, hh, ld_q, ld_kv, ld_o, scale); break;
+    }
+    return hipGetLastError();
+  }
+  AttnArgs a;
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  a.o = static_cast<uint16_t*>(o);
+  a.n_q = static_cast<int>(n_q);
+  a.n_kv = static_cast<int>(n_kv);
+  a.heads = static_cast<int>(heads);
+  a.ld_q = ld_q;
+  a.ld_kv = ld_kv;
+  a.ld_o = ld_o;
+  a.c = scale * kLog2e;
+  AttnSplit sp = attn_split(B, n_q, n_kv, heads);
+  const size_t need = attn_workspace_bytes(B, n_q, n_kv, heads, D, true);
+  if (sp.nsplit > 1 && (ws == nullptr || ws_bytes < need)) {
+    sp.nsplit = 1;
+    sp.keys_per_split = static_cast<int>(ceil_div(n_kv, kAttKT) * kAttKT);
+  }
+  a.keys_per_split = sp.keys_per_split;
+  const int64_t rows = B * heads * n_q;
+  if (sp.nsplit > 1) {
+    a.o_part = static_cast<float*>(ws);
+    a.ml_part = a.o_part + static_cast<int64_t>(sp.nsplit) * rows * kAttD;
+  } else {
+    a.o_part = nullptr;
+    a.ml_part = nullptr;
+  }
+  dim3 grid(static_cast<unsigned>(ceil_div(n_q, kAttQT)), static_cast<unsigned>(B * heads),
+            static_cast<unsigned>(sp.nsplit));
+  hipLaunchKernelGGL(attn_bf16_kernel, grid, dim3(kAttThreads), 0, s, a);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess || sp.nsplit <= 1) return err;
+  hipLaunchKernelGGL(attn_merge_kernel, dim3(static_cast<unsigned>(ceil_div(rows * 16, 256))), dim3(256), 0, s,
+                     a.o_part, a.ml_part, a.o, sp.nsplit, a.n_q, a.heads, ld_o, rows);
+  return hipGetLastError();
+}
+
+}  // namespace dpp

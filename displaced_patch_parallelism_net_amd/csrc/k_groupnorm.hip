@@ -1,0 +1,255 @@
+// a2 -- GroupNorm of one patch with statistics corrected by stale sums.
+//
+// DistriGroupNorm (DistriFusion architecture article, normalisation section):
+// the group statistics are those of the spliced image -- the other patches'
+// raw sums (sum x, sum x^2) from the previous step plus the own patch's fresh
+// sums (DistriFusion reading notes, Introduction, fourth paragraph).
+//
+// Three launches, all deterministic (no atomics):
+//   1. partial: workgroup (chunk, b) sums its pixels per channel in float32
+//      registers (each thread owns one 16-byte channel vector and walks
+//      pixels), folds channels into groups through LDS in a fixed order and
+//      writes one (s1, s2) per group to the workspace;
+//   2. finalize: one workgroup per b adds the chunk partials in float64 (fixed
+//      order), adds the other patches' stale sums, writes the fresh sums to
+//      stats_out[b,p] and mean/rstd to the workspace;
+//   3. apply: y = x * a_c + b_c with a_c = rstd_g gamma_c, b_c = beta_c -
+//      mean_g a_c; one 16-byte load and store per vector.
+// The second read of x (step 3) normally hits the 256 MB last-level cache.
+#include "dpp_common.h"
+
+namespace dpp {
+
+constexpr int kGnMaxThreads = 256;
+constexpr int kGnStatChunks = 256;    // total partial workgroups (over B)
+constexpr int kGnApplyChunks = 1024;  // total apply workgroups (over B)
+
+struct GnGeom {
+  int vec;      // elements per 16-byte vector
+  int V;        // vectors per pixel = C / vec
+  int KP;       // pixels walked in parallel per workgroup
+  int threads;  // KP * V
+  int64_t npix;
+  int64_t nstat, stat_ppc;    // partial chunks per b, pixels per chunk
+  int64_t napply, apply_ppc;  // apply chunks per b, pixels per chunk
+};
+
+static GnGeom gn_geom(int64_t B, int64_t rows, int64_t W, int64_t C, bool bf16) {
+  GnGeom g;
+  g.vec = bf16 ? 8 : 4;
+  g.V = static_cast<int>(C / g.vec);
+  g.KP = kGnMaxThreads / g.V;
+  if (g.KP < 1) g.KP = 1;
+  g.threads = g.KP * g.V;
+  g.npix = rows * W;
+  const int64_t maxc = ceil_div(g.npix, g.KP);
+  int64_t want = ceil_div(kGnStatChunks, B);
+  g.nstat = want < maxc ? want : maxc;
+  if (g.nstat < 1) g.nstat = 1;
+  g.stat_ppc = ceil_div(g.npix, g.nstat);
+  g.nstat = ceil_div(g.npix, g.stat_ppc);
+  want = ceil_div(kGnApplyChunks, B);
+  g.napply = want < maxc ? want : maxc;
+  if (g.napply < 1) g.napply = 1;
+  g.apply_ppc = ceil_div(g.npix, g.napply);
+  g.napply = ceil_div(g.npix, g.apply_ppc);
+  return g;
+}
+
+size_t gn_workspace_bytes(int64_t B, int64_t rows, int64_t W, int64_t C, int64_t G) {
+  // bf16 and f32 differ in chunking; size for the larger of the two that
+  // the channel count admits.
+  int64_t nstat = gn_geom(B, rows, W, C, false).nstat;
+  if (C % 8 == 0) {
+    const int64_t nb = gn_geom(B, rows, W, C, true).nstat;
+    if (nb > nstat) nstat = nb;
+  }
+  return static_cast<size_t>(B * nstat * G * 2 + B * G * 2) * sizeof(float);
+}
+
+template <typename T>
+__global__ __launch_bounds__(kGnMaxThreads) void gn_partial_kernel(const T* __restrict__ x, float* __restrict__ partial,
+                                                                   int64_t npix, int C, int G, int V, int KP,
+                                                                   int64_t ppc, int64_t nchunk) {
+  constexpr int VEC = Elem<T>::kVec;
+  __shared__ float red1[kGnMaxThreads * 8];
+  __shared__ float red2[kGnMaxThreads * 8];
+  const int b = blockIdx.y;
+  const int64_t chunk = blockIdx.x;
+  const int t = threadIdx.x;
+  const int v = t % V, k = t / V;
+  const int64_t p0 = chunk * ppc;
+  const int64_t p1 = (p0 + ppc < npix) ? p0 + ppc : npix;
+  const uint4* xv = reinterpret_cast<const uint4*>(x + static_cast<int64_t>(b) * npix * C);
+  float s1[VEC], s2[VEC];
+#pragma unroll
+  for (int j = 0; j < VEC; ++j) { s1[j] = 0.f; s2[j] = 0.f; }
+  if (k < KP) {
+    int64_t pix = p0 + k;
+    // two vectors in flight per iteration
+    for (; pix + KP < p1; pix += 2 * KP) {
+      const uint4 a = xv[pix * V + v];
+      const uint4 c = xv[(pix + KP) * V + v];
+      float fa[VEC], fc[VEC];
+      Elem<T>::unpack(a, fa);
+      Elem<T>::unpack(c, fc);
+#pragma unroll
+      for (int j = 0; j < VEC; ++j) {
+        s1[j] += fa[j] + fc[j];
+        s2[j] = fmaf(fa[j], fa[j], s2[j]);
+        s2[j] = fmaf(fc[j], fc[j], s2[j]);
+      }
+    }
+    if (pix < p1) {
+      float fa[VEC];
+      Elem<T>::unpack(xv[pix * V + v], fa);
+#pragma unroll
+      for (int j = 0; j < VEC; ++j) { s1[j] += fa[j]; s2[j] = fmaf(fa[j], fa[j], s2[j]); }
+    }
+#pragma unroll
+    for (int j = 0; j < VEC; ++j) {
+      red1[k * C + v * VEC + j] = s1[j];
+      red2[k * C + v * VEC + j] = s2[j];
+    }
+  }
+  __syncthreads();
+  const int cg = C / G;
+  for (int g = t; g < G; g += blockDim.x) {
+    float a = 0.f, c = 0.f;
+    for (int kk = 0; kk < KP; ++kk)
+      for (int ch = g * cg; ch < (g + 1) * cg; ++ch) {
+        a += red1[kk * C + ch];
+        c += red2[kk * C + ch];
+      }
+    float* out = partial + ((static_cast<int64_t>(b) * nchunk + chunk) * G + g) * 2;
+    out[0] = a;
+    out[1] = c;
+  }
+}
+
+__global__ __launch_bounds__(kGnMaxThreads) void gn_finalize_kernel(
+    const float* __restrict__ partial, int64_t nchunk, const float* __restrict__ stale, float* __restrict__ stats_out,
+    float* __restrict__ coef, int G, int P, int p, double n, float eps) {
+  __shared__ double r1[kGnMaxThreads], r2[kGnMaxThreads];
+  const int b = blockIdx.x;
+  const int t = threadIdx.x;
+  const int nparts = kGnMaxThreads / G;  // G <= 256 (host check)
+  const int g = t % G, part = t / G;
+  double a = 0.0, c = 0.0;
+  if (part < nparts) {
+    for (int64_t ch = part; ch < nchunk; ch += nparts) {
+      const float* pr = partial + ((static_cast<int64_t>(b) * nchunk + ch) * G + g) * 2;
+      a += pr[0];
+      c += pr[1];
+    }
+  }
+  r1[t] = a;
+  r2[t] = c;
+  __syncthreads();
+  if (t < G) {
+    double s1 = 0.0, s2 = 0.0;
+    for (int q = 0; q < nparts; ++q) { s1 += r1[q * G + t]; s2 += r2[q * G + t]; }
+    float* so = stats_out + ((static_cast<int64_t>(b) * P + p) * G + t) * 2;
+    so[0] = static_cast<float>(s1);
+    so[1] = static_cast<float>(s2);
+    if (coef != nullptr) {
+      double T1 = s1, T2 = s2;
+      if (stale != nullptr)
+        for (int q = 0; q < P; ++q)
+          if (q != p) {
+            const float* st = stale + ((static_cast<int64_t>(b) * P + q) * G + t) * 2;
+            T1 += st[0];
+            T2 += st[1];
+          }
+      const double mean = T1 / n;
+      double var = T2 / n - mean * mean;
+      if (var < 0.0) var = 0.0;
+      const double rstd = 1.0 / sqrt(var + static_cast<double>(eps));
+      coef[(static_cast<int64_t>(b) * G + t) * 2] = static_cast<float>(mean);
+      coef[(static_cast<int64_t>(b) * G + t) * 2 + 1] = static_cast<float>(rstd);
+    }
+  }
+}
+
+template <typename T>
+__global__ __launch_bounds__(kGnMaxThreads) void gn_apply_kernel(const T* __restrict__ x, T* __restrict__ y,
+                                                                 const float* __restrict__ coef,
+                                                                 const float* __restrict__ gamma,
+                                                                 const float* __restrict__ beta, int64_t npix, int C,
+                                                                 int G, int V, int KP, int64_t ppc) {
+  constexpr int VEC = Elem<T>::kVec;
+  const int b = blockIdx.y;
+  const int t = threadIdx.x;
+  const int v = t % V, k = t / V;
+  if (k >= KP) return;
+  const int cg = C / G;
+  float a[VEC], sh[VEC];
+#pragma unroll
+  for (int j = 0; j < VEC; ++j) {
+    const int c = v * VEC + j;
+    const int g = c / cg;
+    const float mean = coef[(b * G + g) * 2], rstd = coef[(b * G + g) * 2 + 1];
+    a[j] = rstd * gamma[c];
+    sh[j] = fmaf(-mean, a[j], beta[c]);
+  }
+  const int64_t p0 = static_cast<int64_t>(blockIdx.x) * ppc;
+  const int64_t p1 = (p0 + ppc < npix) ? p0 + ppc : npix;
+  const int64_t off = static_cast<int64_t>(b) * npix * V;
+  const uint4* xv = reinterpret_cast<const uint4*>(x) + off;
+  uint4* yv = reinterpret_cast<uint4*>(y) + off;
+  int64_t pix = p0 + k;
+  for (; pix + KP < p1; pix += 2 * KP) {
+    const uint4 u0 = xv[pix * V + v];
+    const uint4 u1 = xv[(pix + KP) * V + v];
+    float f0[VEC], f1[VEC];
+    Elem<T>::unpack(u0, f0);
+    Elem<T>::unpack(u1, f1);
+#pragma unroll
+    for (int j = 0; j < VEC; ++j) { f0[j] = fmaf(f0[j], a[j], sh[j]); f1[j] = fmaf(f1[j], a[j], sh[j]); }
+    yv[pix * V + v] = Elem<T>::pack(f0);
+    yv[(pix + KP) * V + v] = Elem<T>::pack(f1);
+  }
+  if (pix < p1) {
+    float f0[VEC];
+    Elem<T>::unpack(xv[pix * V + v], f0);
+#pragma unroll
+    for (int j = 0; j < VEC; ++j) f0[j] = fmaf(f0[j], a[j], sh[j]);
+    yv[pix * V + v] = Elem<T>::pack(f0);
+  }
+}
+
+template <typename T>
+static hipError_t gn_run(T* y, float* stats_out, const T* x, const float* stale, const float* gamma,
+                         const float* beta, int64_t B, int64_t H, int64_t W, int64_t C, int64_t G, int64_t P,
+                         int64_t p, int64_t rows, float eps, void* ws, hipStream_t s) {
+  const GnGeom g = gn_geom(B, rows, W, C, sizeof(T) == 2);
+  float* partial = static_cast<float*>(ws);
+  float* coef = partial + B * g.nstat * G * 2;
+  hipLaunchKernelGGL(gn_partial_kernel<T>, dim3(static_cast<unsigned>(g.nstat), static_cast<unsigned>(B)),
+                     dim3(g.threads), 0, s, x, partial, g.npix, static_cast<int>(C), static_cast<int>(G), g.V, g.KP,
+                     g.stat_ppc, g.nstat);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  const double n = static_cast<double>(H) * static_cast<double>(W) * static_cast<double>(C / G);
+  hipLaunchKernelGGL(gn_finalize_kernel, dim3(static_cast<unsigned>(B)), dim3(kGnMaxThreads), 0, s, partial, g.nstat,
+                     stale, stats_out, y ? coef : nullptr, static_cast<int>(G), static_cast<int>(P),
+                     static_cast<int>(p), n, eps);
+  err = hipGetLastError();
+  if (err != hipSuccess || y == nullptr) return err;
+  hipLaunchKernelGGL(gn_apply_kernel<T>, dim3(static_cast<unsigned>(g.napply), static_cast<unsigned>(B)),
+                     dim3(g.threads), 0, s, x, y, coef, gamma, beta, g.npix, static_cast<int>(C), static_cast<int>(G),
+                     g.V, g.KP, g.apply_ppc);
+  return hipGetLastError();
+}
+
+hipError_t launch_groupnorm(void* y, float* stats_out, const void* x, const float* stale_stats, const float* gamma,
+                            const float* beta, int64_t B, int64_t H, int64_t W, int64_t C, int64_t G, int64_t P,
+                            int64_t p, int64_t rows, float eps, void* ws, bool bf16, hipStream_t s) {
+  if (bf16)
+    return gn_run(static_cast<uint16_t*>(y), stats_out, static_cast<const uint16_t*>(x), stale_stats, gamma, beta, B,
+                  H, W, C, G, P, p, rows, eps, ws, s);
+  return gn_run(static_cast<float*>(y), stats_out, static_cast<const float*>(x), stale_stats, gamma, beta, B, H, W, C,
+                G, P, p, rows, eps, ws, s);
+}
+
+}  // namespace dpp

@@ -1,0 +1,79 @@
+"""Call sequence of one device's share of a displaced-patch-parallel layer step.
+
+One emulated device (patch p of P row bands) runs GroupNorm -> 3x3 conv ->
+splice -> self-attention with identity Q/K/V projections: the conv output of
+its rows is the query set, and K = V = its private full-image buffer, i.e. the
+previous step's conv output with its own rows replaced by the fresh ones.  The
+previous step is the synchronous first step (DistriFusion reading notes,
+Introduction, fourth paragraph): per-patch raw GroupNorm sums of the stale
+input, GroupNorm and conv of the whole stale image.
+
+Every arithmetic step runs in libdpp's kernels; this module only allocates
+device buffers (torch) and issues the calls on the current stream.  Each
+emulated patch owns a private K/V buffer so that one patch's fresh rows never
+reach another patch within the same step (on real devices they arrive with the
+next step's exchange).
+"""
+from __future__ import annotations
+
+import torch
+
+from . import _lib as L
+
+
+class DisplacedLayer:
+    def __init__(self, B, H, W, C, P, G, heads, dtype, device="cuda", eps=1e-5, head_dim=64):
+        if H % P:
+            raise ValueError("H must divide into P equal row bands")
+        self.B, self.H, self.W, self.C, self.P, self.G = B, H, W, C, P, G
+        self.heads, self.D, self.eps = heads, head_dim, eps
+        self.R = H // P
+        self.dtype = dtype
+        self.device = device
+        f32 = dict(dtype=torch.float32, device=device)
+        act = dict(dtype=dtype, device=device)
+        self.stats_prev = torch.zeros(B, P, G, 2, **f32)   # stale sums (previous step)
+        self.stats_next = torch.zeros(B, P, G, 2, **f32)   # fresh sums (this step)
+        self.a1 = torch.empty(B, H, W, C, **act)           # previous GN output (conv halo source)
+        self.a2 = torch.empty(B, H, W, C, **act)           # previous conv output (stale K/V)
+        self.kv = [None] * P                               # private spliced K/V buffers
+        self.y1 = torch.empty(B, self.R, W, C, **act)
+        self.y2 = torch.empty(B, self.R, W, C, **act)
+        self.o = torch.empty(B, self.R * W, C, **act)
+        gw = max(L.dpp_groupnorm_stale_workspace_bytes(B, H, W, C, G),
+                 L.dpp_groupnorm_stale_workspace_bytes(B, self.R, W, C, G))
+        self.gn_ws = torch.empty(max(gw, 256), dtype=torch.uint8, device=device)
+        aw = L.dpp_self_attn_workspace_bytes(B, self.R * W, H * W, heads, head_dim,
+                                             L.DPP_BF16 if dtype == torch.bfloat16 else L.DPP_F32)
+        self.attn_ws = torch.empty(aw, dtype=torch.uint8, device=device) if aw else None
+        self._stats_full = torch.zeros(B, 1, G, 2, **f32)
+
+    def band(self, x, p):
+        """Rows of patch p of a [B,H,W,C] tensor, contiguous."""
+        return x[:, p * self.R:(p + 1) * self.R].contiguous()
+
+    def synchronous_step(self, x_stale, gamma, beta, weight, bias):
+        """Previous-step state from the stale input (every patch fresh)."""
+        for q in range(self.P):
+            L.dpp_groupnorm_stale(None, self.stats_prev, self.band(x_stale, q), None, None, None,
+                                  self.H, self.G, self.P, q, self.eps, self.gn_ws)
+        L.dpp_groupnorm_stale(self.a1, self._stats_full, x_stale, None, gamma, beta,
+                              self.H, self.G, 1, 0, self.eps, self.gn_ws)
+        L.dpp_conv3x3_halo(self.a2, self.a1, None, weight, bias, self.H, 0)
+        for p in range(self.P):
+            if self.kv[p] is None:
+                self.kv[p] = torch.empty_like(self.a2)
+            self.kv[p].copy_(self.a2)
+
+    def patch_step(self, p, x_patch, gamma, beta, weight, bias):
+        """Patch p's share of the current step; returns the attention output
+        [B, R*W, C] (a buffer reused by the next call)."""
+        r0 = p * self.R
+        L.dpp_groupnorm_stale(self.y1, self.stats_next, x_patch, self.stats_prev, gamma, beta,
+                              self.H, self.G, self.P, p, self.eps, self.gn_ws)
+        L.dpp_conv3x3_halo(self.y2, self.y1, self.a1, weight, bias, self.H, r0)
+        L.dpp_splice_patch(self.kv[p], self.y2, r0)
+        kv = self.kv[p].view(self.B, self.H * self.W, self.C)
+        L.dpp_self_attn_displaced(self.o, self.y2.view(self.B, self.R * self.W, self.C), kv, kv,
+                                  self.heads, self.D, 0.0, self.attn_ws)
+        return self.o

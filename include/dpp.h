@@ -1,0 +1,198 @@
+/*
+ * dpp.h -- C ABI of libdpp: one device's share of a displaced-patch-parallel
+ * diffusion denoising step, as gfx950 (MI355X) HIP kernels.
+ *
+ * The method (DistriFusion reading notes, Introduction, fourth paragraph):
+ * the image is split into patches, one per device; after a synchronous first
+ * step, each device computes only its own patch from fresh activations and
+ * takes the rest of the image (global context, patch interaction) from the
+ * activations of the previous denoising step.  The layers that need the rest
+ * of the image are GroupNorm, 3x3 convolution and self-attention
+ * (DistriFusion architecture article: DistriGroupNorm, DistriConv2dPP,
+ * DistriSelfAttentionPP); after each layer the patch outputs are gathered and
+ * concatenated along the height axis into a reused full-image buffer
+ * (same article, communication section).  On one device that gather becomes
+ * dpp_splice_patch.  Classifier-free guidance combines a conditional and an
+ * unconditional branch, and the relative error between their noise
+ * predictions (rel-MAE) is the denoising discrepancy that drives
+ * condition-split scheduling (Hybridiff technical summary, sections 2A, 2B).
+ *
+ * Conventions for every call:
+ *  - Layout is token-major (NHWC): an activation is [B,H,W,C], row-major,
+ *    contiguous; a patch is the row band [row0, row0+rows) of it, stored
+ *    contiguously as [B,rows,W,C]; token t = row*W + col.
+ *  - Every pointer is a device pointer owned by the caller.  The library
+ *    allocates, frees and synchronises nothing, keeps no state between calls,
+ *    and may be called from several host threads.
+ *  - dtype selects the storage type of activations and conv weights:
+ *    DPP_BF16 (bf16 bit patterns) or DPP_F32.  GroupNorm gamma/beta, conv
+ *    bias, group statistics and the rel-MAE scalar are always float32.
+ *    Arithmetic is float32 (statistics float64) with one rounding to the
+ *    output type at the end.
+ *  - stream is a hipStream_t passed as void* (NULL = the null stream).  Work
+ *    is enqueued on it and the call returns at once; faults inside a kernel
+ *    surface at the caller's next synchronisation.
+ *  - Return value: DPP_OK, or a negative DPP_ERR_* code.  Arguments are
+ *    validated on the host before anything is enqueued: on an error nothing
+ *    is launched and nothing is written.
+ *  - Workspaces are caller-owned device scratch, at least the size the
+ *    matching *_workspace_bytes() returns, 256-byte aligned.  They need no
+ *    initialisation and hold nothing useful after the call.  Calls that
+ *    share a workspace must be ordered (same stream).
+ */
+#ifndef DPP_H_
+#define DPP_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DPP_VERSION 1
+
+enum dpp_dtype { DPP_BF16 = 0, DPP_F32 = 1 };
+
+enum dpp_status {
+  DPP_OK = 0,
+  DPP_ERR_NULL = -1,        /* a required pointer is NULL                    */
+  DPP_ERR_SHAPE = -2,       /* non-positive size, band outside the image,
+                               C % G != 0, heads*head_dim > ld, ...          */
+  DPP_ERR_DTYPE = -3,       /* dtype is neither DPP_BF16 nor DPP_F32         */
+  DPP_ERR_ALIGN = -4,       /* a pointer or row stride is not 16-byte aligned
+                               where the kernel reads 16-byte vectors        */
+  DPP_ERR_ALIAS = -5,       /* an output overlaps an input it may not alias  */
+  DPP_ERR_WORKSPACE = -6,   /* workspace NULL or smaller than required       */
+  DPP_ERR_UNSUPPORTED = -7, /* valid shape this build has no kernel for      */
+  DPP_ERR_LAUNCH = -8       /* the HIP runtime rejected a launch             */
+};
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* dpp_strerror(int status);
+
+/* DPP_VERSION of the built library. */
+int dpp_version(void);
+
+/*
+ * a1 -- splice.  Writes the fresh patch into rows [row0, row0+rows) of the
+ * full-image buffer: full[b, row0+i, w, c] = patch[b, i, w, c].  Other rows
+ * are left untouched.  This is the local stand-in for gathering every
+ * device's patch output and concatenating along the height axis into the
+ * reused full-image buffer (DistriFusion architecture article, communication
+ * section); on one device, only the own patch is fresh, so the buffer holds
+ * fresh own rows and the previous step's rows elsewhere (DistriFusion reading
+ * notes, Introduction, fourth paragraph).
+ *   full  [B,H,W,C] in/out.   patch [B,rows,W,C] in; must not overlap full.
+ *   Requires 0 <= row0, rows >= 1, row0 + rows <= H.  Bit-exact copy.
+ */
+int dpp_splice_patch(void* full, const void* patch,
+                     int64_t B, int64_t H, int64_t W, int64_t C,
+                     int64_t row0, int64_t rows, int dtype, void* stream);
+
+/*
+ * a2 -- GroupNorm with stale statistics (DistriGroupNorm; DistriFusion
+ * architecture article, normalisation section).  Normalises patch p with the
+ * group statistics of the spliced image: the other patches' contribution is
+ * their raw sums from the previous step, the own patch's is recomputed from
+ * the fresh x.  Per batch b and group g (C/G channels each):
+ *   s1, s2   = sum of x, x^2 over the patch (rows x W x C/G values)
+ *   T_k      = s_k + sum_{q != p} stale_stats[b,q,g,k]
+ *   mean     = T_1/n,  var = max(T_2/n - mean^2, 0),  n = H*W*C/G
+ *   y        = (x - mean)/sqrt(var + eps) * gamma[c] + beta[c]
+ *   stats_out[b,p,g,:] = (s1, s2)   (the next step's stale_stats slot p;
+ *                                    other slots are not written)
+ *   x, y        [B,rows,W,C]   (y may equal NULL: only stats_out is produced,
+ *                               the first half of the synchronous step; then
+ *                               gamma, beta and stale_stats may be NULL)
+ *   stale_stats [B,P,G,2] float32, slot p ignored; NULL allowed when P == 1
+ *   stats_out   [B,P,G,2] float32; must not overlap stale_stats or y
+ *   gamma, beta [C] float32
+ *   Requires C % G == 0, 0 <= p < P, 1 <= rows <= H, C <= 8*256 (bf16) or
+ *   4*256 (f32), C % 8 == 0 (bf16) or C % 4 == 0 (f32), x and y 16-byte
+ *   aligned.  Workspace: dpp_groupnorm_stale_workspace_bytes().
+ */
+size_t dpp_groupnorm_stale_workspace_bytes(int64_t B, int64_t rows, int64_t W,
+                                           int64_t C, int64_t G);
+int dpp_groupnorm_stale(void* y, float* stats_out, const void* x,
+                        const float* stale_stats, const float* gamma,
+                        const float* beta, int64_t B, int64_t H, int64_t W,
+                        int64_t C, int64_t G, int64_t P, int64_t p,
+                        int64_t rows, float eps, void* workspace,
+                        size_t workspace_bytes, int dtype, void* stream);
+
+/*
+ * a3 -- 3x3 convolution of the patch rows with halo rows from the stale image
+ * (DistriConv2dPP; DistriFusion architecture article, conv section; only the
+ * own region is computed: DistriFusion reading notes, Introduction, fourth
+ * paragraph).  Stride 1, zero padding 1 at the image border, cross-
+ * correlation:
+ *   y[b,i,w,o] = bias[o] + sum_{dy,dx in 0..2} sum_c
+ *                weight[o,dy,dx,c] * S[b, row0+i+dy-1, w+dx-1, c]
+ * where S is the spliced image: rows [row0, row0+rows) from x, rows row0-1
+ * and row0+rows (the halos) from stale_full, zero outside the image.  No
+ * other row of stale_full is read.
+ *   x          [B,rows,W,Cin]
+ *   stale_full [B,H,W,Cin]; may be NULL when both halo rows are outside the
+ *              image (row0 == 0 and rows == H)
+ *   weight     [Cout,3,3,Cin] (dtype)   bias [Cout] float32 or NULL
+ *   y          [B,rows,W,Cout]; must not overlap any input
+ *   bf16 requires Cin % 64 == 0, Cout % 16 == 0 and 16-byte aligned x,
+ *   stale_full, weight, y.  f32 has no divisibility requirement.
+ */
+int dpp_conv3x3_halo(void* y, const void* x, const void* stale_full,
+                     const void* weight, const float* bias, int64_t B,
+                     int64_t H, int64_t W, int64_t Cin, int64_t Cout,
+                     int64_t row0, int64_t rows, int dtype, void* stream);
+
+/*
+ * a4 -- displaced self-attention (DistriSelfAttentionPP; DistriFusion
+ * architecture article, attention section).  The patch's queries attend over
+ * all tokens of the spliced full-image K/V buffer (fresh own rows, previous
+ * step's rows elsewhere: DistriFusion reading notes, Introduction, fourth
+ * paragraph).  Per batch b, head h (channels [h*D, (h+1)*D)) and query i:
+ *   o[b,i,h] = sum_j softmax_j(scale * <q[b,i,h], k[b,j,h]>) v[b,j,h]
+ *   q [B,n_q,ld_q], k and v [B,n_kv,ld_kv], o [B,n_q,ld_o]: row strides in
+ *   elements, ld >= heads*head_dim; k and v may be the same pointer.
+ *   scale <= 0 selects 1/sqrt(head_dim).  o must not overlap q, k or v.
+ *   bf16 requires head_dim == 64, 16-byte aligned pointers and ld % 8 == 0.
+ *   f32 requires head_dim in {16, 32, 64, 128}.
+ *   workspace: optional.  With workspace_bytes >=
+ *   dpp_self_attn_workspace_bytes(...) the key range may be split across
+ *   workgroups and merged in a second pass (more parallelism for short query
+ *   ranges); with NULL / 0 the call runs unsplit.
+ */
+size_t dpp_self_attn_workspace_bytes(int64_t B, int64_t n_q, int64_t n_kv,
+                                     int64_t heads, int64_t head_dim,
+                                     int dtype);
+int dpp_self_attn_displaced(void* o, const void* q, const void* k,
+                            const void* v, int64_t B, int64_t n_q,
+                            int64_t n_kv, int64_t heads, int64_t head_dim,
+                            int64_t ld_q, int64_t ld_kv, int64_t ld_o,
+                            float scale, void* workspace,
+                            size_t workspace_bytes, int dtype, void* stream);
+
+/*
+ * a5 -- classifier-free guidance combine and denoising discrepancy
+ * (Hybridiff technical summary, section 2A: conditional and unconditional
+ * branches; section 2B: rel-MAE between their noise predictions).
+ *   eps[i]  = eps_u[i] + guidance * (eps_c[i] - eps_u[i])
+ *   *relmae = sum_i |eps_c[i] - eps_u[i]| / sum_i |eps_u[i]|
+ *             (float64 accumulation, deterministic order; 0/0 -> NaN,
+ *              x/0 -> +inf)
+ *   eps, eps_c, eps_u: n elements; eps may be exactly eps_c or eps_u, and
+ *   must not partly overlap them.  relmae: one device float32, or NULL to
+ *   skip the reduction.  Workspace: dpp_cfg_combine_workspace_bytes(n)
+ *   (may be NULL when relmae is NULL).
+ */
+size_t dpp_cfg_combine_workspace_bytes(int64_t n);
+int dpp_cfg_combine_relmae(void* eps, float* relmae, const void* eps_c,
+                           const void* eps_u, int64_t n, float guidance,
+                           void* workspace, size_t workspace_bytes, int dtype,
+                           void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DPP_H_ */

@@ -225,15 +225,17 @@ def previous_step_state(x_stale, gamma, beta, weight, bias, P: int, G: int, eps:
 
     Returns dict: stale_stats [B,P,G,2] raw sums of each patch of x_stale;
     a1 = GN(x_stale) [B,H,W,C] (stored: bf16-rounded when bf16); a2 =
-    conv(a1) [B,H,W,C] (stored)."""
+    conv(a1) [B,H,W,C] (stored); a1_exact, a2_exact: the same layer outputs
+    before storage rounding (a2_exact is computed from the stored a1)."""
     xs = _f64(x_stale)
     B, H, W, C = xs.shape
     R = H // P
     stats = np.stack([patch_sums(xs[:, q * R:(q + 1) * R], G) for q in range(P)], axis=1)
-    a1, _ = groupnorm_stale(xs, None, gamma, beta, H, G, 0, eps)
-    a1 = _store(a1, bf16)
-    a2 = _store(conv3x3_halo(a1, None, weight, bias, 0), bf16)
-    return {"stale_stats": stats, "a1": a1, "a2": a2}
+    a1_exact, _ = groupnorm_stale(xs, None, gamma, beta, H, G, 0, eps)
+    a1 = _store(a1_exact, bf16)
+    a2_exact = conv3x3_halo(a1, None, weight, bias, 0)
+    a2 = _store(a2_exact, bf16)
+    return {"stale_stats": stats, "a1": a1, "a2": a2, "a1_exact": a1_exact, "a2_exact": a2_exact}
 
 
 def displaced_block(x_fresh, state, gamma, beta, weight, bias, P: int, p: int, G: int, heads: int,
@@ -244,19 +246,24 @@ def displaced_block(x_fresh, state, gamma, beta, weight, bias, P: int, p: int, G
     previous_step_state(...) of the stale input.  Identity projections: the
     conv output of the patch is Q; K = V = the previous step's conv output with
     the patch's rows replaced by the fresh conv output (reading R6).
-    Returns dict y1 (GN out), y2 (conv out), kv (spliced buffer), o
-    (attention out; only attn_rows=(b_idx, q_idx) when given), stats (fresh
+    Returns dict y1 (GN out), y2 (conv out), kv (spliced buffer) as stored,
+    y1_exact, y2_exact, kv_exact (the same before storage rounding; each
+    stage computed from the previous stage's stored values), o (attention
+    out, unrounded; only attn_rows=(b_idx, q_idx) when given), stats (fresh
     sums)."""
     xf = _f64(x_fresh)
     B, H, W, C = xf.shape
     R = H // P
     r0 = p * R
     x_p = xf[:, r0:r0 + R]
-    y1, fresh = groupnorm_stale(x_p, state["stale_stats"], gamma, beta, H, G, p, eps)
-    y1 = _store(y1, bf16)
-    y2 = _store(conv3x3_halo(y1, state["a1"], weight, bias, r0), bf16)
+    y1_exact, fresh = groupnorm_stale(x_p, state["stale_stats"], gamma, beta, H, G, p, eps)
+    y1 = _store(y1_exact, bf16)
+    y2_exact = conv3x3_halo(y1, state["a1"], weight, bias, r0)
+    y2 = _store(y2_exact, bf16)
     kv = splice(state["a2"], y2, r0)
+    kv_exact = splice(state["a2_exact"], y2_exact, r0)
     q = y2.reshape(B, R * W, C)
     kvt = kv.reshape(B, H * W, C)
     o = self_attn_displaced(q, kvt, kvt, heads, rows=attn_rows)
-    return {"y1": y1, "y2": y2, "kv": kv, "o": o, "stats": fresh}
+    return {"y1": y1, "y2": y2, "kv": kv, "y1_exact": y1_exact, "y2_exact": y2_exact, "kv_exact": kv_exact,
+            "o": o, "stats": fresh}

@@ -1,0 +1,67 @@
+"""Shared helpers for the GPU tests: host <-> device transfer of the seeded
+inputs and the parity bar.
+
+The bar: float32 paths max-abs-err <= 1e-4; bf16 paths max-abs-err <= 2e-2 x
+RMS of the oracle output, measured beyond the output's own storage rounding:
+a bf16 result cannot be nearer the exact value than half a bf16 ulp of that
+value, so each element's distance is reduced by that half ulp before the
+comparison (the raw max-abs-err is printed as well); the rel-MAE scalar
+within 1e-3 relative; splices bit-exact."""
+import numpy as np
+
+F32_TOL = 1e-4
+BF16_TOL = 2e-2
+REL_TOL = 1e-3
+
+
+def to_dev(a, dtype: str):
+    """Stored numpy tensor (uint16 bf16 bits or float32) -> CUDA tensor."""
+    import torch
+    if dtype == "bf16":
+        t = torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16)
+    else:
+        t = torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32))
+    return t.cuda()
+
+
+def to_host(t) -> np.ndarray:
+    """CUDA tensor -> float64 numpy (bf16 widened exactly)."""
+    import torch
+    return t.detach().to(torch.float32).cpu().numpy().astype(np.float64)
+
+
+def bits(t) -> np.ndarray:
+    import torch
+    if t.dtype == torch.bfloat16:
+        return t.detach().view(torch.int16).cpu().numpy().view(np.uint16)
+    return t.detach().cpu().numpy().view(np.uint32)
+
+
+def half_ulp_bf16(v) -> np.ndarray:
+    """Half the spacing of bf16 values at |v| (8 significant bits): the
+    largest distance between v and its bf16 rounding."""
+    a = np.abs(np.asarray(v, dtype=np.float64))
+    e = np.floor(np.log2(np.where(a > 0, a, 1.0)))
+    h = np.exp2(e - 8.0)
+    return np.where(a >= 2.0 ** -126, h, 2.0 ** -134)
+
+
+def parity(got, want, dtype: str, what: str):
+    got = np.asarray(got, dtype=np.float64)
+    want = np.asarray(want, dtype=np.float64)
+    assert got.shape == want.shape, (what, got.shape, want.shape)
+    assert np.all(np.isfinite(got)), f"{what}: non-finite output"
+    diff = np.abs(got - want)
+    err = float(diff.max())
+    rms = float(np.sqrt(np.mean(want * want)))
+    if dtype == "bf16":
+        excess = float(np.maximum(diff - half_ulp_bf16(want), 0.0).max())
+        ok = excess <= BF16_TOL * rms
+        bar = f"beyond half an output ulp {excess:.3e} = {excess / max(rms, 1e-30):.3e} x rms <= {BF16_TOL} x rms"
+    else:
+        ok = err <= F32_TOL
+        bar = f"<= {F32_TOL}"
+    msg = f"{what}: max-abs-err {err:.3e}, rms {rms:.3e}, err/rms {err / max(rms, 1e-30):.3e} (bar: {bar})"
+    print(msg, flush=True)
+    assert ok, msg
+    return err, rms

@@ -1,0 +1,190 @@
+"""Host-side checks of the C ABI: the library loads, exports every symbol the
+header declares, and rejects invalid arguments with the documented status
+before touching the device (these calls never launch anything, so they run
+without a GPU).  Pointers here are fake aligned addresses: validation reads no
+memory."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import displaced_patch_parallelism_net_amd as dpp
+from displaced_patch_parallelism_net_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+L = _lib.LIB
+OK, NULL, SHAPE, DTYPE, ALIGN, ALIAS, WS, UNSUP = 0, -1, -2, -3, -4, -5, -6, -7
+BF16, F32 = 0, 1
+A = 0x10000000        # fake 16-byte aligned device addresses, far apart
+Bp = 0x20000000
+Cp = 0x30000000
+Dp = 0x40000000
+Ep = 0x50000000
+WSP = 0x60000000
+
+
+def header_symbols():
+    text = open(os.path.join(ROOT, "include", "dpp.h")).read()
+    return sorted(set(re.findall(r"\b(dpp_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_symbols_exported_and_bound():
+    syms = header_symbols()
+    assert len(syms) == 10, syms
+    for s in syms:
+        assert hasattr(L, s), s
+        assert s in _lib.SIGNATURES, s
+    assert set(_lib.SIGNATURES) == set(syms)
+
+
+def test_exported_symbols_via_nm():
+    import subprocess
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\bT (dpp_[a-z0-9_]+)", out))
+    assert set(header_symbols()) <= exported
+
+
+def test_version_and_strerror():
+    assert dpp.dpp_version() == 1
+    for code in range(0, -9, -1):
+        assert dpp.dpp_strerror(code).startswith("DPP")
+    assert "unknown" in dpp.dpp_strerror(17)
+
+
+# ----------------------------------------------------------------- splice
+def splice(full=A, patch=Bp, B=1, H=8, W=4, C=16, row0=0, rows=2, dtype=BF16):
+    return L.dpp_splice_patch(full, patch, B, H, W, C, row0, rows, dtype, None)
+
+
+def test_splice_validation():
+    assert splice(dtype=7) == DTYPE
+    assert splice(full=None) == NULL
+    assert splice(patch=None) == NULL
+    assert splice(rows=0) == SHAPE
+    assert splice(row0=-1) == SHAPE
+    assert splice(row0=7, rows=2) == SHAPE
+    assert splice(W=0) == SHAPE
+    assert splice(patch=A + 64) == ALIAS          # patch inside the full buffer
+    assert splice(B=70000) == UNSUP
+
+
+# ----------------------------------------------------------------- GroupNorm
+def gn(y=A, so=Bp, x=Cp, st=Dp, gamma=Ep, beta=Ep + 4096, B=1, H=8, W=4, C=64, G=8, P=2, p=0, rows=4, eps=1e-5,
+       ws=WSP, wsb=1 << 20, dtype=BF16):
+    return L.dpp_groupnorm_stale(y, so, x, st, gamma, beta, B, H, W, C, G, P, p, rows, eps, ws, wsb, dtype, None)
+
+
+def test_groupnorm_validation():
+    assert gn(dtype=2) == DTYPE
+    assert gn(x=None) == NULL
+    assert gn(so=None) == NULL
+    assert gn(gamma=None) == NULL
+    assert gn(st=None) == NULL                     # P > 1 needs stale sums
+    assert gn(C=60, G=8) == SHAPE                  # C % G
+    assert gn(p=2) == SHAPE
+    assert gn(rows=9) == SHAPE
+    assert gn(eps=-1.0) == SHAPE
+    assert gn(C=20, G=4) == UNSUP                  # bf16 needs C % 8
+    assert gn(C=4096, G=32) == UNSUP               # more than 256 vectors per pixel
+    assert gn(x=Cp + 2) == ALIGN
+    assert gn(y=A + 8) == ALIGN
+    assert gn(so=Dp) == ALIAS                      # stats_out == stale_stats
+    assert gn(y=Cp) == ALIAS                       # in place is not allowed
+    assert gn(ws=None) == WS
+    assert gn(wsb=16) == WS
+    assert gn(ws=Cp) == ALIAS
+
+
+def test_groupnorm_stats_only_mode_needs_no_affine():
+    # y == NULL: gamma/beta/stale may be NULL; validation passes all the way
+    # to the workspace check
+    assert gn(y=None, gamma=None, beta=None, st=None, ws=None) == WS
+    assert gn(y=None, st=None, P=1) != NULL
+
+
+def test_groupnorm_workspace_query():
+    assert dpp.dpp_groupnorm_stale_workspace_bytes(1, 30, 240, 640, 32) > 0
+    assert dpp.dpp_groupnorm_stale_workspace_bytes(1, 30, 240, 630, 32) == 0
+    assert dpp.dpp_groupnorm_stale_workspace_bytes(0, 30, 240, 640, 32) == 0
+
+
+# ----------------------------------------------------------------- conv
+def conv(y=A, x=Bp, st=Cp, w=Dp, bias=Ep, B=1, H=8, W=16, Cin=64, Cout=64, row0=2, rows=2, dtype=BF16):
+    return L.dpp_conv3x3_halo(y, x, st, w, bias, B, H, W, Cin, Cout, row0, rows, dtype, None)
+
+
+def test_conv_validation():
+    assert conv(dtype=-1) == DTYPE
+    assert conv(y=None) == NULL
+    assert conv(w=None) == NULL
+    assert conv(st=None) == NULL                   # halos inside the image need the stale image
+    assert conv(row0=6, rows=3) == SHAPE
+    assert conv(Cout=0) == SHAPE
+    assert conv(Cin=32) == UNSUP                   # bf16 needs Cin % 64
+    assert conv(Cout=24) == UNSUP                  # bf16 needs Cout % 16
+    assert conv(x=Bp + 4) == ALIGN
+    assert conv(y=Bp) == ALIAS
+    assert conv(y=Cp + 256) == ALIAS               # inside the stale image
+    assert conv(y=Dp) == ALIAS
+    # f32 has no divisibility or alignment requirement
+    assert conv(Cin=3, Cout=5, dtype=F32, x=None) == NULL
+
+
+def test_conv_whole_image_needs_no_stale():
+    assert conv(st=None, row0=0, rows=8, y=None) == NULL   # reaches the pointer checks only
+    assert conv(st=None, row0=0, rows=7) == NULL
+
+
+# ----------------------------------------------------------------- attention
+def attn(o=A, q=Bp, k=Cp, v=Dp, B=1, nq=100, nkv=300, heads=2, D=64, ldq=128, ldkv=128, ldo=128, scale=0.0, ws=None,
+         wsb=0, dtype=BF16):
+    return L.dpp_self_attn_displaced(o, q, k, v, B, nq, nkv, heads, D, ldq, ldkv, ldo, scale, ws, wsb, dtype, None)
+
+
+def test_attention_validation():
+    assert attn(dtype=3) == DTYPE
+    assert attn(q=None) == NULL
+    assert attn(v=None) == NULL
+    assert attn(nq=0) == SHAPE
+    assert attn(ldq=64) == SHAPE
+    assert attn(D=32) == UNSUP                     # bf16 kernels are head_dim 64
+    assert attn(D=48, dtype=F32, ldq=96, ldkv=96, ldo=96) == UNSUP
+    assert attn(q=Bp + 2) == ALIGN
+    assert attn(ldkv=132) == ALIGN
+    assert attn(o=Cp) == ALIAS
+    assert attn(o=Bp + 128) == ALIAS
+    assert attn(ws=A, wsb=1024) == ALIAS
+
+
+def test_attention_workspace_query():
+    # short query ranges are split over the keys; the split needs workspace
+    assert dpp.dpp_self_attn_workspace_bytes(1, 1024, 4096, 10, 64, BF16) > 0
+    assert dpp.dpp_self_attn_workspace_bytes(1, 1024, 4096, 10, 64, F32) == 0
+    assert dpp.dpp_self_attn_workspace_bytes(1, 1024, 4096, 10, 32, BF16) == 0
+    assert dpp.dpp_self_attn_workspace_bytes(1, 0, 4096, 10, 64, BF16) == 0
+
+
+# ----------------------------------------------------------------- CFG
+def cfg(eps=A, rel=Bp, c=Cp, u=Dp, n=1000, w=7.5, ws=WSP, wsb=1 << 16, dtype=BF16):
+    return L.dpp_cfg_combine_relmae(eps, rel, c, u, n, w, ws, wsb, dtype, None)
+
+
+def test_cfg_validation():
+    assert cfg(dtype=5) == DTYPE
+    assert cfg(c=None) == NULL
+    assert cfg(n=0) == SHAPE
+    assert cfg(eps=Cp + 2) == ALIAS                # partial overlap with eps_c
+    assert cfg(ws=None) == WS
+    assert cfg(wsb=8) == WS
+    assert cfg(ws=A) == ALIAS
+    assert cfg(rel=A + 16) == ALIAS
+    # relmae == NULL skips the reduction: no workspace needed (reaches launch)
+    assert dpp.dpp_cfg_combine_workspace_bytes(1 << 16) >= 16
+    assert dpp.dpp_cfg_combine_workspace_bytes(0) == 0
+
+
+def test_binding_raises_on_error_status():
+    with pytest.raises(dpp.DppError) as ei:
+        _lib._check("dpp_splice_patch", -2)
+    assert ei.value.status == -2

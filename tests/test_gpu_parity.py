@@ -1,0 +1,460 @@
+"""GPU parity: every libdpp call against the CPU oracle on the same seeded
+inputs, element by element.  Small shapes are compared in full (several tiles
+plus ragged tails); the full workload sizes are compared on sampled outputs
+the oracle computes one by one.  Each test prints the case it runs before
+touching the GPU."""
+import numpy as np
+import pytest
+
+import oracle
+from dpp_synth import CONFIGS, Config, attention_inputs, cfg_inputs, layer_inputs, rows_of, tokens, values
+from tests._helpers import REL_TOL, bits, parity, to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    assert torch.cuda.is_available(), "GPU tests need a visible gfx950 device"
+    import displaced_patch_parallelism_net_amd as dpp  # fails loudly without libdpp.so
+    return dpp
+
+
+def say(*a):
+    print("[case]", *a, flush=True)
+
+
+def _dpp():
+    import displaced_patch_parallelism_net_amd as dpp
+    return dpp
+
+
+def tdt(dtype):
+    return torch.bfloat16 if dtype == "bf16" else torch.float32
+
+
+# ======================================================================== splice
+SPLICE_CASES = [(n, None) for n in ["tiny_f32", "sdxl_1024", "sdxl_2048", "sdxl_3840", "cfg_pair_1024"]] + [
+    ("ragged_vec", Config("rv", B=2, H=7, W=5, C=64, P=7, G=8, heads=1, D=64)),
+    ("ragged_elem", Config("re", B=3, H=6, W=5, C=20, P=3, G=4, heads=1, D=20)),
+    ("ragged_f32", Config("rf", B=2, H=9, W=3, C=12, P=3, G=3, heads=1, D=12, dtype="f32")),
+]
+
+
+@pytest.mark.parametrize("name,cfg", SPLICE_CASES, ids=[c[0] for c in SPLICE_CASES])
+def test_splice_bit_exact(name, cfg):
+    dpp = _dpp()
+    cfg = cfg or CONFIGS[name]
+    inp = layer_inputs(cfg)
+    for p in sorted({0, cfg.P - 1, cfg.P // 2}):
+        say("splice", name, "patch", p)
+        full = to_dev(inp["x_stale"], cfg.dtype)
+        patch = to_dev(rows_of(inp["x_fresh"], cfg.row0(p), cfg.rows), cfg.dtype)
+        dpp.dpp_splice_patch(full, patch, cfg.row0(p))
+        torch.cuda.synchronize()
+        want = oracle.splice(inp["x_stale"], rows_of(inp["x_fresh"], cfg.row0(p), cfg.rows), cfg.row0(p))
+        np.testing.assert_array_equal(bits(full), want.view(np.uint16 if cfg.dtype == "bf16" else np.uint32))
+
+
+# ======================================================================== GroupNorm
+def _stale_stats(xs_vals, cfg):
+    return np.stack([oracle.patch_sums(xs_vals[:, cfg.row0(q):cfg.row0(q) + cfg.rows], cfg.G) for q in range(cfg.P)],
+                    axis=1)
+
+
+def _check_stats(got, want, n_per_group, what):
+    # raw sums in float32: |err| of s1 within 1e-5 * n (values ~ N(0,1)), s2 relative 1e-5
+    e1 = np.abs(got[..., 0] - want[..., 0]).max()
+    e2 = (np.abs(got[..., 1] - want[..., 1]) / np.abs(want[..., 1])).max()
+    print(f"{what}: sum err {e1:.3e} (n {n_per_group}), sumsq rel err {e2:.3e}", flush=True)
+    assert e1 <= 1e-5 * n_per_group and e2 <= 1e-5
+
+
+GN_CASES = [(n, None) for n in ["tiny_f32", "sdxl_1024", "sdxl_2048", "sdxl_3840", "cfg_pair_1024"]] + [
+    ("ragged_bf16", Config("rg", B=2, H=9, W=7, C=96, P=3, G=12, heads=1, D=96)),
+    ("ragged_f32", Config("rgf", B=2, H=10, W=3, C=12, P=5, G=3, heads=1, D=12, dtype="f32")),
+    ("one_patch", Config("g1", B=1, H=6, W=11, C=64, P=1, G=32, heads=1, D=64)),
+]
+
+
+@pytest.mark.parametrize("name,cfg", GN_CASES, ids=[c[0] for c in GN_CASES])
+def test_groupnorm_stale_parity(name, cfg):
+    dpp = _dpp()
+    cfg = cfg or CONFIGS[name]
+    inp = layer_inputs(cfg)
+    xf, xs = values(cfg, inp["x_fresh"]), values(cfg, inp["x_stale"])
+    stale = _stale_stats(xs.astype(np.float64), cfg).astype(np.float32)
+    d_stale = torch.from_numpy(stale).cuda()
+    gamma, beta = torch.from_numpy(inp["gamma"]).cuda(), torch.from_numpy(inp["beta"]).cuda()
+    ws = torch.empty(dpp.dpp_groupnorm_stale_workspace_bytes(cfg.B, cfg.rows, cfg.W, cfg.C, cfg.G), dtype=torch.uint8,
+                     device="cuda")
+    for p in sorted({0, cfg.P - 1}):
+        say("groupnorm", name, "patch", p)
+        x_np = rows_of(inp["x_fresh"], cfg.row0(p), cfg.rows)
+        x = to_dev(x_np, cfg.dtype)
+        y = torch.empty_like(x)
+        so = torch.full((cfg.B, cfg.P, cfg.G, 2), 7.0, device="cuda")
+        dpp.dpp_groupnorm_stale(y, so, x, d_stale if cfg.P > 1 else None, gamma, beta, cfg.H, cfg.G, cfg.P, p,
+                                cfg.gn_eps, ws)
+        torch.cuda.synchronize()
+        want_y, want_s = oracle.groupnorm_stale(values(cfg, x_np), stale if cfg.P > 1 else None, inp["gamma"],
+                                                inp["beta"], cfg.H, cfg.G, p, cfg.gn_eps)
+        parity(to_host(y), want_y, cfg.dtype, f"gn {name} p{p}")
+        so_h = so.cpu().numpy()
+        _check_stats(so_h[:, p], want_s, cfg.rows * cfg.W * cfg.C // cfg.G, f"gn stats {name} p{p}")
+        others = np.delete(so_h, p, axis=1)
+        assert np.all(others == 7.0), "stats_out slots of other patches were written"
+
+
+def test_groupnorm_stats_only_and_stale_equals_fresh():
+    # Synchronous first step: sums of every patch (stats-only calls), then
+    # normalising each patch with them equals GroupNorm of the whole image.
+    dpp = _dpp()
+    cfg = CONFIGS["sdxl_1024"]
+    inp = layer_inputs(cfg)
+    say("groupnorm sync step", cfg.name)
+    gamma, beta = torch.from_numpy(inp["gamma"]).cuda(), torch.from_numpy(inp["beta"]).cuda()
+    ws = torch.empty(dpp.dpp_groupnorm_stale_workspace_bytes(cfg.B, cfg.H, cfg.W, cfg.C, cfg.G), dtype=torch.uint8,
+                     device="cuda")
+    stats = torch.zeros(cfg.B, cfg.P, cfg.G, 2, device="cuda")
+    xfull = to_dev(inp["x_fresh"], cfg.dtype)
+    for q in range(cfg.P):
+        band = xfull[:, cfg.row0(q):cfg.row0(q) + cfg.rows].contiguous()
+        dpp.dpp_groupnorm_stale(None, stats, band, None, None, None, cfg.H, cfg.G, cfg.P, q, cfg.gn_eps, ws)
+    yfull = torch.empty_like(xfull)
+    s1 = torch.zeros(cfg.B, 1, cfg.G, 2, device="cuda")
+    dpp.dpp_groupnorm_stale(yfull, s1, xfull, None, gamma, beta, cfg.H, cfg.G, 1, 0, cfg.gn_eps, ws)
+    out = []
+    nxt = torch.zeros_like(stats)
+    for q in range(cfg.P):
+        band = xfull[:, cfg.row0(q):cfg.row0(q) + cfg.rows].contiguous()
+        y = torch.empty_like(band)
+        dpp.dpp_groupnorm_stale(y, nxt, band, stats, gamma, beta, cfg.H, cfg.G, cfg.P, q, cfg.gn_eps, ws)
+        out.append(y)
+    torch.cuda.synchronize()
+    # patch sums add up to the image sums
+    np.testing.assert_allclose(stats.sum(dim=1).cpu().numpy(), s1[:, 0].cpu().numpy(), rtol=1e-4, atol=1e-2)
+    np.testing.assert_array_equal(nxt.cpu().numpy(), stats.cpu().numpy())
+    want, _ = oracle.groupnorm_stale(values(cfg, inp["x_fresh"]), None, inp["gamma"], inp["beta"], cfg.H, cfg.G, 0,
+                                     cfg.gn_eps)
+    parity(to_host(yfull), want, cfg.dtype, "gn full image")
+    parity(to_host(torch.cat(out, dim=1)), want, cfg.dtype, "gn patches with exact sums")
+
+
+# ======================================================================== conv
+def _conv_case(cfg, p, sample=None):
+    dpp = _dpp()
+    inp = layer_inputs(cfg)
+    r0 = cfg.row0(p)
+    x_np = rows_of(inp["x_fresh"], r0, cfg.rows)
+    x = to_dev(x_np, cfg.dtype)
+    st = to_dev(inp["x_stale"], cfg.dtype)
+    w = to_dev(inp["conv_w"], cfg.dtype)
+    b = torch.from_numpy(inp["conv_b"]).cuda()
+    y = torch.empty(cfg.B, cfg.rows, cfg.W, cfg.C, dtype=tdt(cfg.dtype), device="cuda")
+    only_patch = cfg.P == 1
+    dpp.dpp_conv3x3_halo(y, x, None if only_patch else st, w, b, cfg.H, r0)
+    torch.cuda.synchronize()
+    yh = to_host(y)
+    xv, sv, wv = values(cfg, x_np), values(cfg, inp["x_stale"]), values(cfg, inp["conv_w"])
+    if sample is None:
+        want = oracle.conv3x3_halo(xv, None if only_patch else sv, wv, inp["conv_b"], r0)
+        parity(yh, want, cfg.dtype, f"conv {cfg.name} p{p}")
+    else:
+        bi, ii, wi = sample
+        want = oracle.conv3x3_halo_sampled(xv, sv, wv, inp["conv_b"], r0, bi, ii, wi)
+        parity(yh[bi, ii, wi], want, cfg.dtype, f"conv {cfg.name} p{p} sampled {len(bi)}")
+    return y
+
+
+CONV_FULL = [
+    ("tiny_f32", 0), ("tiny_f32", 1), ("sdxl_1024", 1), ("sdxl_2048", 0), ("cfg_pair_1024", 3),
+]
+
+
+@pytest.mark.parametrize("name,p", CONV_FULL, ids=[f"{n}-p{p}" for n, p in CONV_FULL])
+def test_conv_parity_full(name, p):
+    say("conv", name, "patch", p)
+    _conv_case(CONFIGS[name], p)
+
+
+RAGGED_CONV = [
+    Config("cv_w5", B=2, H=9, W=5, C=128, P=3, G=8, heads=2, D=64),     # 16-column tiles, wide tail
+    Config("cv_w20", B=1, H=8, W=20, C=64, P=2, G=8, heads=1, D=64),    # 32-column tiles
+    Config("cv_w37", B=2, H=12, W=37, C=192, P=4, G=8, heads=3, D=64),  # 64-column tiles + tail, 192 channels
+    Config("cv_f32", B=2, H=6, W=7, C=12, P=3, G=3, heads=1, D=12, dtype="f32"),
+    Config("cv_one", B=1, H=5, W=9, C=64, P=1, G=8, heads=1, D=64),     # whole image, no stale
+]
+
+
+@pytest.mark.parametrize("cfg", RAGGED_CONV, ids=[c.name for c in RAGGED_CONV])
+def test_conv_parity_ragged(cfg):
+    for p in sorted({0, cfg.P // 2, cfg.P - 1}):
+        say("conv", cfg.name, "patch", p)
+        _conv_case(cfg, p)
+
+
+def test_conv_ragged_cout():
+    # Cout not a multiple of the 128-channel tile, Cin != Cout
+    dpp = _dpp()
+    rng = np.random.default_rng(5)
+    B, H, W, Cin, Cout, r0, R = 1, 10, 19, 64, 80, 3, 4
+    say("conv ragged cout", Cin, Cout)
+    xs = rng.standard_normal((B, H, W, Cin)).astype(np.float32)
+    xp = rng.standard_normal((B, R, W, Cin)).astype(np.float32)
+    wt = (0.05 * rng.standard_normal((Cout, 3, 3, Cin))).astype(np.float32)
+    from dpp_synth import f32_to_bf16_bits
+    xs_b, xp_b, w_b = (f32_to_bf16_bits(a) for a in (xs, xp, wt))
+    y = torch.empty(B, R, W, Cout, dtype=torch.bfloat16, device="cuda")
+    dpp.dpp_conv3x3_halo(y, to_dev(xp_b, "bf16"), to_dev(xs_b, "bf16"), to_dev(w_b, "bf16"), None, H, r0)
+    torch.cuda.synchronize()
+    want = oracle.conv3x3_halo(values("bf16", xp_b), values("bf16", xs_b), values("bf16", w_b), None, r0)
+    parity(to_host(y), want, "bf16", "conv ragged cout")
+
+
+def test_conv_only_halo_rows_read_on_gpu():
+    dpp = _dpp()
+    cfg = Config("halo", B=1, H=12, W=33, C=64, P=4, G=8, heads=1, D=64)
+    inp = layer_inputs(cfg)
+    p, r0 = 2, cfg.row0(2)
+    say("conv halo rows", cfg.name)
+    x = to_dev(rows_of(inp["x_fresh"], r0, cfg.rows), "bf16")
+    w = to_dev(inp["conv_w"], "bf16")
+    st = to_dev(inp["x_stale"], "bf16")
+    y1 = torch.empty(1, cfg.rows, cfg.W, cfg.C, dtype=torch.bfloat16, device="cuda")
+    y2 = torch.empty_like(y1)
+    dpp.dpp_conv3x3_halo(y1, x, st, w, None, cfg.H, r0)
+    st2 = st.clone()
+    st2[:, :r0 - 1] = 3.0
+    st2[:, r0:r0 + cfg.rows] = 1e4
+    st2[:, r0 + cfg.rows + 1:] = -2.0
+    dpp.dpp_conv3x3_halo(y2, x, st2, w, None, cfg.H, r0)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(bits(y1), bits(y2))
+
+
+@pytest.mark.parametrize("name", ["sdxl_2048", "sdxl_3840"])
+def test_conv_parity_full_size_sampled(name):
+    cfg = CONFIGS[name]
+    rng = np.random.default_rng(11)
+    for p in (0, cfg.P - 1, 3):
+        say("conv sampled", name, "patch", p)
+        n = 256
+        ii = np.concatenate([[0, cfg.rows - 1, 0, cfg.rows - 1], rng.integers(0, cfg.rows, n - 4)])
+        wi = np.concatenate([[0, cfg.W - 1, cfg.W - 1, 0], rng.integers(0, cfg.W, n - 4)])
+        bi = np.zeros(n, dtype=np.int64)
+        _conv_case(cfg, p, sample=(bi, ii, wi))
+
+
+# ======================================================================== attention
+def _attn_case(cfg, p, sample_rows=None, use_ws=True, what=""):
+    """Queries: patch p's rows of q; K/V: stale buffer with patch p's fresh rows
+    spliced in (GPU: dpp_splice_patch; oracle: oracle.splice)."""
+    dpp = _dpp()
+    inp = attention_inputs(cfg)
+    B, H, W, C = cfg.B, cfg.H, cfg.W, cfg.C
+    r0 = cfg.row0(p)
+
+    def img(a):
+        return a.reshape(B, H, W, C)
+    q_np = np.ascontiguousarray(img(inp["q"])[:, r0:r0 + cfg.rows]).reshape(B, cfg.Nq, C)
+    kf = rows_of(img(inp["k"]), r0, cfg.rows)
+    vf = rows_of(img(inp["v"]), r0, cfg.rows)
+    k_d = to_dev(img(inp["k_stale"]), cfg.dtype)
+    v_d = to_dev(img(inp["v_stale"]), cfg.dtype)
+    dpp.dpp_splice_patch(k_d, to_dev(kf, cfg.dtype), r0)
+    dpp.dpp_splice_patch(v_d, to_dev(vf, cfg.dtype), r0)
+    q_d = to_dev(q_np, cfg.dtype)
+    o = torch.empty(B, cfg.Nq, C, dtype=tdt(cfg.dtype), device="cuda")
+    wsb = dpp.dpp_self_attn_workspace_bytes(B, cfg.Nq, cfg.N, cfg.heads, cfg.D, 0 if cfg.dtype == "bf16" else 1)
+    ws = torch.empty(wsb, dtype=torch.uint8, device="cuda") if (use_ws and wsb) else None
+    dpp.dpp_self_attn_displaced(o, q_d, k_d.view(B, cfg.N, C), v_d.view(B, cfg.N, C), cfg.heads, cfg.D, 0.0, ws)
+    torch.cuda.synchronize()
+    kk = tokens(oracle.splice(values(cfg, img(inp["k_stale"])), values(cfg, kf), r0))
+    vv = tokens(oracle.splice(values(cfg, img(inp["v_stale"])), values(cfg, vf), r0))
+    qv = values(cfg, q_np)
+    oh = to_host(o)
+    if sample_rows is None:
+        want = oracle.self_attn_displaced(qv, kk, vv, cfg.heads)
+        parity(oh, want, cfg.dtype, f"attn {cfg.name} p{p} {what}")
+    else:
+        bi, qi = sample_rows
+        want = oracle.self_attn_displaced(qv, kk, vv, cfg.heads, rows=(bi, qi))
+        parity(oh[bi, qi], want, cfg.dtype, f"attn {cfg.name} p{p} sampled {len(bi)} {what}")
+
+
+ATTN_FULL = [("tiny_f32", 0), ("tiny_f32", 1), ("sdxl_1024", 2), ("cfg_pair_1024", 0)]
+
+
+@pytest.mark.parametrize("name,p", ATTN_FULL, ids=[f"{n}-p{p}" for n, p in ATTN_FULL])
+def test_attention_parity_full(name, p):
+    say("attention", name, "patch", p)
+    _attn_case(CONFIGS[name], p)
+
+
+@pytest.mark.parametrize("use_ws", [True, False], ids=["split", "unsplit"])
+def test_attention_parity_ragged(use_ws):
+    # 7 x 43 tokens: n_q = 301 (one full 256-query tile + a 45-query tail),
+    # n_kv = 1505 (23 full 64-key tiles + a 33-key tail); 3 heads, batch 2
+    cfg = Config("at_rag", B=2, H=35, W=43, C=192, P=5, G=8, heads=3, D=64)
+    for p in (0, 4):
+        say("attention ragged", "split" if use_ws else "unsplit", "patch", p)
+        _attn_case(cfg, p, use_ws=use_ws, what="split" if use_ws else "unsplit")
+
+
+def test_attention_strided_rows_and_tiny_kv():
+    # ld > heads*D on every operand; 5 keys only (single partial tile); 1 query
+    dpp = _dpp()
+    rng = np.random.default_rng(3)
+    from dpp_synth import f32_to_bf16_bits
+    for (B, nq, nkv, heads, ld) in [(2, 70, 5, 2, 136), (1, 1, 200, 1, 64), (1, 33, 64, 2, 128)]:
+        say("attention strided", B, nq, nkv, heads, ld)
+        q = f32_to_bf16_bits(rng.standard_normal((B, nq, ld)).astype(np.float32))
+        k = f32_to_bf16_bits(rng.standard_normal((B, nkv, ld)).astype(np.float32))
+        v = f32_to_bf16_bits(rng.standard_normal((B, nkv, ld)).astype(np.float32))
+        o = torch.zeros(B, nq, ld + 8, dtype=torch.bfloat16, device="cuda")
+        wsb = dpp.dpp_self_attn_workspace_bytes(B, nq, nkv, heads, 64, 0)
+        ws = torch.empty(wsb, dtype=torch.uint8, device="cuda") if wsb else None
+        dpp.dpp_self_attn_displaced(o, to_dev(q, "bf16"), to_dev(k, "bf16"), to_dev(v, "bf16"), heads, 64, 0.0, ws)
+        torch.cuda.synchronize()
+        hd = heads * 64
+        want = oracle.self_attn_displaced(values("bf16", q)[..., :hd], values("bf16", k)[..., :hd],
+                                          values("bf16", v)[..., :hd], heads)
+        oh = to_host(o)
+        parity(oh[..., :hd], want, "bf16", f"attn strided {B},{nq},{nkv}")
+        assert np.all(oh[..., hd:] == 0), "wrote outside heads*D columns"
+
+
+def test_attention_closed_form_zero_query():
+    # Q = 0: uniform weights, output = mean of V over all keys
+    dpp = _dpp()
+    rng = np.random.default_rng(4)
+    from dpp_synth import f32_to_bf16_bits
+    B, nq, nkv, heads = 1, 100, 1000, 2
+    say("attention zero query")
+    v = f32_to_bf16_bits(rng.standard_normal((B, nkv, heads * 64)).astype(np.float32))
+    k = f32_to_bf16_bits(rng.standard_normal((B, nkv, heads * 64)).astype(np.float32))
+    o = torch.empty(B, nq, heads * 64, dtype=torch.bfloat16, device="cuda")
+    q = torch.zeros(B, nq, heads * 64, dtype=torch.bfloat16, device="cuda")
+    dpp.dpp_self_attn_displaced(o, q, to_dev(k, "bf16"), to_dev(v, "bf16"), heads, 64)
+    torch.cuda.synchronize()
+    want = np.broadcast_to(values("bf16", v).astype(np.float64).mean(axis=1, keepdims=True), (B, nq, heads * 64))
+    parity(to_host(o), want, "bf16", "attn zero query")
+
+
+@pytest.mark.parametrize("name", ["sdxl_2048", "sdxl_3840"])
+def test_attention_parity_full_size_sampled(name):
+    cfg = CONFIGS[name]
+    rng = np.random.default_rng(12)
+    n = 64
+    qi = np.concatenate([[0, cfg.Nq - 1, cfg.W - 1, cfg.Nq // 2], rng.integers(0, cfg.Nq, n - 4)])
+    bi = np.zeros(n, dtype=np.int64)
+    for p in (0, cfg.P - 1):
+        say("attention sampled", name, "patch", p)
+        _attn_case(cfg, p, sample_rows=(bi, qi))
+
+
+# ======================================================================== CFG
+CFG_CASES = [
+    ("latent_1024", "bf16", 128 * 128 * 4, 0),
+    ("latent_3840", "bf16", 480 * 480 * 4, 0),
+    ("ragged_bf16", "bf16", 1_000_003, 0),
+    ("misaligned_bf16", "bf16", 4099, 1),
+    ("f32", "f32", 777, 0),
+    ("f32_large", "f32", 3_000_001, 0),
+]
+
+
+@pytest.mark.parametrize("name,dtype,n,offset", CFG_CASES, ids=[c[0] for c in CFG_CASES])
+def test_cfg_combine_parity(name, dtype, n, offset):
+    dpp = _dpp()
+    say("cfg", name, n)
+    cfg = CONFIGS["cfg_pair_1024"].replace(dtype=dtype)
+    inp = cfg_inputs(cfg, n=n + offset)
+    c_all, u_all = to_dev(inp["eps_c"], dtype), to_dev(inp["eps_u"], dtype)
+    c, u = c_all[offset:], u_all[offset:]        # offset 1 element: unaligned views -> scalar path
+    eps = torch.empty(n + offset, dtype=tdt(dtype), device="cuda")[offset:]
+    rel = torch.full((1,), -1.0, device="cuda")
+    ws = torch.empty(dpp.dpp_cfg_combine_workspace_bytes(n), dtype=torch.uint8, device="cuda")
+    dpp.dpp_cfg_combine_relmae(eps, rel, c, u, 7.5, ws)
+    torch.cuda.synchronize()
+    want_eps, want_rel = oracle.cfg_combine_relmae(values(dtype, inp["eps_c"])[offset:],
+                                                   values(dtype, inp["eps_u"])[offset:], 7.5)
+    parity(to_host(eps), want_eps, dtype, f"cfg eps {name}")
+    got_rel = float(rel.item())
+    print(f"rel-MAE gpu {got_rel:.8f} oracle {want_rel:.8f}", flush=True)
+    assert abs(got_rel - want_rel) <= REL_TOL * abs(want_rel)
+    # deterministic: a second call gives the same bits
+    rel2 = torch.full((1,), -1.0, device="cuda")
+    dpp.dpp_cfg_combine_relmae(eps, rel2, c, u, 7.5, ws)
+    torch.cuda.synchronize()
+    assert rel2.item() == got_rel
+
+
+def test_cfg_in_place_and_closed_forms():
+    dpp = _dpp()
+    say("cfg in place / closed forms")
+    u = torch.tensor([1.0, -2.0, 3.0, 0.5] * 1000, device="cuda")
+    c = torch.tensor([2.0, -2.0, 2.5, 1.5] * 1000, device="cuda")
+    rel = torch.zeros(1, device="cuda")
+    ws = torch.empty(dpp.dpp_cfg_combine_workspace_bytes(u.numel()), dtype=torch.uint8, device="cuda")
+    eps = c.clone()
+    dpp.dpp_cfg_combine_relmae(eps, rel, eps, u, 7.5, ws)    # eps aliases eps_c
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(eps.cpu().numpy()[:4], [8.5, -2.0, -0.75, 8.0])
+    assert abs(rel.item() - 2.5 / 6.5) <= 1e-6
+    eps0 = torch.empty_like(u)
+    dpp.dpp_cfg_combine_relmae(eps0, rel, c, u, 0.0, ws)       # w = 0 -> eps_u
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(eps0.cpu().numpy(), u.cpu().numpy())
+    dpp.dpp_cfg_combine_relmae(eps0, rel, u, u, 7.5, ws)       # identical branches -> 0
+    torch.cuda.synchronize()
+    assert rel.item() == 0.0
+    z = torch.zeros(64, device="cuda")
+    dpp.dpp_cfg_combine_relmae(eps0[:64], rel, z, z, 7.5, ws)  # 0/0 -> NaN
+    torch.cuda.synchronize()
+    assert np.isnan(rel.item())
+    dpp.dpp_cfg_combine_relmae(eps0, None, c, u, 7.5, None)     # no reduction, no workspace
+    torch.cuda.synchronize()
+
+
+# ======================================================================== chained block
+def _block_case(cfg, patches):
+    from displaced_patch_parallelism_net_amd.step import DisplacedLayer
+    inp = layer_inputs(cfg)
+    bf = cfg.dtype == "bf16"
+    xs_v, xf_v, w_v = values(cfg, inp["x_stale"]), values(cfg, inp["x_fresh"]), values(cfg, inp["conv_w"])
+    state = oracle.previous_step_state(xs_v, inp["gamma"], inp["beta"], w_v, inp["conv_b"], cfg.P, cfg.G,
+                                       cfg.gn_eps, bf16=bf)
+    layer = DisplacedLayer(cfg.B, cfg.H, cfg.W, cfg.C, cfg.P, cfg.G, cfg.heads, tdt(cfg.dtype), eps=cfg.gn_eps,
+                           head_dim=cfg.D)
+    gamma, beta = torch.from_numpy(inp["gamma"]).cuda(), torch.from_numpy(inp["beta"]).cuda()
+    w, b = to_dev(inp["conv_w"], cfg.dtype), torch.from_numpy(inp["conv_b"]).cuda()
+    say("block sync step", cfg.name)
+    layer.synchronous_step(to_dev(inp["x_stale"], cfg.dtype), gamma, beta, w, b)
+    torch.cuda.synchronize()
+    parity(to_host(layer.a1), state["a1_exact"], cfg.dtype, f"block {cfg.name} previous GN")
+    parity(to_host(layer.a2), state["a2_exact"], cfg.dtype, f"block {cfg.name} previous conv")
+    _check_stats(layer.stats_prev.cpu().numpy(), state["stale_stats"], cfg.rows * cfg.W * cfg.C // cfg.G,
+                 f"block {cfg.name} previous sums")
+    xf_d = to_dev(inp["x_fresh"], cfg.dtype)
+    for p in patches:
+        say("block patch step", cfg.name, "patch", p)
+        o = layer.patch_step(p, layer.band(xf_d, p), gamma, beta, w, b)
+        torch.cuda.synchronize()
+        want = oracle.displaced_block(xf_v, state, inp["gamma"], inp["beta"], w_v, inp["conv_b"], cfg.P, p, cfg.G,
+                                      cfg.heads, cfg.gn_eps, bf16=bf)
+        parity(to_host(layer.y1), want["y1_exact"], cfg.dtype, f"block {cfg.name} p{p} GN")
+        parity(to_host(layer.y2), want["y2_exact"], cfg.dtype, f"block {cfg.name} p{p} conv")
+        parity(to_host(layer.kv[p]), want["kv_exact"], cfg.dtype, f"block {cfg.name} p{p} spliced K/V")
+        parity(to_host(o), want["o"], cfg.dtype, f"block {cfg.name} p{p} attention")
+        _check_stats(layer.stats_next[:, p].cpu().numpy(), want["stats"], cfg.rows * cfg.W * cfg.C // cfg.G,
+                     f"block {cfg.name} p{p} fresh sums")
+
+
+@pytest.mark.parametrize("name,patches", [("tiny_f32", (0, 1)), ("sdxl_1024", (0, 3)), ("cfg_pair_1024", (1,))],
+                         ids=["tiny_f32", "sdxl_1024", "cfg_pair_1024"])
+def test_block_parity(name, patches):
+    _block_case(CONFIGS[name], patches)

@@ -440,3 +440,14 @@ def test_oracle_and_synth_are_independent_of_the_gpu_package():
         text = f.read_text()
         assert "displaced_patch_parallelism_net_amd" not in text, f
         assert "ctypes" not in text, f
+
+
+def test_half_ulp_helper_bounds_bf16_rounding():
+    # the parity allowance is exactly the worst rounding distance
+    from tests._helpers import half_ulp_bf16
+    a = RNG.standard_normal(50000) * np.exp(RNG.uniform(-10, 10, 50000))
+    d = np.abs(oracle.bf16_round(a) - a)
+    assert np.all(d <= half_ulp_bf16(a) * (1 + 1e-12))
+    assert np.max(d / half_ulp_bf16(a)) > 0.99
+    assert half_ulp_bf16(np.array([1.0]))[0] == 2.0 ** -8
+    assert half_ulp_bf16(np.array([6.0]))[0] == 2.0 ** -6
