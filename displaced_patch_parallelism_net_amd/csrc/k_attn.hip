@@ -97,7 +97,12 @@ __device__ __forceinline__ int kperm16(int key) {
   return (key & ~15) | (a << 3) | (g << 2) | (key & 3);
 }
 
-__global__ __launch_bounds__(kAttThreads) void attn_bf16_kernel(AttnArgs a) {
+// Lazy rescaling: a query's running max m only moves when a tile's max
+// exceeds it by more than kTau (log2 units).  Softmax is invariant to the
+// reference point, so this is exact; P = 2^(s - m) then stays <= 2^kTau.
+constexpr float kTau = 8.0f;
+
+__global__ __launch_bounds__(kAttThreads, 2) void attn_bf16_kernel(AttnArgs a) {
   __shared__ uint16_t Ks[2][kAttKT * kAttRow];
   __shared__ uint16_t Vt[2][kAttD * kAttRow];
 
@@ -122,8 +127,8 @@ __global__ __launch_bounds__(kAttThreads) void attn_bf16_kernel(AttnArgs a) {
     const int qi = q0 + qb2 * 32 + l32;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
-      uint4 u = make_uint4(0, 0, 0, 0);
-      if (qi < a.n_q) u = *reinterpret_cast<const uint4*>(qb + static_cast<int64_t>(qi) * a.ld_q + ks * 16 + g * 8);
+      uint4 u = *reinterpret_cast<const uint4*>(qb + static_cast<int64_t>(min(qi, a.n_q - 1)) * a.ld_q + ks * 16 + g * 8);
+      if (qi >= a.n_q) u = make_uint4(0, 0, 0, 0);
       qf[qb2][ks] = __builtin_bit_cast(bf16x8, u);
     }
   }
@@ -131,13 +136,23 @@ __global__ __launch_bounds__(kAttThreads) void attn_bf16_kernel(AttnArgs a) {
   // Tile loader: thread -> key pair kp = tid / 8 (keys 2kp, 2kp+1), d vector dv = tid % 8.
   const int kp = tid >> 3, dv = tid & 7;
   uint4 kr0, kr1, vr0, vr1;
+  // Rows past the key range are loaded from a clamped (valid) row and zeroed
+  // by value: a select between a global pointer and a local zero would force
+  // the zero into scratch and turn the loads into flat loads.
   auto load_tile = [&](int t0) {
     const int k0 = t0 + 2 * kp, k1 = k0 + 1;
-    const uint4 z = make_uint4(0, 0, 0, 0);
-    kr0 = (k0 < k_end) ? *reinterpret_cast<const uint4*>(kb + static_cast<int64_t>(k0) * a.ld_kv + dv * 8) : z;
-    kr1 = (k1 < k_end) ? *reinterpret_cast<const uint4*>(kb + static_cast<int64_t>(k1) * a.ld_kv + dv * 8) : z;
-    vr0 = (k0 < k_end) ? *reinterpret_cast<const uint4*>(vb + static_cast<int64_t>(k0) * a.ld_kv + dv * 8) : z;
-    vr1 = (k1 < k_end) ? *reinterpret_cast<const uint4*>(vb + static_cast<int64_t>(k1) * a.ld_kv + dv * 8) : z;
+    const int c0 = min(k0, k_end - 1), c1 = min(k1, k_end - 1);
+    kr0 = *reinterpret_cast<const uint4*>(kb + static_cast<int64_t>(c0) * a.ld_kv + dv * 8);
+    kr1 = *reinterpret_cast<const uint4*>(kb + static_cast<int64_t>(c1) * a.ld_kv + dv * 8);
+    vr0 = *reinterpret_cast<const uint4*>(vb + static_cast<int64_t>(c0) * a.ld_kv + dv * 8);
+    vr1 = *reinterpret_cast<const uint4*>(vb + static_cast<int64_t>(c1) * a.ld_kv + dv * 8);
+    if (t0 + kAttKT > k_end) {
+      const uint32_t m0 = k0 < k_end ? 0xffffffffu : 0u, m1 = k1 < k_end ? 0xffffffffu : 0u;
+      kr0.x &= m0; kr0.y &= m0; kr0.z &= m0; kr0.w &= m0;
+      vr0.x &= m0; vr0.y &= m0; vr0.z &= m0; vr0.w &= m0;
+      kr1.x &= m1; kr1.y &= m1; kr1.z &= m1; kr1.w &= m1;
+      vr1.x &= m1; vr1.y &= m1; vr1.z &= m1; vr1.w &= m1;
+    }
   };
   auto store_tile = [&](int buf) {
     *reinterpret_cast<uint4*>(&Ks[buf][(2 * kp) * kAttRow + dv * 8]) = kr0;
@@ -216,33 +231,38 @@ __global__ __launch_bounds__(kAttThreads) void attn_bf16_kernel(AttnArgs a) {
       for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, S[kb2][qb2][r]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
-      const float m_new = fmaxf(m_run[qb2], mx * a.c);
-      const float alpha = __builtin_amdgcn_exp2f(m_run[qb2] - m_new);
-      m_run[qb2] = m_new;
-      float lsum = 0.f;
+      mx = fmaxf(mx, __shfl_xor(mx, 32, kWave)) * a.c;
+      const bool move = mx > m_run[qb2] + kTau;
+      if (__builtin_amdgcn_ballot_w64(move) != 0) {  // wave-uniform, rare after the first tile
+        const float m_new = move ? mx : m_run[qb2];
+        const float alpha = __builtin_amdgcn_exp2f(m_run[qb2] - m_new);
+        m_run[qb2] = m_new;
+        l_run[qb2] *= alpha;
+#pragma unroll
+        for (int db = 0; db < 2; ++db)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) O[qb2][db][r] *= alpha;
+      }
+      const float m_cur = m_run[qb2];
+      const bf16x2 ones = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
+      float lsum = l_run[qb2];
 #pragma unroll
       for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
         for (int t16 = 0; t16 < 2; ++t16) {
           float p[8];
 #pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            p[e] = __builtin_amdgcn_exp2f(fmaf(S[kb2][qb2][t16 * 8 + e], a.c, -m_new));
-            lsum += p[e];
+          for (int e = 0; e < 8; ++e) p[e] = __builtin_amdgcn_exp2f(fmaf(S[kb2][qb2][t16 * 8 + e], a.c, -m_cur));
+          uint32_t w[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            w[e] = pack_bf16x2(p[2 * e], p[2 * e + 1]);
+            // row sum of the rounded weights (the ones the PV product uses)
+            lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w[e]), ones, lsum, false);
           }
-          uint4 u;
-          u.x = pack_bf16x2(p[0], p[1]);
-          u.y = pack_bf16x2(p[2], p[3]);
-          u.z = pack_bf16x2(p[4], p[5]);
-          u.w = pack_bf16x2(p[6], p[7]);
-          P[qb2][kb2][t16] = __builtin_bit_cast(bf16x8, u);
+          P[qb2][kb2][t16] = __builtin_bit_cast(bf16x8, make_uint4(w[0], w[1], w[2], w[3]));
         }
-      l_run[qb2] = fmaf(l_run[qb2], alpha, lsum);
-#pragma unroll
-      for (int db = 0; db < 2; ++db)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) O[qb2][db][r] *= alpha;
+      l_run[qb2] = lsum;
     }
 #pragma unroll
     for (int db = 0; db < 2; ++db)
@@ -329,8 +349,11 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(const float* __restrict
 }
 
 // Key-range split policy: depends on the shape only (so the workspace query
-// needs no device).  Aim for at least ~2 workgroups per CU of a 256-CU
-// MI355X while keeping >= 8 key tiles per split.
+// needs no device).  An MI355X holds 256 CUs x 2 resident workgroups of this
+// kernel; pick the smallest split count whose workgroup count fills the
+// resident slots in whole rounds to >= 90 % (else the best one), keeping
+// >= 8 key tiles per split.
+constexpr int64_t kAttSlots = 256 * 2;
 struct AttnSplit {
   int nsplit;
   int keys_per_split;
@@ -338,14 +361,19 @@ struct AttnSplit {
 static AttnSplit attn_split(int64_t B, int64_t n_q, int64_t n_kv, int64_t heads) {
   const int64_t qtiles = ceil_div(n_q, kAttQT) * B * heads;
   const int64_t ktiles = ceil_div(n_kv, kAttKT);
-  int64_t ns = 1;
-  const int64_t target = 512;
-  if (qtiles < target) ns = ceil_div(target, qtiles);
-  const int64_t max_ns = ktiles / 8 > 0 ? ktiles / 8 : 1;
-  if (ns > max_ns) ns = max_ns;
-  if (ns < 1) ns = 1;
-  int64_t kps = ceil_div(ktiles, ns) * kAttKT;
-  ns = ceil_div(n_kv, kps);
+  const int64_t max_ns = ktiles / 8 > 1 ? (ktiles / 8 < 16 ? ktiles / 8 : 16) : 1;
+  int64_t best = 1;
+  double best_eff = 0.0;
+  for (int64_t ns = 1; ns <= max_ns; ++ns) {
+    const int64_t kps_t = ceil_div(ktiles, ns);
+    const int64_t ns_eff = ceil_div(ktiles, kps_t);
+    const int64_t total = qtiles * ns_eff;
+    const double eff = static_cast<double>(total) / static_cast<double>(ceil_div(total, kAttSlots) * kAttSlots);
+    if (eff > best_eff + 1e-9) { best_eff = eff; best = ns; }
+    if (eff >= 0.9) break;
+  }
+  const int64_t kps = ceil_div(ktiles, best) * kAttKT;
+  const int64_t ns = ceil_div(n_kv, kps);
   return AttnSplit{static_cast<int>(ns), static_cast<int>(kps)};
 }
 
