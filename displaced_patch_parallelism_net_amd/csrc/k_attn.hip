@@ -97,10 +97,23 @@ __device__ __forceinline__ int kperm16(int key) {
   return (key & ~15) | (a << 3) | (g << 2) | (key & 3);
 }
 
-// Lazy rescaling: a query's running max m only moves when a tile's max
-// exceeds it by more than kTau (log2 units).  Softmax is invariant to the
-// reference point, so this is exact; P = 2^(s - m) then stays <= 2^kTau.
+// Lazy rescaling.  The running reference m of a query only moves when a
+// tile's max exceeds it by more than kTau (log2 units); softmax does not
+// depend on the reference point, so this is exact as long as P = 2^(s - m)
+// stays finite and representable.  The fast path therefore skips the tile
+// max entirely: it exponentiates with the current m and checks the lane's
+// partial row sum -- if that sum is <= kSumCap every P in it is too.  A lane
+// above the cap (or inf/NaN: the first tile, m = -inf) sends the whole wave
+// through the exact path for that tile: true tile max, rescale, recompute.
 constexpr float kTau = 8.0f;
+constexpr float kSumCap = 4096.0f;
+
+// gfx9 buffer resource word 3 (32-bit raw access, no swizzle).
+constexpr int kBufWord3 = 0x00020000;
+
+__device__ __forceinline__ uint4 buffer_load16(__amdgpu_buffer_rsrc_t r, int voff) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0));
+}
 
 __global__ __launch_bounds__(kAttThreads, 2) void attn_bf16_kernel(AttnArgs a) {
   __shared__ uint16_t Ks[2][kAttKT * kAttRow];
@@ -119,6 +132,7 @@ __global__ __launch_bounds__(kAttThreads, 2) void attn_bf16_kernel(AttnArgs a) {
   const uint16_t* qb = a.q + static_cast<int64_t>(b) * a.n_q * a.ld_q + h * kAttD;
   const uint16_t* kb = a.k + static_cast<int64_t>(b) * a.n_kv * a.ld_kv + h * kAttD;
   const uint16_t* vb = a.v + static_cast<int64_t>(b) * a.n_kv * a.ld_kv + h * kAttD;
+  const int row_bytes = static_cast<int>(a.ld_kv) * 2;
 
   // Q^T fragments (B operand of S^T = K Q^T): lane -> query l32, d = 16 ks + 8 g + 0..7
   bf16x8 qf[2][4];
@@ -133,41 +147,39 @@ __global__ __launch_bounds__(kAttThreads, 2) void attn_bf16_kernel(AttnArgs a) {
     }
   }
 
-  // Tile loader: thread -> key pair kp = tid / 8 (keys 2kp, 2kp+1), d vector dv = tid % 8.
+  // Tile loader.  K: thread -> key pair kp = tid / 8 (keys 2kp, 2kp+1), 16-byte
+  // column dv = tid % 8 (8 lanes cover one 128-byte key row).  Buffer loads
+  // against a per-tile resource that ends at the last valid key: rows past it
+  // read as zero, offsets stay 32-bit and need no per-tile address math.
   const int kp = tid >> 3, dv = tid & 7;
+  const int off0 = (2 * kp) * row_bytes + dv * 16, off1 = off0 + row_bytes;
   uint4 kr0, kr1, vr0, vr1;
-  // Rows past the key range are loaded from a clamped (valid) row and zeroed
-  // by value: a select between a global pointer and a local zero would force
-  // the zero into scratch and turn the loads into flat loads.
   auto load_tile = [&](int t0) {
-    const int k0 = t0 + 2 * kp, k1 = k0 + 1;
-    const int c0 = min(k0, k_end - 1), c1 = min(k1, k_end - 1);
-    kr0 = *reinterpret_cast<const uint4*>(kb + static_cast<int64_t>(c0) * a.ld_kv + dv * 8);
-    kr1 = *reinterpret_cast<const uint4*>(kb + static_cast<int64_t>(c1) * a.ld_kv + dv * 8);
-    vr0 = *reinterpret_cast<const uint4*>(vb + static_cast<int64_t>(c0) * a.ld_kv + dv * 8);
-    vr1 = *reinterpret_cast<const uint4*>(vb + static_cast<int64_t>(c1) * a.ld_kv + dv * 8);
-    if (t0 + kAttKT > k_end) {
-      const uint32_t m0 = k0 < k_end ? 0xffffffffu : 0u, m1 = k1 < k_end ? 0xffffffffu : 0u;
-      kr0.x &= m0; kr0.y &= m0; kr0.z &= m0; kr0.w &= m0;
-      vr0.x &= m0; vr0.y &= m0; vr0.z &= m0; vr0.w &= m0;
-      kr1.x &= m1; kr1.y &= m1; kr1.z &= m1; kr1.w &= m1;
-      vr1.x &= m1; vr1.y &= m1; vr1.z &= m1; vr1.w &= m1;
-    }
+    const int valid = min(k_end - t0, kAttKT);
+    const int nrec = (valid - 1) * row_bytes + kAttD * 2;
+    const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(kb + static_cast<int64_t>(t0) * a.ld_kv), 0, nrec, kBufWord3);
+    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(vb + static_cast<int64_t>(t0) * a.ld_kv), 0, nrec, kBufWord3);
+    kr0 = buffer_load16(rk, off0);
+    kr1 = buffer_load16(rk, off1);
+    vr0 = buffer_load16(rv, off0);
+    vr1 = buffer_load16(rv, off1);
   };
+  const int vpos = kperm16(2 * kp);
   auto store_tile = [&](int buf) {
     *reinterpret_cast<uint4*>(&Ks[buf][(2 * kp) * kAttRow + dv * 8]) = kr0;
     *reinterpret_cast<uint4*>(&Ks[buf][(2 * kp + 1) * kAttRow + dv * 8]) = kr1;
     // V^T: element (key, d) -> Vt[d][kperm16(key)]; keys 2kp, 2kp+1 stay adjacent.
-    const int pos = kperm16(2 * kp);
     const uint32_t a0[4] = {vr0.x, vr0.y, vr0.z, vr0.w};
     const uint32_t a1[4] = {vr1.x, vr1.y, vr1.z, vr1.w};
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      // d = dv*8 + 2e (low halves) and dv*8 + 2e + 1 (high halves)
-      const uint32_t lo = (a0[e] & 0xffffu) | (a1[e] << 16);
-      const uint32_t hi = (a0[e] >> 16) | (a1[e] & 0xffff0000u);
-      *reinterpret_cast<uint32_t*>(&Vt[buf][(dv * 8 + 2 * e) * kAttRow + pos]) = lo;
-      *reinterpret_cast<uint32_t*>(&Vt[buf][(dv * 8 + 2 * e + 1) * kAttRow + pos]) = hi;
+      // d = dv*8 + 2e: low halves of both keys; d + 1: high halves
+      const uint32_t lo = __builtin_amdgcn_perm(a1[e], a0[e], 0x05040100u);
+      const uint32_t hi = __builtin_amdgcn_perm(a1[e], a0[e], 0x07060302u);
+      *reinterpret_cast<uint32_t*>(&Vt[buf][(dv * 8 + 2 * e) * kAttRow + vpos]) = lo;
+      *reinterpret_cast<uint32_t*>(&Vt[buf][(dv * 8 + 2 * e + 1) * kAttRow + vpos]) = hi;
     }
   };
 
@@ -180,16 +192,38 @@ __global__ __launch_bounds__(kAttThreads, 2) void attn_bf16_kernel(AttnArgs a) {
       for (int r = 0; r < 16; ++r) O[i][j][r] = 0.f;
   float m_run[2] = {-INFINITY, -INFINITY};
   float l_run[2] = {0.f, 0.f};
+  const bf16x2 ones = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
+
+  // exponentiate one query block's scores with reference m; returns the
+  // lane's partial sum of the rounded weights
+  auto softmax_block = [&](const f32x16 (&S)[2][2], int qb2, float m, bf16x8 (&P)[2][2]) {
+    float lsum = 0.f;
+#pragma unroll
+    for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+      for (int t16 = 0; t16 < 2; ++t16) {
+        uint32_t w[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float p0 = __builtin_amdgcn_exp2f(fmaf(S[kb2][qb2][t16 * 8 + 2 * e], a.c, -m));
+          const float p1 = __builtin_amdgcn_exp2f(fmaf(S[kb2][qb2][t16 * 8 + 2 * e + 1], a.c, -m));
+          w[e] = pack_bf16x2(p0, p1);
+          lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w[e]), ones, lsum, false);
+        }
+        P[kb2][t16] = __builtin_bit_cast(bf16x8, make_uint4(w[0], w[1], w[2], w[3]));
+      }
+    return lsum;
+  };
 
   const int ntiles = (k_end - k_begin + kAttKT - 1) / kAttKT;
+  // prologue: tile 0 into buffer 0, tile 1 into registers
   load_tile(k_begin);
+  store_tile(0);
+  if (ntiles > 1) load_tile(k_begin + kAttKT);
+  __syncthreads();
   for (int it = 0; it < ntiles; ++it) {
     const int buf = it & 1;
     const int t0 = k_begin + it * kAttKT;
-    __syncthreads();  // readers of buffer `buf` (two tiles ago) are done
-    store_tile(buf);
-    __syncthreads();
-    if (it + 1 < ntiles) load_tile(t0 + kAttKT);
 
     // ---- S^T = K Q^T for 2 key blocks x 2 query blocks
     f32x16 S[2][2];
@@ -222,19 +256,19 @@ __global__ __launch_bounds__(kAttThreads, 2) void attn_bf16_kernel(AttnArgs a) {
         }
     }
 
-    // ---- online softmax per query block, then O^T += V^T P^T
+    // ---- softmax (fast path without the tile max), O^T += V^T P^T
     bf16x8 P[2][2][2];  // [qb][kb][t16]
 #pragma unroll
     for (int qb2 = 0; qb2 < 2; ++qb2) {
-      float mx = S[0][qb2][0];
+      float lsum = softmax_block(S, qb2, m_run[qb2], P[qb2]);
+      if (__builtin_amdgcn_ballot_w64(!(lsum <= kSumCap)) != 0) {  // rare: exact path
+        float mx = S[0][qb2][0];
 #pragma unroll
-      for (int kb2 = 0; kb2 < 2; ++kb2)
+        for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, S[kb2][qb2][r]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32, kWave)) * a.c;
-      const bool move = mx > m_run[qb2] + kTau;
-      if (__builtin_amdgcn_ballot_w64(move) != 0) {  // wave-uniform, rare after the first tile
-        const float m_new = move ? mx : m_run[qb2];
+          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, S[kb2][qb2][r]);
+        mx = fmaxf(mx, __shfl_xor(mx, 32, kWave)) * a.c;
+        const float m_new = (mx > m_run[qb2] + kTau) ? mx : m_run[qb2];
         const float alpha = __builtin_amdgcn_exp2f(m_run[qb2] - m_new);
         m_run[qb2] = m_new;
         l_run[qb2] *= alpha;
@@ -242,27 +276,9 @@ __global__ __launch_bounds__(kAttThreads, 2) void attn_bf16_kernel(AttnArgs a) {
         for (int db = 0; db < 2; ++db)
 #pragma unroll
           for (int r = 0; r < 16; ++r) O[qb2][db][r] *= alpha;
+        lsum = softmax_block(S, qb2, m_new, P[qb2]);
       }
-      const float m_cur = m_run[qb2];
-      const bf16x2 ones = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
-      float lsum = l_run[qb2];
-#pragma unroll
-      for (int kb2 = 0; kb2 < 2; ++kb2)
-#pragma unroll
-        for (int t16 = 0; t16 < 2; ++t16) {
-          float p[8];
-#pragma unroll
-          for (int e = 0; e < 8; ++e) p[e] = __builtin_amdgcn_exp2f(fmaf(S[kb2][qb2][t16 * 8 + e], a.c, -m_cur));
-          uint32_t w[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            w[e] = pack_bf16x2(p[2 * e], p[2 * e + 1]);
-            // row sum of the rounded weights (the ones the PV product uses)
-            lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w[e]), ones, lsum, false);
-          }
-          P[qb2][kb2][t16] = __builtin_bit_cast(bf16x8, make_uint4(w[0], w[1], w[2], w[3]));
-        }
-      l_run[qb2] = lsum;
+      l_run[qb2] += lsum;
     }
 #pragma unroll
     for (int db = 0; db < 2; ++db)
@@ -277,6 +293,13 @@ __global__ __launch_bounds__(kAttThreads, 2) void attn_bf16_kernel(AttnArgs a) {
           for (int qb2 = 0; qb2 < 2; ++qb2)
             O[qb2][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, P[qb2][kb2][t16], O[qb2][db], 0, 0, 0);
         }
+
+    // ---- stage tile it+1 (already in registers) into the other buffer, fetch tile it+2
+    if (it + 1 < ntiles) {
+      store_tile(buf ^ 1);  // buffer buf^1 was last read in iteration it-1, before the barrier below it
+      if (it + 2 < ntiles) load_tile(t0 + 2 * kAttKT);
+    }
+    __syncthreads();
   }
 
   // ---- epilogue: lane holds query l32, d = db*32 + 8*(r/4) + 4*g + r%4
