@@ -115,9 +115,20 @@ __device__ __forceinline__ uint4 buffer_load16(__amdgpu_buffer_rsrc_t r, int vof
   return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0));
 }
 
+// Software pipeline over "units" u = (tile t, key half kb): 32 keys x 64
+// queries per wave.  Within unit u the wave exponentiates S_u on the VALU
+// while the MFMA pipe computes S_{u+1} = K_{u+1} Q^T and O += V_{u-1} P_{u-1}:
+// the two instruction streams are interleaved in four chunks of four MFMAs
+// and one eighth of the exponentials each, so one wave keeps both pipes busy.
+// A tile is read from LDS during three consecutive iterations (K of the next
+// unit, V of the previous one), so four LDS buffers rotate and one barrier
+// per tile suffices: tile t+2 is written at the start of iteration t into the
+// buffer tile t-2 used, which every wave left before the previous barrier.
+constexpr int kAttBufs = 4;
+
 __global__ __launch_bounds__(kAttThreads, 2) void attn_bf16_kernel(AttnArgs a) {
-  __shared__ uint16_t Ks[2][kAttKT * kAttRow];
-  __shared__ uint16_t Vt[2][kAttD * kAttRow];
+  __shared__ uint16_t Ks[kAttBufs][kAttKT * kAttRow];
+  __shared__ uint16_t Vt[kAttBufs][kAttD * kAttRow];
 
   const int tid = threadIdx.x;
   const int wave = tid / kWave, lane = tid % kWave;
@@ -147,12 +158,16 @@ __global__ __launch_bounds__(kAttThreads, 2) void attn_bf16_kernel(AttnArgs a) {
     }
   }
 
-  // Tile loader.  K: thread -> key pair kp = tid / 8 (keys 2kp, 2kp+1), 16-byte
-  // column dv = tid % 8 (8 lanes cover one 128-byte key row).  Buffer loads
-  // against a per-tile resource that ends at the last valid key: rows past it
-  // read as zero, offsets stay 32-bit and need no per-tile address math.
-  const int kp = tid >> 3, dv = tid & 7;
-  const int off0 = (2 * kp) * row_bytes + dv * 16, off1 = off0 + row_bytes;
+  // Tile loader: buffer loads against a per-tile resource ending at the last
+  // valid key; rows past it read as zero.  K: thread -> keys kk and kk+32,
+  // 16-byte column dv (8 lanes per 128-byte row; the two rows of a 16-lane
+  // group land 32 words apart in LDS).  V: thread -> key pair (2kp, 2kp+1),
+  // column dvv; a wave's lanes walk all 32 key pairs of two columns, so its
+  // transposed 32-bit LDS writes cover 64 distinct banks.
+  const int kk = tid >> 3, dv = tid & 7;
+  const int kp = tid & 31, dvv = tid >> 5;
+  const int koff0 = kk * row_bytes + dv * 16, koff1 = koff0 + 32 * row_bytes;
+  const int voff0 = (2 * kp) * row_bytes + dvv * 16, voff1 = voff0 + row_bytes;
   uint4 kr0, kr1, vr0, vr1;
   auto load_tile = [&](int t0) {
     const int valid = min(k_end - t0, kAttKT);
@@ -161,26 +176,31 @@ __global__ __launch_bounds__(kAttThreads, 2) void attn_bf16_kernel(AttnArgs a) {
         const_cast<uint16_t*>(kb + static_cast<int64_t>(t0) * a.ld_kv), 0, nrec, kBufWord3);
     const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint16_t*>(vb + static_cast<int64_t>(t0) * a.ld_kv), 0, nrec, kBufWord3);
-    kr0 = buffer_load16(rk, off0);
-    kr1 = buffer_load16(rk, off1);
-    vr0 = buffer_load16(rv, off0);
-    vr1 = buffer_load16(rv, off1);
+    kr0 = buffer_load16(rk, koff0);
+    kr1 = buffer_load16(rk, koff1);
+    vr0 = buffer_load16(rv, voff0);
+    vr1 = buffer_load16(rv, voff1);
   };
   const int vpos = kperm16(2 * kp);
   auto store_tile = [&](int buf) {
-    *reinterpret_cast<uint4*>(&Ks[buf][(2 * kp) * kAttRow + dv * 8]) = kr0;
-    *reinterpret_cast<uint4*>(&Ks[buf][(2 * kp + 1) * kAttRow + dv * 8]) = kr1;
-    // V^T: element (key, d) -> Vt[d][kperm16(key)]; keys 2kp, 2kp+1 stay adjacent.
+    *reinterpret_cast<uint4*>(&Ks[buf][kk * kAttRow + dv * 8]) = kr0;
+    *reinterpret_cast<uint4*>(&Ks[buf][(kk + 32) * kAttRow + dv * 8]) = kr1;
     const uint32_t a0[4] = {vr0.x, vr0.y, vr0.z, vr0.w};
     const uint32_t a1[4] = {vr1.x, vr1.y, vr1.z, vr1.w};
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      // d = dv*8 + 2e: low halves of both keys; d + 1: high halves
       const uint32_t lo = __builtin_amdgcn_perm(a1[e], a0[e], 0x05040100u);
       const uint32_t hi = __builtin_amdgcn_perm(a1[e], a0[e], 0x07060302u);
-      *reinterpret_cast<uint32_t*>(&Vt[buf][(dv * 8 + 2 * e) * kAttRow + vpos]) = lo;
-      *reinterpret_cast<uint32_t*>(&Vt[buf][(dv * 8 + 2 * e + 1) * kAttRow + vpos]) = hi;
+      *reinterpret_cast<uint32_t*>(&Vt[buf][(dvv * 8 + 2 * e) * kAttRow + vpos]) = lo;
+      *reinterpret_cast<uint32_t*>(&Vt[buf][(dvv * 8 + 2 * e + 1) * kAttRow + vpos]) = hi;
     }
+  };
+  auto k_frag = [&](int buf, int kh, int ks) {
+    return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(&Ks[buf][(kh * 32 + l32) * kAttRow + ks * 16 + g * 8]));
+  };
+  auto v_frag = [&](int buf, int db, int kh, int t16) {
+    return __builtin_bit_cast(
+        bf16x8, *reinterpret_cast<const uint4*>(&Vt[buf][(db * 32 + l32) * kAttRow + kh * 32 + t16 * 16 + g * 8]));
   };
 
   f32x16 O[2][2];
@@ -194,112 +214,160 @@ __global__ __launch_bounds__(kAttThreads, 2) void attn_bf16_kernel(AttnArgs a) {
   float l_run[2] = {0.f, 0.f};
   const bf16x2 ones = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
 
-  // exponentiate one query block's scores with reference m; returns the
-  // lane's partial sum of the rounded weights
-  auto softmax_block = [&](const f32x16 (&S)[2][2], int qb2, float m, bf16x8 (&P)[2][2]) {
-    float lsum = 0.f;
+  // one eighth of a unit's exponentials: query block qb2, keys 16*t16 .. +15 of the half
+  auto exp_chunk = [&](const f32x16 (&S)[2], int qb2, int t16, const float (&m)[2], bf16x8 (&P)[2][2], float (&ls)[2]) {
+    uint32_t w[4];
 #pragma unroll
-    for (int kb2 = 0; kb2 < 2; ++kb2)
-#pragma unroll
-      for (int t16 = 0; t16 < 2; ++t16) {
-        uint32_t w[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float p0 = __builtin_amdgcn_exp2f(fmaf(S[kb2][qb2][t16 * 8 + 2 * e], a.c, -m));
-          const float p1 = __builtin_amdgcn_exp2f(fmaf(S[kb2][qb2][t16 * 8 + 2 * e + 1], a.c, -m));
-          w[e] = pack_bf16x2(p0, p1);
-          lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w[e]), ones, lsum, false);
-        }
-        P[kb2][t16] = __builtin_bit_cast(bf16x8, make_uint4(w[0], w[1], w[2], w[3]));
-      }
-    return lsum;
-  };
-
-  const int ntiles = (k_end - k_begin + kAttKT - 1) / kAttKT;
-  // prologue: tile 0 into buffer 0, tile 1 into registers
-  load_tile(k_begin);
-  store_tile(0);
-  if (ntiles > 1) load_tile(k_begin + kAttKT);
-  __syncthreads();
-  for (int it = 0; it < ntiles; ++it) {
-    const int buf = it & 1;
-    const int t0 = k_begin + it * kAttKT;
-
-    // ---- S^T = K Q^T for 2 key blocks x 2 query blocks
-    f32x16 S[2][2];
-#pragma unroll
-    for (int kb2 = 0; kb2 < 2; ++kb2) {
-#pragma unroll
-      for (int qb2 = 0; qb2 < 2; ++qb2)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) S[kb2][qb2][r] = 0.f;
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const bf16x8 kf = __builtin_bit_cast(
-            bf16x8, *reinterpret_cast<const uint4*>(&Ks[buf][(kb2 * 32 + l32) * kAttRow + ks * 16 + g * 8]));
-#pragma unroll
-        for (int qb2 = 0; qb2 < 2; ++qb2)
-          S[kb2][qb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[qb2][ks], S[kb2][qb2], 0, 0, 0);
-      }
+    for (int e = 0; e < 4; ++e) {
+      const float p0 = __builtin_amdgcn_exp2f(fmaf(S[qb2][t16 * 8 + 2 * e], a.c, -m[qb2]));
+      const float p1 = __builtin_amdgcn_exp2f(fmaf(S[qb2][t16 * 8 + 2 * e + 1], a.c, -m[qb2]));
+      w[e] = pack_bf16x2(p0, p1);
+      ls[qb2] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w[e]), ones, ls[qb2], false);
     }
-    // lane holds keys kb2*32 + 8*(r/4) + 4*g + r%4 of query l32
+    P[qb2][t16] = __builtin_bit_cast(bf16x8, make_uint4(w[0], w[1], w[2], w[3]));
+  };
+  // scores of a unit in the ragged last tile: keys past the range -> -inf
+  auto mask_unit = [&](f32x16 (&S)[2], int t0, int kh) {
     if (t0 + kAttKT > k_end) {
 #pragma unroll
-      for (int kb2 = 0; kb2 < 2; ++kb2)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = t0 + kb2 * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
-          if (key >= k_end) {
-            S[kb2][0][r] = -INFINITY;
-            S[kb2][1][r] = -INFINITY;
-          }
-        }
+      for (int r = 0; r < 16; ++r) {
+        const int key = t0 + kh * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
+        if (key >= k_end) { S[0][r] = -INFINITY; S[1][r] = -INFINITY; }
+      }
     }
-
-    // ---- softmax (fast path without the tile max), O^T += V^T P^T
-    bf16x8 P[2][2][2];  // [qb][kb][t16]
+  };
+  // One unit: exponentiate Scur (reference m_run) into Pcur while issuing
+  // Snext = K(buf_k, kh_next) Q^T and O += V(buf_v, kh_prev) Pprev.  Then the
+  // overflow guard / exact path for Pcur.  Returns nothing; updates l_run.
+  auto unit = [&](const f32x16 (&Scur)[2], bf16x8 (&Pcur)[2][2], f32x16 (&Snext)[2], int buf_k, int kh_next,
+                  const bf16x8 (&Pprev)[2][2], int buf_v, int kh_prev) {
+    const bf16x8 kf0 = k_frag(buf_k, kh_next, 0), kf1 = k_frag(buf_k, kh_next, 1);
+    const bf16x8 kf2 = k_frag(buf_k, kh_next, 2), kf3 = k_frag(buf_k, kh_next, 3);
+    const bf16x8 vf00 = v_frag(buf_v, 0, kh_prev, 0), vf01 = v_frag(buf_v, 0, kh_prev, 1);
+    const bf16x8 vf10 = v_frag(buf_v, 1, kh_prev, 0), vf11 = v_frag(buf_v, 1, kh_prev, 1);
+    float ls[2] = {0.f, 0.f};
+    const float m[2] = {m_run[0], m_run[1]};
+    f32x16 z;
 #pragma unroll
-    for (int qb2 = 0; qb2 < 2; ++qb2) {
-      float lsum = softmax_block(S, qb2, m_run[qb2], P[qb2]);
-      if (__builtin_amdgcn_ballot_w64(!(lsum <= kSumCap)) != 0) {  // rare: exact path
-        float mx = S[0][qb2][0];
+    for (int r = 0; r < 16; ++r) z[r] = 0.f;
+    // chunk 0
+    Snext[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf0, qf[0][0], z, 0, 0, 0);
+    Snext[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf0, qf[1][0], z, 0, 0, 0);
+    Snext[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf1, qf[0][1], Snext[0], 0, 0, 0);
+    Snext[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf1, qf[1][1], Snext[1], 0, 0, 0);
+    exp_chunk(Scur, 0, 0, m, Pcur, ls);
+    // chunk 1
+    Snext[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf2, qf[0][2], Snext[0], 0, 0, 0);
+    Snext[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf2, qf[1][2], Snext[1], 0, 0, 0);
+    Snext[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf3, qf[0][3], Snext[0], 0, 0, 0);
+    Snext[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf3, qf[1][3], Snext[1], 0, 0, 0);
+    exp_chunk(Scur, 0, 1, m, Pcur, ls);
+    // chunk 2
+    O[0][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf00, Pprev[0][0], O[0][0], 0, 0, 0);
+    O[1][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf00, Pprev[1][0], O[1][0], 0, 0, 0);
+    O[0][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf01, Pprev[0][1], O[0][0], 0, 0, 0);
+    O[1][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf01, Pprev[1][1], O[1][0], 0, 0, 0);
+    exp_chunk(Scur, 1, 0, m, Pcur, ls);
+    // chunk 3
+    O[0][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf10, Pprev[0][0], O[0][1], 0, 0, 0);
+    O[1][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf10, Pprev[1][0], O[1][1], 0, 0, 0);
+    O[0][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf11, Pprev[0][1], O[0][1], 0, 0, 0);
+    O[1][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf11, Pprev[1][1], O[1][1], 0, 0, 0);
+    exp_chunk(Scur, 1, 1, m, Pcur, ls);
+    // overflow guard; the exact path runs after this unit's MFMAs were issued,
+    // so the O rescale applies to everything accumulated so far
+    if (__builtin_amdgcn_ballot_w64(!(ls[0] <= kSumCap) || !(ls[1] <= kSumCap)) != 0) {
+      float mn[2];
 #pragma unroll
-        for (int kb2 = 0; kb2 < 2; ++kb2)
+      for (int qb2 = 0; qb2 < 2; ++qb2) {
+        float mx = Scur[qb2][0];
 #pragma unroll
-          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, S[kb2][qb2][r]);
+        for (int r = 1; r < 16; ++r) mx = fmaxf(mx, Scur[qb2][r]);
         mx = fmaxf(mx, __shfl_xor(mx, 32, kWave)) * a.c;
-        const float m_new = (mx > m_run[qb2] + kTau) ? mx : m_run[qb2];
-        const float alpha = __builtin_amdgcn_exp2f(m_run[qb2] - m_new);
-        m_run[qb2] = m_new;
+        mn[qb2] = (mx > m_run[qb2] + kTau) ? mx : m_run[qb2];
+        const float alpha = __builtin_amdgcn_exp2f(m_run[qb2] - mn[qb2]);
+        m_run[qb2] = mn[qb2];
         l_run[qb2] *= alpha;
 #pragma unroll
         for (int db = 0; db < 2; ++db)
 #pragma unroll
           for (int r = 0; r < 16; ++r) O[qb2][db][r] *= alpha;
-        lsum = softmax_block(S, qb2, m_new, P[qb2]);
       }
-      l_run[qb2] += lsum;
+      ls[0] = 0.f;
+      ls[1] = 0.f;
+#pragma unroll
+      for (int qb2 = 0; qb2 < 2; ++qb2)
+#pragma unroll
+        for (int t16 = 0; t16 < 2; ++t16) exp_chunk(Scur, qb2, t16, mn, Pcur, ls);
     }
+    l_run[0] += ls[0];
+    l_run[1] += ls[1];
+  };
+
+  const int ntiles = (k_end - k_begin + kAttKT - 1) / kAttKT;
+  // prologue: tiles 0 and 1 into buffers 0 and 1, tile 2 into registers; the
+  // V^T buffer of "tile -1" (buffer 3) holds zeros for the first unit's
+  // (empty) O update
+  load_tile(k_begin);
+  store_tile(0);
+  if (ntiles > 1) {
+    load_tile(k_begin + kAttKT);
+    store_tile(1);
+  }
+  for (int i = tid; i < kAttD * kAttRow / 2; i += kAttThreads) reinterpret_cast<uint32_t*>(Vt[3])[i] = 0u;
+  if (ntiles > 2) load_tile(k_begin + 2 * kAttKT);
+  __syncthreads();
+
+  f32x16 S0[2], S1[2];   // scores of the current tile's first / second key half
+  bf16x8 P0[2][2], P1[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      P0[i][j] = __builtin_bit_cast(bf16x8, make_uint4(0, 0, 0, 0));
+      P1[i][j] = __builtin_bit_cast(bf16x8, make_uint4(0, 0, 0, 0));
+    }
+  {
+    f32x16 z;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) z[r] = 0.f;
+    S0[0] = z;
+    S0[1] = z;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const bf16x8 kf = k_frag(0, 0, ks);
+      S0[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[0][ks], S0[0], 0, 0, 0);
+      S0[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[1][ks], S0[1], 0, 0, 0);
+    }
+  }
+
+  for (int t = 0; t < ntiles; ++t) {
+    const int t0 = k_begin + t * kAttKT;
+    if (t + 2 < ntiles) {
+      store_tile((t + 2) & 3);
+      if (t + 3 < ntiles) load_tile(t0 + 3 * kAttKT);
+    }
+    const int bt = t & 3, bprev = (t + 3) & 3, bnext = (t + 1) & 3;
+    // unit (t, 0): softmax S0 -> P0; S1 = K(t, half 1) Q^T; O += V(t-1, half 1) P1
+    mask_unit(S0, t0, 0);
+    unit(S0, P0, S1, bt, 1, P1, bprev, 1);
+    // unit (t, 1): softmax S1 -> P1; S0 = K(t+1, half 0) Q^T (unused after the
+    // last tile); O += V(t, half 0) P0
+    mask_unit(S1, t0, 1);
+    unit(S1, P1, S0, bnext, 0, P0, bt, 0);
+    __syncthreads();
+  }
+  // drain: O += V(last, half 1) P1
+  {
+    const int bl = (ntiles - 1) & 3;
 #pragma unroll
     for (int db = 0; db < 2; ++db)
 #pragma unroll
-      for (int kb2 = 0; kb2 < 2; ++kb2)
-#pragma unroll
-        for (int t16 = 0; t16 < 2; ++t16) {
-          const bf16x8 vf = __builtin_bit_cast(
-              bf16x8,
-              *reinterpret_cast<const uint4*>(&Vt[buf][(db * 32 + l32) * kAttRow + kb2 * 32 + t16 * 16 + g * 8]));
-#pragma unroll
-          for (int qb2 = 0; qb2 < 2; ++qb2)
-            O[qb2][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, P[qb2][kb2][t16], O[qb2][db], 0, 0, 0);
-        }
-
-    // ---- stage tile it+1 (already in registers) into the other buffer, fetch tile it+2
-    if (it + 1 < ntiles) {
-      store_tile(buf ^ 1);  // buffer buf^1 was last read in iteration it-1, before the barrier below it
-      if (it + 2 < ntiles) load_tile(t0 + 2 * kAttKT);
-    }
-    __syncthreads();
+      for (int t16 = 0; t16 < 2; ++t16) {
+        const bf16x8 vf = v_frag(bl, db, 1, t16);
+        O[0][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, P1[0][t16], O[0][db], 0, 0, 0);
+        O[1][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, P1[1][t16], O[1][db], 0, 0, 0);
+      }
   }
 
   // ---- epilogue: lane holds query l32, d = db*32 + 8*(r/4) + 4*g + r%4
