@@ -8,14 +8,16 @@
 //
 // bf16 path: implicit GEMM on MFMA.  M = output channels (A = weights,
 // [Cout][tap][Cin] rows are K-contiguous), N = output pixels (B = input
-// pixels, channel-contiguous in NHWC), K = 9 taps x Cin.  A workgroup owns a
-// 128-channel x 128-pixel tile, the pixels being TR rows x TC columns of the
-// patch.  For each 64-channel slice of Cin the (TR+2) x (TC+2) input band,
-// halos included, is staged once in LDS and reused by all nine taps; the
-// weights of one tap are staged per step.  Four waves each compute 64 x 64
-// with v_mfma_f32_16x16x32_bf16; the accumulator's lane layout gives each lane
-// four consecutive output channels of one pixel, stored as one 8-byte write.
-// Loads for the next step are issued before the current step's MFMAs.
+// pixels, channel-contiguous in NHWC), K = 9 taps x Cin.  A workgroup owns 2
+// patch rows x 16*TG columns x 128 output channels (TG chosen per width so
+// the tiles cover the rows exactly where possible: 240 columns -> 3 tiles of
+// 80, one workgroup per CU).  For each 64-channel slice of Cin the halo band
+// (4 rows x 16*TG+2 columns, halo rows from the stale image) is staged once in
+// LDS and reused by all nine taps; the weights of one tap are staged per
+// step; both double-buffered.  Four waves each compute 64 channels x 16*TG
+// pixels with v_mfma_f32_16x16x32_bf16; the accumulator's lane layout gives
+// each lane four consecutive output channels of one pixel, stored as one
+// 8-byte write.
 //
 // f32 path: one thread per output element, direct loops (small shapes).
 #include "dpp_common.h"
@@ -56,10 +58,20 @@ __global__ __launch_bounds__(256) void conv3x3_f32_kernel(float* __restrict__ y,
 }
 
 // ------------------------------------------------------------------ bf16 MFMA implicit GEMM
+// Workgroup tile: 2 patch rows x 16*TG columns of output pixels x 128 output
+// channels; four waves, wave (wr, wn) owns tile row wr and channels
+// [64 wn, 64 wn + 64): TG x 4 accumulator tiles of 16 x 16.  The host picks TG
+// (1..5) so that the tiles cover the row width with the least waste and the
+// workgroup count fills the 256 CUs in whole rounds (e.g. 240 columns ->
+// TG 5: three tiles per row pair).
+// K loop: step = (64-channel slice, tap).  The (2+2) x (16 TG + 2) halo band
+// of a slice is staged once and reused by its nine taps; the weights of one
+// tap (128 x 64) per step.  Both are double-buffered in LDS, the next step's
+// global loads are issued right after the step's single barrier.
 constexpr int kConvThreads = 256;
 constexpr int kConvBM = 128;  // output channels per workgroup
-constexpr int kConvBN = 128;  // output pixels per workgroup
 constexpr int kConvKC = 64;   // input channels per slice (8 x 16-byte vectors)
+constexpr int kConvTR = 2;    // patch rows per workgroup
 
 struct ConvArgs {
   const uint16_t* x;
@@ -68,7 +80,7 @@ struct ConvArgs {
   const float* bias;
   uint16_t* y;
   int H, W, Cin, Cout, row0, rows;
-  int tiles_c;  // column tiles per patch row band
+  int tiles_c;  // column tiles per row pair
 };
 
 // LDS row of 8 x 16-byte slots, slot index XOR-swizzled by the row index so
@@ -76,141 +88,160 @@ struct ConvArgs {
 // the banks.
 __device__ __forceinline__ int swz(int row, int slot) { return row * 8 + (slot ^ (row & 7)); }
 
-template <int TC>
-__global__ __launch_bounds__(kConvThreads) void conv3x3_bf16_mfma_kernel(ConvArgs a) {
-  constexpr int TR = kConvBN / TC;
-  constexpr int BW = TC + 2;           // band columns
-  constexpr int BPIX = (TR + 2) * BW;  // band pixels
-  constexpr int BAND_VEC = BPIX * 8;   // 16-byte vectors per band
+template <int TG>
+__global__ __launch_bounds__(kConvThreads, 1) void conv3x3_bf16_mfma_kernel(ConvArgs a) {
+  constexpr int TC = 16 * TG;           // output columns per tile
+  constexpr int BW = TC + 2;            // band columns
+  constexpr int BPIX = (kConvTR + 2) * BW;
+  constexpr int BAND_VEC = BPIX * 8;    // 16-byte vectors per band
   constexpr int BAND_ITERS = (BAND_VEC + kConvThreads - 1) / kConvThreads;
-  constexpr int W_VEC = kConvBM * 8;
-  constexpr int W_ITERS = W_VEC / kConvThreads;  // 4
+  constexpr int W_ITERS = kConvBM * 8 / kConvThreads;  // 4
 
-  __shared__ uint4 band[BPIX * 8];
-  __shared__ uint4 wts[kConvBM * 8];
+  __shared__ uint4 band[2][BPIX * 8];
+  __shared__ uint4 wts[2][kConvBM * 8];
 
   const int tid = threadIdx.x;
   const int wave = tid / kWave, lane = tid % kWave;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wr = wave >> 1, wn = wave & 1;
   const int b = blockIdx.z;
   const int m0 = blockIdx.y * kConvBM;
   const int tile_r = blockIdx.x / a.tiles_c, tile_c = blockIdx.x % a.tiles_c;
-  const int pr0 = tile_r * TR, pc0 = tile_c * TC;  // patch-relative origin of the pixel tile
+  const int pr0 = tile_r * kConvTR, pc0 = tile_c * TC;  // patch-relative origin of the pixel tile
   const int H = a.H, W = a.W, Cin = a.Cin;
   const int64_t ktot = 9LL * Cin;
 
-  // -------- global -> register staging
   uint4 band_reg[BAND_ITERS];
   uint4 w_reg[W_ITERS];
+
+  // Per-thread source pointers, computed once: band vector u of the first
+  // slice (x for patch rows, the stale image for halo rows; nullptr = zero
+  // padding) and the four weight rows.  Each step only adds a uniform offset.
+  const uint16_t* band_src[BAND_ITERS];
+#pragma unroll
+  for (int u = 0; u < BAND_ITERS; ++u) {
+    const int id = tid + u * kConvThreads;
+    band_src[u] = nullptr;
+    if (id < BAND_VEC) {
+      const int pix = id >> 3, slot = id & 7;
+      const int br = pix / BW, bc = pix % BW;
+      const int r = pr0 - 1 + br;  // patch-relative
+      const int ir = a.row0 + r;   // image row
+      const int col = pc0 - 1 + bc;
+      if (ir >= 0 && ir < H && col >= 0 && col < W)
+        band_src[u] = ((r >= 0 && r < a.rows) ? a.x + ((static_cast<int64_t>(b) * a.rows + r) * W + col) * Cin
+                                              : a.stale + ((static_cast<int64_t>(b) * H + ir) * W + col) * Cin) +
+                      slot * 8;
+    }
+  }
+  const uint16_t* w_src[W_ITERS];
+#pragma unroll
+  for (int u = 0; u < W_ITERS; ++u) {
+    const int id = tid + u * kConvThreads;
+    const int m = id >> 3, slot = id & 7;
+    w_src[u] = (m0 + m < a.Cout) ? a.w + (m0 + m) * ktot + slot * 8 : nullptr;
+  }
 
   auto load_band = [&](int c0) {
 #pragma unroll
     for (int u = 0; u < BAND_ITERS; ++u) {
-      const int id = tid + u * kConvThreads;
       uint4 v = make_uint4(0, 0, 0, 0);
-      if (id < BAND_VEC) {
-        const int pix = id >> 3, slot = id & 7;
-        const int br = pix / BW, bc = pix % BW;
-        const int r = pr0 - 1 + br;  // patch-relative
-        const int ir = a.row0 + r;   // image row
-        const int col = pc0 - 1 + bc;
-        if (ir >= 0 && ir < H && col >= 0 && col < W) {
-          const uint16_t* src = (r >= 0 && r < a.rows)
-                                    ? a.x + ((static_cast<int64_t>(b) * a.rows + r) * W + col) * Cin
-                                    : a.stale + ((static_cast<int64_t>(b) * H + ir) * W + col) * Cin;
-          v = *reinterpret_cast<const uint4*>(src + c0 + slot * 8);
-        }
-      }
+      if (band_src[u] != nullptr) v = *reinterpret_cast<const uint4*>(band_src[u] + c0);
       band_reg[u] = v;
     }
   };
   auto load_w = [&](int tap, int c0) {
+    const int off = tap * Cin + c0;
 #pragma unroll
     for (int u = 0; u < W_ITERS; ++u) {
-      const int id = tid + u * kConvThreads;
-      const int m = id >> 3, slot = id & 7;
       uint4 v = make_uint4(0, 0, 0, 0);
-      if (m0 + m < a.Cout) v = *reinterpret_cast<const uint4*>(a.w + (m0 + m) * ktot + tap * Cin + c0 + slot * 8);
+      if (w_src[u] != nullptr) v = *reinterpret_cast<const uint4*>(w_src[u] + off);
       w_reg[u] = v;
     }
   };
-  auto store_band = [&]() {
+  auto store_band = [&](int buf) {
 #pragma unroll
     for (int u = 0; u < BAND_ITERS; ++u) {
       const int id = tid + u * kConvThreads;
-      if (id < BAND_VEC) band[swz(id >> 3, id & 7)] = band_reg[u];
+      if (id < BAND_VEC) band[buf][swz(id >> 3, id & 7)] = band_reg[u];
     }
   };
-  auto store_w = [&]() {
+  auto store_w = [&](int buf) {
 #pragma unroll
     for (int u = 0; u < W_ITERS; ++u) {
       const int id = tid + u * kConvThreads;
-      wts[swz(id >> 3, id & 7)] = w_reg[u];
+      wts[buf][swz(id >> 3, id & 7)] = w_reg[u];
     }
   };
 
-  f32x4 acc[4][4];
+  f32x4 acc[4][TG];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < TG; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // Per-lane pixel coordinates of the four 16-pixel groups of this wave.
-  int pix_tr[4], pix_tc[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int pt = wn * 64 + j * 16 + (lane & 15);
-    pix_tr[j] = pt / TC;
-    pix_tc[j] = pt % TC;
-  }
-  const int kg = lane >> 4;  // 0..3: which 8-element k group of the 32-wide MFMA step
-
+  const int kg = lane >> 4;     // 0..3: which 8-element k group of the 32-wide MFMA step
+  const int pl = lane & 15;     // pixel (B) / channel (A) row within a 16-group
+  // A fragment rows m = wn*64 + 16 i + pl share (m & 7) = (pl & 7): one swizzled
+  // slot per k step, fragment i at a fixed +16 rows.
+  const int a_row0 = wn * 64 + pl;
+  const int a_slot[2] = {(0 + kg) ^ (pl & 7), (4 + kg) ^ (pl & 7)};
   const int nslices = Cin / kConvKC;
   const int nsteps = nslices * 9;
+  // prologue: step 0 staged, step 1's weights in registers
   load_band(0);
   load_w(0, 0);
+  store_band(0);
+  store_w(0);
+  if (nsteps > 1) load_w(1, 0);
+  __syncthreads();
   for (int step = 0; step < nsteps; ++step) {
-    const int slice = step / 9, tap = step % 9;
-    __syncthreads();  // previous step's LDS reads are done
-    if (tap == 0) store_band();
-    store_w();
-    __syncthreads();
-    if (step + 1 < nsteps) {
-      const int ns = step + 1, nslice = ns / 9, ntap = ns % 9;
-      if (ntap == 0) load_band(nslice * kConvKC);
-      load_w(ntap, nslice * kConvKC);
-    }
-    (void)slice;
-    const int dy = tap / 3, dx = tap % 3;
+    const int slice = step / 9, tap = step - slice * 9;
+    const int bb = slice & 1, wb = step & 1;
+    // the next slice's band: fetched during this slice's first tap
+    if (tap == 0 && slice + 1 < nslices) load_band((slice + 1) * kConvKC);
+    const int dy = tap / 3, dx = tap - dy * 3;
+    // B fragment rows bp = (wr + dy) * BW + dx + 16 j + pl: all fragments of a
+    // tap share (bp & 7), so one swizzled slot per k step serves all j
+    const int bp0 = (wr + dy) * BW + dx + pl;
+    const int b_x = bp0 & 7;
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-      bf16x8 af[4], bfr[4];
+      bf16x8 af[4], bfr[TG];
+      const int bslot = (ks * 4 + kg) ^ b_x;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int m = wm * 64 + i * 16 + (lane & 15);
-        af[i] = __builtin_bit_cast(bf16x8, wts[swz(m, ks * 4 + kg)]);
-      }
+      for (int i = 0; i < 4; ++i) af[i] = __builtin_bit_cast(bf16x8, wts[wb][(a_row0 + 16 * i) * 8 + a_slot[ks]]);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int bp = (pix_tr[j] + dy) * BW + pix_tc[j] + dx;
-        bfr[j] = __builtin_bit_cast(bf16x8, band[swz(bp, ks * 4 + kg)]);
-      }
+      for (int j = 0; j < TG; ++j) bfr[j] = __builtin_bit_cast(bf16x8, band[bb][(bp0 + 16 * j) * 8 + bslot]);
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+        for (int j = 0; j < TG; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+    }
+    // stage step+1: its weights (already in registers) and, at a slice
+    // boundary, the next band; buffers (step+1)&1 and (slice+1)&1 were last
+    // read before the previous barrier
+    if (step + 1 < nsteps) {
+      store_w(wb ^ 1);
+      if (tap == 8) store_band(bb ^ 1);
+    }
+    __syncthreads();
+    if (step + 2 < nsteps) {
+      const int s2 = step + 2, sl2 = s2 / 9;
+      load_w(s2 - sl2 * 9, sl2 * kConvKC);
     }
   }
 
-  // -------- epilogue: lane holds channels m0 + wm*64 + i*16 + 4*(lane/16) + 0..3 of one pixel
+  // -------- epilogue: lane holds channels m0 + wn*64 + i*16 + 4*(lane/16) + 0..3 of one pixel
+  const int r = pr0 + wr;
+  if (r >= a.rows) return;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int r = pr0 + pix_tr[j], col = pc0 + pix_tc[j];
-    if (r >= a.rows || col >= W) continue;
+  for (int j = 0; j < TG; ++j) {
+    const int col = pc0 + j * 16 + pl;
+    if (col >= W) continue;
     uint16_t* yp = a.y + ((static_cast<int64_t>(b) * a.rows + r) * W + col) * a.Cout;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int m = m0 + wm * 64 + i * 16 + 4 * kg;
+      const int m = m0 + wn * 64 + i * 16 + 4 * kg;
       if (m >= a.Cout) continue;
       float v0 = acc[i][j][0], v1 = acc[i][j][1], v2 = acc[i][j][2], v3 = acc[i][j][3];
       if (a.bias) { v0 += a.bias[m]; v1 += a.bias[m + 1]; v2 += a.bias[m + 2]; v3 += a.bias[m + 3]; }
@@ -220,6 +251,22 @@ __global__ __launch_bounds__(kConvThreads) void conv3x3_bf16_mfma_kernel(ConvArg
       *reinterpret_cast<uint2*>(yp + m) = out;
     }
   }
+}
+
+// Column-tile choice: the TG (1..5 groups of 16 columns) whose tiles waste the
+// fewest columns; ties go to the larger tile.
+static int conv_pick_tg(int64_t W) {
+  int best = 1;
+  int64_t best_waste = -1;
+  for (int tg = 1; tg <= 5; ++tg) {
+    const int64_t tc = 16 * tg;
+    const int64_t waste = ceil_div(W, tc) * tc - W;
+    if (best_waste < 0 || waste < best_waste || (waste == best_waste && tg > best)) {
+      best = tg;
+      best_waste = waste;
+    }
+  }
+  return best;
 }
 
 hipError_t launch_conv3x3(void* y, const void* x, const void* stale_full, const void* weight, const float* bias,
@@ -246,17 +293,17 @@ hipError_t launch_conv3x3(void* y, const void* x, const void* stale_full, const 
   a.Cout = static_cast<int>(Cout);
   a.row0 = static_cast<int>(row0);
   a.rows = static_cast<int>(rows);
-  const int TC = W > 32 ? 64 : (W > 16 ? 32 : 16);
-  const int TR = kConvBN / TC;
-  a.tiles_c = static_cast<int>(ceil_div(W, TC));
-  const int64_t tiles = ceil_div(rows, TR) * a.tiles_c;
+  const int tg = conv_pick_tg(W);
+  a.tiles_c = static_cast<int>(ceil_div(W, 16 * tg));
+  const int64_t tiles = ceil_div(rows, kConvTR) * a.tiles_c;
   dim3 grid(static_cast<unsigned>(tiles), static_cast<unsigned>(ceil_div(Cout, kConvBM)), static_cast<unsigned>(B));
-  if (TC == 64)
-    hipLaunchKernelGGL(conv3x3_bf16_mfma_kernel<64>, grid, dim3(kConvThreads), 0, s, a);
-  else if (TC == 32)
-    hipLaunchKernelGGL(conv3x3_bf16_mfma_kernel<32>, grid, dim3(kConvThreads), 0, s, a);
-  else
-    hipLaunchKernelGGL(conv3x3_bf16_mfma_kernel<16>, grid, dim3(kConvThreads), 0, s, a);
+  switch (tg) {
+    case 1: hipLaunchKernelGGL(conv3x3_bf16_mfma_kernel<1>, grid, dim3(kConvThreads), 0, s, a); break;
+    case 2: hipLaunchKernelGGL(conv3x3_bf16_mfma_kernel<2>, grid, dim3(kConvThreads), 0, s, a); break;
+    case 3: hipLaunchKernelGGL(conv3x3_bf16_mfma_kernel<3>, grid, dim3(kConvThreads), 0, s, a); break;
+    case 4: hipLaunchKernelGGL(conv3x3_bf16_mfma_kernel<4>, grid, dim3(kConvThreads), 0, s, a); break;
+    default: hipLaunchKernelGGL(conv3x3_bf16_mfma_kernel<5>, grid, dim3(kConvThreads), 0, s, a); break;
+  }
   return hipGetLastError();
 }
 
