@@ -14,10 +14,11 @@
 // 80, one workgroup per CU).  For each 64-channel slice of Cin the halo band
 // (4 rows x 16*TG+2 columns, halo rows from the stale image) is staged once in
 // LDS and reused by all nine taps; the weights of one tap are staged per
-// step; both double-buffered.  Four waves each compute 64 channels x 16*TG
-// pixels with v_mfma_f32_16x16x32_bf16; the accumulator's lane layout gives
-// each lane four consecutive output channels of one pixel, stored as one
-// 8-byte write.
+// step; both double-buffered in LDS, weights fetched two steps ahead into
+// registers.  Eight waves (two per SIMD) each compute 32 channels x 16*TG
+// pixels of one tile row with v_mfma_f32_16x16x32_bf16; the accumulator's
+// lane layout gives each lane four consecutive output channels of one pixel,
+// stored as one 8-byte write.
 //
 // f32 path: one thread per output element, direct loops (small shapes).
 #include "dpp_common.h"
@@ -59,16 +60,20 @@ __global__ __launch_bounds__(256) void conv3x3_f32_kernel(float* __restrict__ y,
 
 // ------------------------------------------------------------------ bf16 MFMA implicit GEMM
 // Workgroup tile: 2 patch rows x 16*TG columns of output pixels x 128 output
-// channels; four waves, wave (wr, wn) owns tile row wr and channels
-// [64 wn, 64 wn + 64): TG x 4 accumulator tiles of 16 x 16.  The host picks TG
+// channels; 2 x kConvWN waves, wave (wr, wn) owns tile row wr and channels
+// [CW wn, CW wn + CW): TG x CW/16 accumulator tiles of 16 x 16.  The host picks TG
 // (1..5) so that the tiles cover the row width with the least waste and the
 // workgroup count fills the 256 CUs in whole rounds (e.g. 240 columns ->
 // TG 5: three tiles per row pair).
 // K loop: step = (64-channel slice, tap).  The (2+2) x (16 TG + 2) halo band
 // of a slice is staged once and reused by its nine taps; the weights of one
-// tap (128 x 64) per step.  Both are double-buffered in LDS, the next step's
-// global loads are issued right after the step's single barrier.
-constexpr int kConvThreads = 256;
+// tap (128 x 64) per step.  Both are double-buffered in LDS; weights are
+// fetched into registers two steps ahead, right after a step's single
+// barrier.
+constexpr int kConvWN = 4;                      // waves across the 128 output channels
+constexpr int kConvCW = 128 / kConvWN;          // output channels per wave
+constexpr int kConvCG = kConvCW / 16;           // 16-channel MFMA groups per wave
+constexpr int kConvThreads = 2 * kConvWN * 64;  // 2 tile rows x kConvWN
 constexpr int kConvBM = 128;  // output channels per workgroup
 constexpr int kConvKC = 64;   // input channels per slice (8 x 16-byte vectors)
 constexpr int kConvTR = 2;    // patch rows per workgroup
@@ -95,14 +100,14 @@ __global__ __launch_bounds__(kConvThreads, 1) void conv3x3_bf16_mfma_kernel(Conv
   constexpr int BPIX = (kConvTR + 2) * BW;
   constexpr int BAND_VEC = BPIX * 8;    // 16-byte vectors per band
   constexpr int BAND_ITERS = (BAND_VEC + kConvThreads - 1) / kConvThreads;
-  constexpr int W_ITERS = kConvBM * 8 / kConvThreads;  // 4
+  constexpr int W_ITERS = kConvBM * 8 / kConvThreads;
 
   __shared__ uint4 band[2][BPIX * 8];
   __shared__ uint4 wts[2][kConvBM * 8];
 
   const int tid = threadIdx.x;
   const int wave = tid / kWave, lane = tid % kWave;
-  const int wr = wave >> 1, wn = wave & 1;
+  const int wr = wave / kConvWN, wn = wave % kConvWN;
   const int b = blockIdx.z;
   const int m0 = blockIdx.y * kConvBM;
   const int tile_r = blockIdx.x / a.tiles_c, tile_c = blockIdx.x % a.tiles_c;
@@ -111,7 +116,7 @@ __global__ __launch_bounds__(kConvThreads, 1) void conv3x3_bf16_mfma_kernel(Conv
   const int64_t ktot = 9LL * Cin;
 
   uint4 band_reg[BAND_ITERS];
-  uint4 w_reg[W_ITERS];
+  uint4 w_regA[W_ITERS], w_regB[W_ITERS];  // weights of the next two steps
 
   // Per-thread source pointers, computed once: band vector u of the first
   // slice (x for patch rows, the stale image for halo rows; nullptr = zero
@@ -149,8 +154,9 @@ __global__ __launch_bounds__(kConvThreads, 1) void conv3x3_bf16_mfma_kernel(Conv
       band_reg[u] = v;
     }
   };
-  auto load_w = [&](int tap, int c0) {
-    const int off = tap * Cin + c0;
+  auto load_w = [&](uint4 (&w_reg)[W_ITERS], int step) {
+    const int sl = step / 9;
+    const int off = (step - sl * 9) * Cin + sl * kConvKC;
 #pragma unroll
     for (int u = 0; u < W_ITERS; ++u) {
       uint4 v = make_uint4(0, 0, 0, 0);
@@ -165,7 +171,7 @@ __global__ __launch_bounds__(kConvThreads, 1) void conv3x3_bf16_mfma_kernel(Conv
       if (id < BAND_VEC) band[buf][swz(id >> 3, id & 7)] = band_reg[u];
     }
   };
-  auto store_w = [&](int buf) {
+  auto store_w = [&](const uint4 (&w_reg)[W_ITERS], int buf) {
 #pragma unroll
     for (int u = 0; u < W_ITERS; ++u) {
       const int id = tid + u * kConvThreads;
@@ -173,31 +179,28 @@ __global__ __launch_bounds__(kConvThreads, 1) void conv3x3_bf16_mfma_kernel(Conv
     }
   };
 
-  f32x4 acc[4][TG];
+  f32x4 acc[kConvCG][TG];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < kConvCG; ++i)
 #pragma unroll
     for (int j = 0; j < TG; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const int kg = lane >> 4;     // 0..3: which 8-element k group of the 32-wide MFMA step
   const int pl = lane & 15;     // pixel (B) / channel (A) row within a 16-group
-  // A fragment rows m = wn*64 + 16 i + pl share (m & 7) = (pl & 7): one swizzled
+  // A fragment rows m = wn*CW + 16 i + pl share (m & 7) = (pl & 7): one swizzled
   // slot per k step, fragment i at a fixed +16 rows.
-  const int a_row0 = wn * 64 + pl;
+  const int a_row0 = wn * kConvCW + pl;
   const int a_slot[2] = {(0 + kg) ^ (pl & 7), (4 + kg) ^ (pl & 7)};
   const int nslices = Cin / kConvKC;
   const int nsteps = nslices * 9;
-  // prologue: step 0 staged, step 1's weights in registers
-  load_band(0);
-  load_w(0, 0);
-  store_band(0);
-  store_w(0);
-  if (nsteps > 1) load_w(1, 0);
-  __syncthreads();
-  for (int step = 0; step < nsteps; ++step) {
+  // One step: MFMAs on the staged weights/band of `step`; then stage the
+  // weights of step+1 (held in wnext) and, at a slice end, the next band;
+  // barrier; then fetch the weights of step+3 into wnext (two steps of
+  // latency cover).  Buffers written here were last read before the
+  // previous barrier.
+  auto do_step = [&](int step, uint4 (&wnext)[W_ITERS]) {
     const int slice = step / 9, tap = step - slice * 9;
     const int bb = slice & 1, wb = step & 1;
-    // the next slice's band: fetched during this slice's first tap
     if (tap == 0 && slice + 1 < nslices) load_band((slice + 1) * kConvKC);
     const int dy = tap / 3, dx = tap - dy * 3;
     // B fragment rows bp = (wr + dy) * BW + dx + 16 j + pl: all fragments of a
@@ -206,32 +209,39 @@ __global__ __launch_bounds__(kConvThreads, 1) void conv3x3_bf16_mfma_kernel(Conv
     const int b_x = bp0 & 7;
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-      bf16x8 af[4], bfr[TG];
+      bf16x8 af[kConvCG], bfr[TG];
       const int bslot = (ks * 4 + kg) ^ b_x;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) af[i] = __builtin_bit_cast(bf16x8, wts[wb][(a_row0 + 16 * i) * 8 + a_slot[ks]]);
+      for (int i = 0; i < kConvCG; ++i) af[i] = __builtin_bit_cast(bf16x8, wts[wb][(a_row0 + 16 * i) * 8 + a_slot[ks]]);
 #pragma unroll
       for (int j = 0; j < TG; ++j) bfr[j] = __builtin_bit_cast(bf16x8, band[bb][(bp0 + 16 * j) * 8 + bslot]);
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < kConvCG; ++i)
 #pragma unroll
         for (int j = 0; j < TG; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
     }
-    // stage step+1: its weights (already in registers) and, at a slice
-    // boundary, the next band; buffers (step+1)&1 and (slice+1)&1 were last
-    // read before the previous barrier
     if (step + 1 < nsteps) {
-      store_w(wb ^ 1);
+      store_w(wnext, wb ^ 1);
       if (tap == 8) store_band(bb ^ 1);
     }
     __syncthreads();
-    if (step + 2 < nsteps) {
-      const int s2 = step + 2, sl2 = s2 / 9;
-      load_w(s2 - sl2 * 9, sl2 * kConvKC);
-    }
+    if (step + 3 < nsteps) load_w(wnext, step + 3);
+  };
+
+  // prologue: step 0 staged; steps 1 and 2 in registers
+  load_band(0);
+  load_w(w_regB, 0);
+  store_band(0);
+  store_w(w_regB, 0);
+  if (nsteps > 1) load_w(w_regA, 1);
+  if (nsteps > 2) load_w(w_regB, 2);
+  __syncthreads();
+  for (int step = 0; step < nsteps; step += 2) {
+    do_step(step, w_regA);
+    if (step + 1 < nsteps) do_step(step + 1, w_regB);
   }
 
-  // -------- epilogue: lane holds channels m0 + wn*64 + i*16 + 4*(lane/16) + 0..3 of one pixel
+  // -------- epilogue: lane holds channels m0 + wn*CW + i*16 + 4*(lane/16) + 0..3 of one pixel
   const int r = pr0 + wr;
   if (r >= a.rows) return;
 #pragma unroll
@@ -240,8 +250,8 @@ __global__ __launch_bounds__(kConvThreads, 1) void conv3x3_bf16_mfma_kernel(Conv
     if (col >= W) continue;
     uint16_t* yp = a.y + ((static_cast<int64_t>(b) * a.rows + r) * W + col) * a.Cout;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int m = m0 + wn * 64 + i * 16 + 4 * kg;
+    for (int i = 0; i < kConvCG; ++i) {
+      const int m = m0 + wn * kConvCW + i * 16 + 4 * kg;
       if (m >= a.Cout) continue;
       float v0 = acc[i][j][0], v1 = acc[i][j][1], v2 = acc[i][j][2], v3 = acc[i][j][3];
       if (a.bias) { v0 += a.bias[m]; v1 += a.bias[m + 1]; v2 += a.bias[m + 2]; v3 += a.bias[m + 3]; }
