@@ -43,6 +43,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=12.0, help="target oracle time for the CPU baseline")
     ap.add_argument("--kernels", action="store_true", help="also time every kernel family separately")
+    ap.add_argument("--hbm-sweep", action="store_true",
+                    help="also time splice / GroupNorm / CFG over a size sweep, warm and cold last-level cache")
     return ap.parse_args()
 
 
@@ -229,6 +231,8 @@ def main():
     }
     if kernels:
         out["kernels"] = kernels
+    if args.hbm_sweep:
+        out["hbm_sweep"] = hbm_sweep(cfg, dpp, torch)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(cfg, args.cpu_budget_s)
     print(json.dumps(out), flush=True)
@@ -276,6 +280,64 @@ def time_kernels(cfg, layer, x_patches, gamma, beta, w, b, eps, rel, eps_c, eps_
         rate = amount / (ms * 1e-3) / (1e12 if unit == "TFLOP/s" else 1e9)
         res[k] = {"avg_ms": round(ms, 5), unit: round(rate, 2), "frac_peak": round(rate / peak, 4),
                   "work": amount}
+    return res
+
+
+def hbm_sweep(cfg, dpp, torch, reps=20):
+    """Bandwidth of the HBM-bound calls over sizes: the 3840 px patch stacked
+    B = 1, 4, 16 times (splice, GroupNorm) and n = 2^16 .. 2^26 (CFG).  Warm:
+    back-to-back calls; cold: a 512 MB write between calls evicts the 256 MB
+    last-level cache.  Algorithmic bytes: one read and one write of the patch
+    (plus the tiny statistics) / three n-element streams."""
+    dev = "cuda"
+    flush = torch.empty(512 * 2 ** 20 // 4, dtype=torch.float32, device=dev)
+
+    def timeit(fn, cold):
+        ts = []
+        for _ in range(reps):
+            if cold:
+                flush.fill_(1.0)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        return float(np.median(ts))
+
+    res = []
+    R, W, C, H, G, P = cfg.rows, cfg.W, cfg.C, cfg.H, cfg.G, cfg.P
+    for B in (1, 4, 16):
+        full = torch.zeros(B, H, W, C, dtype=torch.bfloat16, device=dev)
+        x = torch.randn(B, R, W, C, device=dev).to(torch.bfloat16)
+        y = torch.empty_like(x)
+        st = torch.ones(B, P, G, 2, device=dev)
+        so = torch.zeros(B, P, G, 2, device=dev)
+        gamma = torch.ones(C, device=dev)
+        beta = torch.zeros(C, device=dev)
+        ws = torch.empty(dpp.dpp_groupnorm_stale_workspace_bytes(B, R, W, C, G), dtype=torch.uint8, device=dev)
+        nbytes = 2.0 * B * R * W * C * 2
+        for name, fn in (("splice", lambda: dpp.dpp_splice_patch(full, x, 3 * R)),
+                         ("groupnorm", lambda: dpp.dpp_groupnorm_stale(y, so, x, st, gamma, beta, H, G, P, 3, 1e-5, ws))):
+            for cold in (False, True):
+                ms = timeit(fn, cold)
+                res.append({"kernel": name, "batch": B, "bytes": nbytes, "cache": "cold" if cold else "warm",
+                            "us": round(ms * 1e3, 2), "GB/s": round(nbytes / (ms * 1e-3) / 1e9, 1),
+                            "frac_hbm": round(nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)})
+        del full, x, y
+    for lg in (16, 20, 23, 26):
+        n = 2 ** lg
+        c = torch.randn(n, device=dev).to(torch.bfloat16)
+        u = torch.randn(n, device=dev).to(torch.bfloat16)
+        e = torch.empty_like(c)
+        rel = torch.zeros(1, device=dev)
+        ws = torch.empty(dpp.dpp_cfg_combine_workspace_bytes(n), dtype=torch.uint8, device=dev)
+        nbytes = 3.0 * n * 2
+        for cold in (False, True):
+            ms = timeit(lambda: dpp.dpp_cfg_combine_relmae(e, rel, c, u, 7.5, ws), cold)
+            res.append({"kernel": "cfg", "n": n, "bytes": nbytes, "cache": "cold" if cold else "warm",
+                        "us": round(ms * 1e3, 2), "GB/s": round(nbytes / (ms * 1e-3) / 1e9, 1),
+                        "frac_hbm": round(nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)})
     return res
 
 

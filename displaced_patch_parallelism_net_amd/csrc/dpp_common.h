@@ -11,6 +11,7 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWave = 64;
 
@@ -74,6 +75,18 @@ template <> struct Elem<uint16_t> {
   __device__ static void unpack(const uint4& u, float* f) { unpack8(u, f); }
   __device__ static uint4 pack(const float* f) { return pack8(f); }
 };
+
+// Streaming (non-temporal) 16-byte access for data touched once: it does not
+// displace reusable lines from the caches, and measured faster for large
+// cold copies on gfx950.
+__device__ __forceinline__ uint4 ld_stream(const uint4* p) {
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ void st_stream(uint4* p, const uint4& u) {
+  const u32x4 v = {u.x, u.y, u.z, u.w};
+  __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
+}
 
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll

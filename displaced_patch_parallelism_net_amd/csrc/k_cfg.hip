@@ -2,7 +2,7 @@
 //
 // eps = eps_u + w (eps_c - eps_u) elementwise, and rel-MAE = sum|eps_c -
 // eps_u| / sum|eps_u| (Hybridiff technical summary, sections 2A and 2B).
-// HBM-bound: one read of each branch, one write.  The reduction is
+// HBM-bound: one streaming read of each branch, one streaming write.  The reduction is
 // deterministic: a grid whose size depends only on n writes one float64 pair
 // per workgroup, and a single workgroup sums those pairs in a fixed order.
 #include "dpp_common.h"
@@ -11,7 +11,7 @@ namespace dpp {
 
 constexpr int kCfgThreads = 256;
 constexpr int kCfgMaxBlocks = 1024;
-constexpr int kCfgVecPerThread = 4;  // target vectors per thread per pass
+constexpr int kCfgVecPerThread = 1;  // target vectors per thread per pass
 
 static int cfg_blocks(int64_t n) {
   // 8 elements per 16-byte bf16 vector; the same grid serves fp32.
@@ -53,8 +53,8 @@ __global__ __launch_bounds__(kCfgThreads) void cfg_kernel(T* eps, const T* eps_c
     uint4* e4 = reinterpret_cast<uint4*>(eps);
     for (int64_t i = tid; i < nvec; i += stride) {
       float c[V], u[V], e[V];
-      Elem<T>::unpack(c4[i], c);
-      Elem<T>::unpack(u4[i], u);
+      Elem<T>::unpack(ld_stream(c4 + i), c);
+      Elem<T>::unpack(ld_stream(u4 + i), u);
 #pragma unroll
       for (int j = 0; j < V; ++j) {
         const float d = c[j] - u[j];
@@ -62,7 +62,7 @@ __global__ __launch_bounds__(kCfgThreads) void cfg_kernel(T* eps, const T* eps_c
         sd += fabsf(d);
         su += fabsf(u[j]);
       }
-      e4[i] = Elem<T>::pack(e);
+      st_stream(e4 + i, Elem<T>::pack(e));
     }
     // elements past the last whole vector: first threads of block 0
     if (blockIdx.x == 0 && tail0 + threadIdx.x < n) {

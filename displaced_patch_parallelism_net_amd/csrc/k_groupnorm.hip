@@ -14,13 +14,14 @@
 //      order), adds the other patches' stale sums, writes the fresh sums to
 //      stats_out[b,p] and mean/rstd to the workspace;
 //   3. apply: y = x * a_c + b_c with a_c = rstd_g gamma_c, b_c = beta_c -
-//      mean_g a_c; one 16-byte load and store per vector.
+//      mean_g a_c; one 16-byte load and one streaming store per vector.
 // The second read of x (step 3) normally hits the 256 MB last-level cache.
 #include "dpp_common.h"
 
 namespace dpp {
 
 constexpr int kGnMaxThreads = 256;
+constexpr int kGnFinThreads = 1024;  // finalize: threads per batch entry
 constexpr int kGnStatChunks = 256;    // total partial workgroups (over B)
 constexpr int kGnApplyChunks = 1024;  // total apply workgroups (over B)
 
@@ -86,21 +87,20 @@ __global__ __launch_bounds__(kGnMaxThreads) void gn_partial_kernel(const T* __re
   for (int j = 0; j < VEC; ++j) { s1[j] = 0.f; s2[j] = 0.f; }
   if (k < KP) {
     int64_t pix = p0 + k;
-    // two vectors in flight per iteration
-    for (; pix + KP < p1; pix += 2 * KP) {
-      const uint4 a = xv[pix * V + v];
-      const uint4 c = xv[(pix + KP) * V + v];
-      float fa[VEC], fc[VEC];
-      Elem<T>::unpack(a, fa);
-      Elem<T>::unpack(c, fc);
+    // four vectors in flight per iteration
+    for (; pix + 3 * KP < p1; pix += 4 * KP) {
+      uint4 u[4];
 #pragma unroll
-      for (int j = 0; j < VEC; ++j) {
-        s1[j] += fa[j] + fc[j];
-        s2[j] = fmaf(fa[j], fa[j], s2[j]);
-        s2[j] = fmaf(fc[j], fc[j], s2[j]);
+      for (int q = 0; q < 4; ++q) u[q] = xv[(pix + q * KP) * V + v];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        float f[VEC];
+        Elem<T>::unpack(u[q], f);
+#pragma unroll
+        for (int j = 0; j < VEC; ++j) { s1[j] += f[j]; s2[j] = fmaf(f[j], f[j], s2[j]); }
       }
     }
-    if (pix < p1) {
+    for (; pix < p1; pix += KP) {
       float fa[VEC];
       Elem<T>::unpack(xv[pix * V + v], fa);
 #pragma unroll
@@ -127,13 +127,13 @@ __global__ __launch_bounds__(kGnMaxThreads) void gn_partial_kernel(const T* __re
   }
 }
 
-__global__ __launch_bounds__(kGnMaxThreads) void gn_finalize_kernel(
+__global__ __launch_bounds__(kGnFinThreads) void gn_finalize_kernel(
     const float* __restrict__ partial, int64_t nchunk, const float* __restrict__ stale, float* __restrict__ stats_out,
     float* __restrict__ coef, int G, int P, int p, double n, float eps) {
-  __shared__ double r1[kGnMaxThreads], r2[kGnMaxThreads];
+  __shared__ double r1[kGnFinThreads], r2[kGnFinThreads];
   const int b = blockIdx.x;
   const int t = threadIdx.x;
-  const int nparts = kGnMaxThreads / G;  // G <= 256 (host check)
+  const int nparts = kGnFinThreads / G;  // G <= 256 (host check)
   const int g = t % G, part = t / G;
   double a = 0.0, c = 0.0;
   if (part < nparts) {
@@ -198,23 +198,25 @@ __global__ __launch_bounds__(kGnMaxThreads) void gn_apply_kernel(const T* __rest
   const uint4* xv = reinterpret_cast<const uint4*>(x) + off;
   uint4* yv = reinterpret_cast<uint4*>(y) + off;
   int64_t pix = p0 + k;
-  for (; pix + KP < p1; pix += 2 * KP) {
-    const uint4 u0 = xv[pix * V + v];
-    const uint4 u1 = xv[(pix + KP) * V + v];
-    float f0[VEC], f1[VEC];
-    Elem<T>::unpack(u0, f0);
-    Elem<T>::unpack(u1, f1);
+  for (; pix + 3 * KP < p1; pix += 4 * KP) {
+    uint4 u[4];
 #pragma unroll
-    for (int j = 0; j < VEC; ++j) { f0[j] = fmaf(f0[j], a[j], sh[j]); f1[j] = fmaf(f1[j], a[j], sh[j]); }
-    yv[pix * V + v] = Elem<T>::pack(f0);
-    yv[(pix + KP) * V + v] = Elem<T>::pack(f1);
+    for (int q = 0; q < 4; ++q) u[q] = xv[(pix + q * KP) * V + v];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      float f[VEC];
+      Elem<T>::unpack(u[q], f);
+#pragma unroll
+      for (int j = 0; j < VEC; ++j) f[j] = fmaf(f[j], a[j], sh[j]);
+      st_stream(yv + (pix + q * KP) * V + v, Elem<T>::pack(f));
+    }
   }
-  if (pix < p1) {
+  for (; pix < p1; pix += KP) {
     float f0[VEC];
     Elem<T>::unpack(xv[pix * V + v], f0);
 #pragma unroll
     for (int j = 0; j < VEC; ++j) f0[j] = fmaf(f0[j], a[j], sh[j]);
-    yv[pix * V + v] = Elem<T>::pack(f0);
+    st_stream(yv + pix * V + v, Elem<T>::pack(f0));
   }
 }
 
@@ -231,7 +233,7 @@ static hipError_t gn_run(T* y, float* stats_out, const T* x, const float* stale,
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   const double n = static_cast<double>(H) * static_cast<double>(W) * static_cast<double>(C / G);
-  hipLaunchKernelGGL(gn_finalize_kernel, dim3(static_cast<unsigned>(B)), dim3(kGnMaxThreads), 0, s, partial, g.nstat,
+  hipLaunchKernelGGL(gn_finalize_kernel, dim3(static_cast<unsigned>(B)), dim3(kGnFinThreads), 0, s, partial, g.nstat,
                      stale, stats_out, y ? coef : nullptr, static_cast<int>(G), static_cast<int>(P),
                      static_cast<int>(p), n, eps);
   err = hipGetLastError();

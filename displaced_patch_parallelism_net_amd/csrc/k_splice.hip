@@ -4,8 +4,8 @@
 // concatenating along the height axis into the reused full-image buffer
 // (DistriFusion architecture article, communication section).  In NHWC the
 // row band of one batch entry is a single contiguous slab, so the splice is B
-// slab copies: HBM-bound, 16-byte vector loads/stores, several vectors in
-// flight per thread.
+// slab copies: HBM-bound, 16-byte streaming (non-temporal) loads/stores,
+// four vectors in flight per thread.
 #include "dpp_common.h"
 
 namespace dpp {
@@ -24,12 +24,12 @@ __global__ __launch_bounds__(kSpliceThreads) void splice_vec_kernel(
 #pragma unroll
   for (int u = 0; u < kSpliceUnroll; ++u) {
     const int64_t i = base + u * kSpliceThreads;
-    if (i < slab) r[u] = src[i];
+    if (i < slab) r[u] = ld_stream(src + i);
   }
 #pragma unroll
   for (int u = 0; u < kSpliceUnroll; ++u) {
     const int64_t i = base + u * kSpliceThreads;
-    if (i < slab) dst[i] = r[u];
+    if (i < slab) st_stream(dst + i, r[u]);
   }
 }
 
