@@ -212,18 +212,24 @@ __global__ __launch_bounds__(kAttThreads, 2) void attn_bf16_kernel(AttnArgs a) {
       for (int r = 0; r < 16; ++r) O[i][j][r] = 0.f;
   float m_run[2] = {-INFINITY, -INFINITY};
   float l_run[2] = {0.f, 0.f};
-  const bf16x2 ones = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
 
-  // one eighth of a unit's exponentials: query block qb2, keys 16*t16 .. +15 of the half
+  // One eighth of a unit's exponentials: query block qb2, keys 16*t16 .. +15
+  // of the half.  The row sum adds the float32 weights (before their bf16
+  // rounding) in a short tree: on gfx950 plain adds issue beside a running
+  // MFMA far better than the packed bf16 dot product, and the normaliser
+  // then differs from the sum of the rounded weights only by their
+  // independent rounding errors.
   auto exp_chunk = [&](const f32x16 (&S)[2], int qb2, int t16, const float (&m)[2], bf16x8 (&P)[2][2], float (&ls)[2]) {
     uint32_t w[4];
+    float s2[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const float p0 = __builtin_amdgcn_exp2f(fmaf(S[qb2][t16 * 8 + 2 * e], a.c, -m[qb2]));
       const float p1 = __builtin_amdgcn_exp2f(fmaf(S[qb2][t16 * 8 + 2 * e + 1], a.c, -m[qb2]));
       w[e] = pack_bf16x2(p0, p1);
-      ls[qb2] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w[e]), ones, ls[qb2], false);
+      s2[e] = p0 + p1;
     }
+    ls[qb2] += (s2[0] + s2[1]) + (s2[2] + s2[3]);
     P[qb2][t16] = __builtin_bit_cast(bf16x8, make_uint4(w[0], w[1], w[2], w[3]));
   };
   // scores of a unit in the ragged last tile: keys past the range -> -inf
