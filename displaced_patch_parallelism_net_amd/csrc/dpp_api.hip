@@ -129,6 +129,8 @@ int dpp_self_attn_displaced(void* o, const void* q, const void* k, const void* v
   const int64_t hd = heads * head_dim;
   if (ld_q < hd || ld_kv < hd || ld_o < hd) return DPP_ERR_SHAPE;
   if (B * heads > 65535 || n_q > (1LL << 30) || n_kv > (1LL << 30)) return DPP_ERR_UNSUPPORTED;
+  // bf16 grid: 256-query tiles x B*heads x up to 16 key splits, one int32 id each
+  if (((n_q + 255) / 256) * B * heads * 16 > 0x7fffffffLL) return DPP_ERR_UNSUPPORTED;
   if (dtype == DPP_BF16) {
     if (head_dim != 64) return DPP_ERR_UNSUPPORTED;
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || ld_q % 8 || ld_kv % 8 || ld_o % 8)

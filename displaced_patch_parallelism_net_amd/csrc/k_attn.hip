@@ -89,6 +89,7 @@ struct AttnArgs {
   int64_t ld_q, ld_kv, ld_o;
   float c;          // scale * log2(e)
   int keys_per_split;
+  int n_qt, n_bh;   // query tiles, batch*heads
 };
 
 // Position of key (0..15) inside its 16-key group in the MFMA k order.
@@ -133,12 +134,20 @@ __global__ __launch_bounds__(kAttThreads, 2) void attn_bf16_kernel(AttnArgs a) {
   const int tid = threadIdx.x;
   const int wave = tid / kWave, lane = tid % kWave;
   const int g = lane >> 5, l32 = lane & 31;
-  const int bh = blockIdx.y;
+  // XCD-aware order: the hardware deals workgroup ids round-robin to the 8
+  // XCDs; give each XCD a contiguous range of logical ids, query tile
+  // fastest, so workgroups sharing a (head, key range) share one L2.
+  const int total = gridDim.x, lid = blockIdx.x;
+  const int per = total / 8, rem = total % 8, xcd = lid % 8;
+  const int logical = xcd * per + min(xcd, rem) + lid / 8;
+  const int qtile = logical % a.n_qt;
+  const int bh = (logical / a.n_qt) % a.n_bh;
+  const int split = logical / (a.n_qt * a.n_bh);
   const int b = bh / a.heads, h = bh % a.heads;
-  const int split = blockIdx.z;
   const int k_begin = split * a.keys_per_split;
   const int k_end = min(a.n_kv, k_begin + a.keys_per_split);
-  const int q0 = blockIdx.x * kAttQT + wave * kAttQW;
+  const int q0 = qtile * kAttQT + wave * kAttQW;
+  const bool active = q0 < a.n_q;  // waves wholly past the queries only stage tiles
 
   const uint16_t* qb = a.q + static_cast<int64_t>(b) * a.n_q * a.ld_q + h * kAttD;
   const uint16_t* kb = a.k + static_cast<int64_t>(b) * a.n_kv * a.ld_kv + h * kAttD;
@@ -355,12 +364,14 @@ __global__ __launch_bounds__(kAttThreads, 2) void attn_bf16_kernel(AttnArgs a) {
     }
     const int bt = t & 3, bprev = (t + 3) & 3, bnext = (t + 1) & 3;
     // unit (t, 0): softmax S0 -> P0; S1 = K(t, half 1) Q^T; O += V(t-1, half 1) P1
-    mask_unit(S0, t0, 0);
-    unit(S0, P0, S1, bt, 1, P1, bprev, 1);
-    // unit (t, 1): softmax S1 -> P1; S0 = K(t+1, half 0) Q^T (unused after the
-    // last tile); O += V(t, half 0) P0
-    mask_unit(S1, t0, 1);
-    unit(S1, P1, S0, bnext, 0, P0, bt, 0);
+    if (active) {
+      mask_unit(S0, t0, 0);
+      unit(S0, P0, S1, bt, 1, P1, bprev, 1);
+      // unit (t, 1): softmax S1 -> P1; S0 = K(t+1, half 0) Q^T (unused after
+      // the last tile); O += V(t, half 0) P0
+      mask_unit(S1, t0, 1);
+      unit(S1, P1, S0, bnext, 0, P0, bt, 0);
+    }
     __syncthreads();
   }
   // drain: O += V(last, half 1) P1
@@ -396,7 +407,7 @@ __global__ __launch_bounds__(kAttThreads, 2) void attn_bf16_kernel(AttnArgs a) {
           *reinterpret_cast<uint2*>(op + d) = u;
         }
     } else {
-      const int64_t row = (static_cast<int64_t>(split) * gridDim.y + bh) * a.n_q + qi;
+      const int64_t row = (static_cast<int64_t>(split) * a.n_bh + bh) * a.n_q + qi;
       float* op = a.o_part + row * kAttD;
 #pragma unroll
       for (int db = 0; db < 2; ++db)
@@ -448,8 +459,9 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(const float* __restrict
 // Key-range split policy: depends on the shape only (so the workspace query
 // needs no device).  An MI355X holds 256 CUs x 2 resident workgroups of this
 // kernel; pick the smallest split count whose workgroup count fills the
-// resident slots in whole rounds to >= 90 % (else the best one), keeping
-// >= 8 key tiles per split.
+// resident slots in whole rounds to >= 97 % (else the best one), keeping
+// >= 8 key tiles per split.  (At 7200 queries x 57600 keys x 10 heads: 7
+// splits, 2030 workgroups, 99 % of four rounds.)
 constexpr int64_t kAttSlots = 256 * 2;
 struct AttnSplit {
   int nsplit;
@@ -467,7 +479,7 @@ static AttnSplit attn_split(int64_t B, int64_t n_q, int64_t n_kv, int64_t heads)
     const int64_t total = qtiles * ns_eff;
     const double eff = static_cast<double>(total) / static_cast<double>(ceil_div(total, kAttSlots) * kAttSlots);
     if (eff > best_eff + 1e-9) { best_eff = eff; best = ns; }
-    if (eff >= 0.9) break;
+    if (eff >= 0.97) break;
   }
   const int64_t kps = ceil_div(ktiles, best) * kAttKT;
   const int64_t ns = ceil_div(n_kv, kps);
@@ -527,8 +539,9 @@ hipError_t launch_attention(void* o, const void* q, const void* k, const void* v
     a.o_part = nullptr;
     a.ml_part = nullptr;
   }
-  dim3 grid(static_cast<unsigned>(ceil_div(n_q, kAttQT)), static_cast<unsigned>(B * heads),
-            static_cast<unsigned>(sp.nsplit));
+  a.n_qt = static_cast<int>(ceil_div(n_q, kAttQT));
+  a.n_bh = static_cast<int>(B * heads);
+  dim3 grid(static_cast<unsigned>(static_cast<int64_t>(a.n_qt) * a.n_bh * sp.nsplit));
   hipLaunchKernelGGL(attn_bf16_kernel, grid, dim3(kAttThreads), 0, s, a);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || sp.nsplit <= 1) return err;

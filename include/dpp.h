@@ -157,6 +157,8 @@ int dpp_conv3x3_halo(void* y, const void* x, const void* stale_full,
  *   scale <= 0 selects 1/sqrt(head_dim).  o must not overlap q, k or v.
  *   bf16 requires head_dim == 64, 16-byte aligned pointers and ld % 8 == 0.
  *   f32 requires head_dim in {16, 32, 64, 128}.
+ *   Limits (else DPP_ERR_UNSUPPORTED): B*heads <= 65535, n_q and n_kv <=
+ *   2^30, ceil(n_q/256)*B*heads*16 < 2^31.
  *   workspace: optional.  With workspace_bytes >=
  *   dpp_self_attn_workspace_bytes(...) the key range may be split across
  *   workgroups and merged in a second pass (more parallelism for short query
