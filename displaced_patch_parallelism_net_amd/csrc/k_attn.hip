@@ -289,6 +289,10 @@ __global__ __launch_bounds__(kAttThreads, 2) void attn_bf16_kernel(AttnArgs a) {
     O[0][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf11, Pprev[0][1], O[0][1], 0, 0, 0);
     O[1][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf11, Pprev[1][1], O[1][1], 0, 0, 0);
     exp_chunk(Scur, 1, 1, m, Pcur, ls);
+    // Materialise the packed weights before the guard branch: the exact path
+    // overwrites them, so the compiler would otherwise sink their conversion
+    // past the branch, where no MFMA is left to overlap it.
+    asm volatile("" ::"v"(Pcur[0][0]), "v"(Pcur[0][1]), "v"(Pcur[1][0]), "v"(Pcur[1][1]));
     // overflow guard; the exact path runs after this unit's MFMAs were issued,
     // so the O rescale applies to everything accumulated so far
     if (__builtin_amdgcn_ballot_w64(!(ls[0] <= kSumCap) || !(ls[1] <= kSumCap)) != 0) {
