@@ -19,8 +19,10 @@ on a bounded sample of the same workload.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -32,6 +34,13 @@ if ROOT not in sys.path:
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+
+# Counter-based HBM traffic of one attention call, recorded from rocprofv3
+# FETCH_SIZE / WRITE_SIZE passes scaled by a plain-copy calibration.  It is
+# reported only while the attention sources still hash to the recorded value.
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_sdxl_3840_traffic.md")
+ATTN_SOURCES = ("displaced_patch_parallelism_net_amd/csrc/k_attn.hip",
+                "displaced_patch_parallelism_net_amd/csrc/dpp_common.h")
 
 
 def parse():
@@ -45,7 +54,53 @@ def parse():
     ap.add_argument("--kernels", action="store_true", help="also time every kernel family separately")
     ap.add_argument("--hbm-sweep", action="store_true",
                     help="also time splice / GroupNorm / CFG over a size sweep, warm and cold last-level cache")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="only run a plain 512 MiB device copy (the splice kernel) 3 times: the known-size "
+                         "reference for scaling FETCH_SIZE / WRITE_SIZE counters")
     return ap.parse_args()
+
+
+def attn_source_hash():
+    h = hashlib.sha256()
+    for f in ATTN_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload):
+    """HBM bytes per attention call from the recorded counter summary, or
+    None when there is none for this workload or the kernel changed since."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            text = fh.read()
+    except OSError:
+        return None
+    m = re.search(r"```json\n(.*?)\n```", text, re.S)
+    if not m:
+        return None
+    rec = json.loads(m.group(1))
+    if rec.get("workload") != workload or rec.get("kernel_source_sha256") != attn_source_hash():
+        return None
+    return rec.get("traffic_bytes_per_call")
+
+
+def calib_copy(mib=512, reps=3):
+    """A plain copy of known size: one contiguous bf16 slab of `mib` MiB
+    spliced into a buffer twice its size, `reps` times."""
+    import torch
+    import displaced_patch_parallelism_net_amd as dpp
+    W, C = 1024, 1024
+    R = mib * 2 ** 20 // (W * C * 2)
+    full = torch.zeros(1, 2 * R, W, C, dtype=torch.bfloat16, device="cuda")
+    patch = torch.ones(1, R, W, C, dtype=torch.bfloat16, device="cuda")
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        dpp.dpp_splice_patch(full, patch, R)
+    torch.cuda.synchronize()
+    nbytes = patch.numel() * 2
+    print(json.dumps({"calib_copy": "splice_vec_kernel", "bytes_read_per_call": nbytes,
+                      "bytes_written_per_call": nbytes, "calls": reps}), flush=True)
 
 
 def flops(cfg):
@@ -120,6 +175,9 @@ def main():
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1 "
                                    "(the multi-GPU exchange is designed, not built)"}))
         sys.exit(2)
+    if args.calib_copy:
+        calib_copy()
+        return
     import torch
     import displaced_patch_parallelism_net_amd as dpp
     from displaced_patch_parallelism_net_amd.step import DisplacedLayer
@@ -224,7 +282,8 @@ def main():
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
-            "traffic": None,
+            "traffic": measured_traffic(cfg.name),
+            "traffic_unit": "bytes per call (attention + split merge), FETCH_SIZE + WRITE_SIZE scaled by a plain copy",
             "avg_launch_ms": round(attn_ms, 5),
             "flops_per_launch": f_attn,
         },
