@@ -429,7 +429,10 @@ __global__ __launch_bounds__(kAttThreads, 2) void attn_bf16_kernel(AttnArgs a) {
   }
 }
 
-// Merge of key-range splits: thread per (b*heads, query, 4 channels).
+// Merge of key-range splits: thread per (b*heads, query, 4 channels).  All
+// of a thread's partial loads are issued before any is used (the split count
+// is at most MAXS), so a thread waits for one memory round trip, not nsplit.
+template <int MAXS>
 __global__ __launch_bounds__(256) void attn_merge_kernel(const float* __restrict__ o_part,
                                                          const float* __restrict__ ml_part, uint16_t* __restrict__ o,
                                                          int nsplit, int n_q, int heads, int64_t ld_o, int64_t rows) {
@@ -437,18 +440,32 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(const float* __restrict
   if (idx >= rows * 16) return;
   const int64_t row = idx / 16;  // bh * n_q + qi
   const int dq = static_cast<int>(idx % 16);
+  float2 ml[MAXS];
+  f32x4 ov[MAXS];
+#pragma unroll
+  for (int s = 0; s < MAXS; ++s) {
+    if (s < nsplit) {
+      const int64_t r = s * rows + row;
+      ml[s] = *reinterpret_cast<const float2*>(ml_part + r * 2);
+      ov[s] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(o_part + r * kAttD + dq * 4));
+    }
+  }
   float M = -INFINITY;
-  for (int s = 0; s < nsplit; ++s) M = fmaxf(M, ml_part[(s * rows + row) * 2]);
+#pragma unroll
+  for (int s = 0; s < MAXS; ++s)
+    if (s < nsplit) M = fmaxf(M, ml[s].x);
   float L = 0.f;
   float acc[4] = {0.f, 0.f, 0.f, 0.f};
-  for (int s = 0; s < nsplit; ++s) {
-    const float w = __builtin_amdgcn_exp2f(ml_part[(s * rows + row) * 2] - M);
-    L = fmaf(w, ml_part[(s * rows + row) * 2 + 1], L);
-    const float4 ov = *reinterpret_cast<const float4*>(o_part + (s * rows + row) * kAttD + dq * 4);
-    acc[0] = fmaf(w, ov.x, acc[0]);
-    acc[1] = fmaf(w, ov.y, acc[1]);
-    acc[2] = fmaf(w, ov.z, acc[2]);
-    acc[3] = fmaf(w, ov.w, acc[3]);
+#pragma unroll
+  for (int s = 0; s < MAXS; ++s) {
+    if (s < nsplit) {
+      const float w = __builtin_amdgcn_exp2f(ml[s].x - M);
+      L = fmaf(w, ml[s].y, L);
+      acc[0] = fmaf(w, ov[s].x, acc[0]);
+      acc[1] = fmaf(w, ov[s].y, acc[1]);
+      acc[2] = fmaf(w, ov[s].z, acc[2]);
+      acc[3] = fmaf(w, ov[s].w, acc[3]);
+    }
   }
   const float inv = 1.f / L;
   const int64_t bh = row / n_q, qi = row % n_q;
@@ -549,8 +566,13 @@ hipError_t launch_attention(void* o, const void* q, const void* k, const void* v
   hipLaunchKernelGGL(attn_bf16_kernel, grid, dim3(kAttThreads), 0, s, a);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || sp.nsplit <= 1) return err;
-  hipLaunchKernelGGL(attn_merge_kernel, dim3(static_cast<unsigned>(ceil_div(rows * 16, 256))), dim3(256), 0, s,
-                     a.o_part, a.ml_part, a.o, sp.nsplit, a.n_q, a.heads, ld_o, rows);
+  const dim3 mgrid(static_cast<unsigned>(ceil_div(rows * 16, 256)));
+  if (sp.nsplit <= 8)
+    hipLaunchKernelGGL(attn_merge_kernel<8>, mgrid, dim3(256), 0, s, a.o_part, a.ml_part, a.o, sp.nsplit, a.n_q,
+                       a.heads, ld_o, rows);
+  else
+    hipLaunchKernelGGL(attn_merge_kernel<16>, mgrid, dim3(256), 0, s, a.o_part, a.ml_part, a.o, sp.nsplit, a.n_q,
+                       a.heads, ld_o, rows);
   return hipGetLastError();
 }
 
