@@ -8,7 +8,7 @@
 // Three launches, all deterministic (no atomics):
 //   1. partial: workgroup (chunk, b) sums its pixels per channel in float32
 //      registers (each thread owns one 16-byte channel vector and walks
-//      pixels), folds channels into groups through LDS in a fixed order and
+//      pixels, eight loads in flight), folds channels into groups through LDS in a fixed order and
 //      writes one (s1, s2) per group to the workspace;
 //   2. finalize: one workgroup per b adds the chunk partials in float64 (fixed
 //      order), adds the other patches' stale sums, writes the fresh sums to
@@ -24,6 +24,7 @@ constexpr int kGnMaxThreads = 256;
 constexpr int kGnFinThreads = 1024;  // finalize: threads per batch entry
 constexpr int kGnStatChunks = 256;    // total partial workgroups (over B)
 constexpr int kGnApplyChunks = 1024;  // total apply workgroups (over B)
+constexpr int kGnInFlight = 8;        // 16-byte loads in flight per thread
 
 struct GnGeom {
   int vec;      // elements per 16-byte vector
@@ -87,13 +88,13 @@ __global__ __launch_bounds__(kGnMaxThreads) void gn_partial_kernel(const T* __re
   for (int j = 0; j < VEC; ++j) { s1[j] = 0.f; s2[j] = 0.f; }
   if (k < KP) {
     int64_t pix = p0 + k;
-    // four vectors in flight per iteration
-    for (; pix + 3 * KP < p1; pix += 4 * KP) {
-      uint4 u[4];
+    // kGnInFlight vectors in flight per iteration
+    for (; pix + (kGnInFlight - 1) * KP < p1; pix += kGnInFlight * KP) {
+      uint4 u[kGnInFlight];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) u[q] = xv[(pix + q * KP) * V + v];
+      for (int q = 0; q < kGnInFlight; ++q) u[q] = xv[(pix + q * KP) * V + v];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
+      for (int q = 0; q < kGnInFlight; ++q) {
         float f[VEC];
         Elem<T>::unpack(u[q], f);
 #pragma unroll
@@ -127,20 +128,41 @@ __global__ __launch_bounds__(kGnMaxThreads) void gn_partial_kernel(const T* __re
   }
 }
 
+// Finalize: thread t of batch entry b owns group t % G and every
+// (1024/G)-th chunk from t / G; its chunk loads are all issued before they
+// are summed (up to kGnFinLoads each, else a loop), and the other patches'
+// stale sums are loaded into LDS by the same threads meanwhile.
+constexpr int kGnFinLoads = 8;
+constexpr int kGnFinStale = 2048;  // stale (q, g) pairs staged in LDS: P * G <= this
+
 __global__ __launch_bounds__(kGnFinThreads) void gn_finalize_kernel(
     const float* __restrict__ partial, int64_t nchunk, const float* __restrict__ stale, float* __restrict__ stats_out,
     float* __restrict__ coef, int G, int P, int p, double n, float eps) {
   __shared__ double r1[kGnFinThreads], r2[kGnFinThreads];
+  __shared__ float2 sst[kGnFinStale];
   const int b = blockIdx.x;
   const int t = threadIdx.x;
   const int nparts = kGnFinThreads / G;  // G <= 256 (host check)
   const int g = t % G, part = t / G;
+  const bool stage_stale = stale != nullptr && coef != nullptr && P * G <= kGnFinStale;
+  if (stage_stale)
+    for (int i = t; i < P * G; i += kGnFinThreads)
+      sst[i] = *reinterpret_cast<const float2*>(stale + (static_cast<int64_t>(b) * P * G + i) * 2);
   double a = 0.0, c = 0.0;
   if (part < nparts) {
-    for (int64_t ch = part; ch < nchunk; ch += nparts) {
-      const float* pr = partial + ((static_cast<int64_t>(b) * nchunk + ch) * G + g) * 2;
-      a += pr[0];
-      c += pr[1];
+    const float* base = partial + (static_cast<int64_t>(b) * nchunk * G + g) * 2;
+    int64_t ch = part;
+    for (; ch + (kGnFinLoads - 1) * nparts < nchunk; ch += kGnFinLoads * nparts) {
+      float2 v[kGnFinLoads];
+#pragma unroll
+      for (int j = 0; j < kGnFinLoads; ++j) v[j] = *reinterpret_cast<const float2*>(base + (ch + j * nparts) * G * 2);
+#pragma unroll
+      for (int j = 0; j < kGnFinLoads; ++j) { a += v[j].x; c += v[j].y; }
+    }
+    for (; ch < nchunk; ch += nparts) {
+      const float2 v = *reinterpret_cast<const float2*>(base + ch * G * 2);
+      a += v.x;
+      c += v.y;
     }
   }
   r1[t] = a;
@@ -157,9 +179,10 @@ __global__ __launch_bounds__(kGnFinThreads) void gn_finalize_kernel(
       if (stale != nullptr)
         for (int q = 0; q < P; ++q)
           if (q != p) {
-            const float* st = stale + ((static_cast<int64_t>(b) * P + q) * G + t) * 2;
-            T1 += st[0];
-            T2 += st[1];
+            const float2 st = stage_stale ? sst[q * G + t]
+                                          : *reinterpret_cast<const float2*>(stale + ((static_cast<int64_t>(b) * P + q) * G + t) * 2);
+            T1 += st.x;
+            T2 += st.y;
           }
       const double mean = T1 / n;
       double var = T2 / n - mean * mean;
@@ -198,12 +221,12 @@ __global__ __launch_bounds__(kGnMaxThreads) void gn_apply_kernel(const T* __rest
   const uint4* xv = reinterpret_cast<const uint4*>(x) + off;
   uint4* yv = reinterpret_cast<uint4*>(y) + off;
   int64_t pix = p0 + k;
-  for (; pix + 3 * KP < p1; pix += 4 * KP) {
-    uint4 u[4];
+  for (; pix + (kGnInFlight - 1) * KP < p1; pix += kGnInFlight * KP) {
+    uint4 u[kGnInFlight];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) u[q] = xv[(pix + q * KP) * V + v];
+    for (int q = 0; q < kGnInFlight; ++q) u[q] = xv[(pix + q * KP) * V + v];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
+    for (int q = 0; q < kGnInFlight; ++q) {
       float f[VEC];
       Elem<T>::unpack(u[q], f);
 #pragma unroll
