@@ -327,6 +327,29 @@ def test_attention_strided_rows_and_tiny_kv():
         assert np.all(oh[..., hd:] == 0), "wrote outside heads*D columns"
 
 
+def test_attention_many_key_splits():
+    # Few queries over many keys: the key range is split 9 and 16 ways (the
+    # merge kernel's 16-split instantiation), with a ragged key tail.
+    dpp = _dpp()
+    rng = np.random.default_rng(5)
+    from dpp_synth import f32_to_bf16_bits
+    for (B, nq, nkv, heads) in [(1, 64, 8192, 1), (2, 100, 5000, 2)]:
+        say("attention many splits", B, nq, nkv, heads)
+        hd = heads * 64
+        q = f32_to_bf16_bits(rng.standard_normal((B, nq, hd)).astype(np.float32))
+        k = f32_to_bf16_bits(rng.standard_normal((B, nkv, hd)).astype(np.float32))
+        v = f32_to_bf16_bits(rng.standard_normal((B, nkv, hd)).astype(np.float32))
+        wsb = dpp.dpp_self_attn_workspace_bytes(B, nq, nkv, heads, 64, 0)
+        nsplit = wsb // (B * heads * nq * 66 * 4)
+        assert nsplit > 8, (B, nq, nkv, heads, nsplit)
+        ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+        o = torch.empty(B, nq, hd, dtype=torch.bfloat16, device="cuda")
+        dpp.dpp_self_attn_displaced(o, to_dev(q, "bf16"), to_dev(k, "bf16"), to_dev(v, "bf16"), heads, 64, 0.0, ws)
+        torch.cuda.synchronize()
+        want = oracle.self_attn_displaced(values("bf16", q), values("bf16", k), values("bf16", v), heads)
+        parity(to_host(o), want, "bf16", f"attn {nsplit} splits {B},{nq},{nkv}")
+
+
 def test_attention_closed_form_zero_query():
     # Q = 0: uniform weights, output = mean of V over all keys
     dpp = _dpp()
