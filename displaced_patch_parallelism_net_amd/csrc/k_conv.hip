@@ -77,6 +77,7 @@ constexpr int kConvThreads = 2 * kConvWN * 64;  // 2 tile rows x kConvWN
 constexpr int kConvBM = 128;  // output channels per workgroup
 constexpr int kConvKC = 64;   // input channels per slice (8 x 16-byte vectors)
 constexpr int kConvTR = 2;    // patch rows per workgroup
+constexpr int kConvTPS = 2;   // taps per barrier step
 
 struct ConvArgs {
   const uint16_t* x;
@@ -103,7 +104,7 @@ __global__ __launch_bounds__(kConvThreads, 1) void conv3x3_bf16_mfma_kernel(Conv
   constexpr int W_ITERS = kConvBM * 8 / kConvThreads;
 
   __shared__ uint4 band[2][BPIX * 8];
-  __shared__ uint4 wts[2][kConvBM * 8];
+  __shared__ uint4 wts[2][kConvTPS][kConvBM * 8];
 
   const int tid = threadIdx.x;
   const int wave = tid / kWave, lane = tid % kWave;
@@ -116,7 +117,7 @@ __global__ __launch_bounds__(kConvThreads, 1) void conv3x3_bf16_mfma_kernel(Conv
   const int64_t ktot = 9LL * Cin;
 
   uint4 band_reg[BAND_ITERS];
-  uint4 w_regA[W_ITERS], w_regB[W_ITERS];  // weights of the next two steps
+  uint4 w_regA[kConvTPS][W_ITERS], w_regB[kConvTPS][W_ITERS];  // weights of the next two steps
 
   // Per-thread source pointers, computed once: band vector u of the first
   // slice (x for patch rows, the stale image for halo rows; nullptr = zero
@@ -154,14 +155,21 @@ __global__ __launch_bounds__(kConvThreads, 1) void conv3x3_bf16_mfma_kernel(Conv
       band_reg[u] = v;
     }
   };
-  auto load_w = [&](uint4 (&w_reg)[W_ITERS], int step) {
-    const int sl = step / 9;
-    const int off = (step - sl * 9) * Cin + sl * kConvKC;
+  const int nslices = Cin / kConvKC;
+  const int nflat = nslices * 9;  // (slice, tap) pairs
+  const int nsteps = (nflat + kConvTPS - 1) / kConvTPS;
+  auto load_w = [&](uint4 (&w_reg)[kConvTPS][W_ITERS], int step) {
 #pragma unroll
-    for (int u = 0; u < W_ITERS; ++u) {
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (w_src[u] != nullptr) v = *reinterpret_cast<const uint4*>(w_src[u] + off);
-      w_reg[u] = v;
+    for (int i = 0; i < kConvTPS; ++i) {
+      const int f = step * kConvTPS + i;
+      const int sl = f / 9;
+      const int off = (f - sl * 9) * Cin + sl * kConvKC;
+#pragma unroll
+      for (int u = 0; u < W_ITERS; ++u) {
+        uint4 v = make_uint4(0, 0, 0, 0);
+        if (w_src[u] != nullptr && f < nflat) v = *reinterpret_cast<const uint4*>(w_src[u] + off);
+        w_reg[i][u] = v;
+      }
     }
   };
   auto store_band = [&](int buf) {
@@ -171,12 +179,14 @@ __global__ __launch_bounds__(kConvThreads, 1) void conv3x3_bf16_mfma_kernel(Conv
       if (id < BAND_VEC) band[buf][swz(id >> 3, id & 7)] = band_reg[u];
     }
   };
-  auto store_w = [&](const uint4 (&w_reg)[W_ITERS], int buf) {
+  auto store_w = [&](const uint4 (&w_reg)[kConvTPS][W_ITERS], int buf) {
 #pragma unroll
-    for (int u = 0; u < W_ITERS; ++u) {
-      const int id = tid + u * kConvThreads;
-      wts[buf][swz(id >> 3, id & 7)] = w_reg[u];
-    }
+    for (int i = 0; i < kConvTPS; ++i)
+#pragma unroll
+      for (int u = 0; u < W_ITERS; ++u) {
+        const int id = tid + u * kConvThreads;
+        wts[buf][i][swz(id >> 3, id & 7)] = w_reg[i][u];
+      }
   };
 
   f32x4 acc[kConvCG][TG];
@@ -191,39 +201,48 @@ __global__ __launch_bounds__(kConvThreads, 1) void conv3x3_bf16_mfma_kernel(Conv
   // slot per k step, fragment i at a fixed +16 rows.
   const int a_row0 = wn * kConvCW + pl;
   const int a_slot[2] = {(0 + kg) ^ (pl & 7), (4 + kg) ^ (pl & 7)};
-  const int nslices = Cin / kConvKC;
-  const int nsteps = nslices * 9;
-  // One step: MFMAs on the staged weights/band of `step`; then stage the
-  // weights of step+1 (held in wnext) and, at a slice end, the next band;
-  // barrier; then fetch the weights of step+3 into wnext (two steps of
-  // latency cover).  Buffers written here were last read before the
-  // previous barrier.
-  auto do_step = [&](int step, uint4 (&wnext)[W_ITERS]) {
-    const int slice = step / 9, tap = step - slice * 9;
-    const int bb = slice & 1, wb = step & 1;
-    if (tap == 0 && slice + 1 < nslices) load_band((slice + 1) * kConvKC);
-    const int dy = tap / 3, dx = tap - dy * 3;
-    // B fragment rows bp = (wr + dy) * BW + dx + 16 j + pl: all fragments of a
-    // tap share (bp & 7), so one swizzled slot per k step serves all j
-    const int bp0 = (wr + dy) * BW + dx + pl;
-    const int b_x = bp0 & 7;
+  // One step = kConvTPS consecutive (slice, tap) pairs f: MFMAs on the
+  // staged weights of the step and the band of each f's slice; then stage
+  // the weights of step+1 (held in wnext) and, once per slice (at its tap
+  // 6, at least a step before the slice's end), the next slice's band into
+  // the other band buffer, which the previous slice last used before an
+  // earlier barrier; barrier; then fetch the weights of step+3 into wnext
+  // (two steps of latency cover).
+  auto do_step = [&](int step, uint4 (&wnext)[kConvTPS][W_ITERS]) {
+    const int wb = step & 1;
+    int next_band = -1;  // slice whose band is stored at this step's end
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      bf16x8 af[kConvCG], bfr[TG];
-      const int bslot = (ks * 4 + kg) ^ b_x;
+    for (int sub = 0; sub < kConvTPS; ++sub) {
+      const int f = step * kConvTPS + sub;
+      if (f < nflat) {
+        const int slice = f / 9, tap = f - slice * 9;
+        const int bb = slice & 1;
+        if (tap == 0 && slice + 1 < nslices) load_band((slice + 1) * kConvKC);
+        if (tap == 6 && slice + 1 < nslices) next_band = slice + 1;
+        const int dy = tap / 3, dx = tap - dy * 3;
+        // B fragment rows bp = (wr + dy) * BW + dx + 16 j + pl: all fragments
+        // of a tap share (bp & 7), so one swizzled slot per k step serves all j
+        const int bp0 = (wr + dy) * BW + dx + pl;
+        const int b_x = bp0 & 7;
 #pragma unroll
-      for (int i = 0; i < kConvCG; ++i) af[i] = __builtin_bit_cast(bf16x8, wts[wb][(a_row0 + 16 * i) * 8 + a_slot[ks]]);
+        for (int ks = 0; ks < 2; ++ks) {
+          bf16x8 af[kConvCG], bfr[TG];
+          const int bslot = (ks * 4 + kg) ^ b_x;
 #pragma unroll
-      for (int j = 0; j < TG; ++j) bfr[j] = __builtin_bit_cast(bf16x8, band[bb][(bp0 + 16 * j) * 8 + bslot]);
+          for (int i = 0; i < kConvCG; ++i)
+            af[i] = __builtin_bit_cast(bf16x8, wts[wb][sub][(a_row0 + 16 * i) * 8 + a_slot[ks]]);
 #pragma unroll
-      for (int i = 0; i < kConvCG; ++i)
+          for (int j = 0; j < TG; ++j) bfr[j] = __builtin_bit_cast(bf16x8, band[bb][(bp0 + 16 * j) * 8 + bslot]);
 #pragma unroll
-        for (int j = 0; j < TG; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+          for (int i = 0; i < kConvCG; ++i)
+#pragma unroll
+            for (int j = 0; j < TG; ++j)
+              acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+        }
+      }
     }
-    if (step + 1 < nsteps) {
-      store_w(wnext, wb ^ 1);
-      if (tap == 8) store_band(bb ^ 1);
-    }
+    if (step + 1 < nsteps) store_w(wnext, wb ^ 1);
+    if (next_band >= 0) store_band(next_band & 1);
     __syncthreads();
     if (step + 3 < nsteps) load_w(wnext, step + 3);
   };
