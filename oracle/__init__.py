@@ -41,6 +41,11 @@ Readings where the pages are silent (each also listed in the design notes):
       projections; bf16 configurations round each stored layer output to bf16;
       the previous step is the synchronous full-image run of the same block on
       the stale input.
+  R11 projected attention: q/k/v/out are linear maps x W^T + b of the wrapped
+      attention module; the patch's fresh k and v replace its tokens in the
+      previous step's projected K and V (splicing rows commutes with a
+      row-wise linear map, so this equals projecting the spliced input);
+  R12 GroupNorm + SiLU: z * sigmoid(z) applied to the GroupNorm output.
 """
 from .dpp_oracle import (  # noqa: F401
     bf16_round,
@@ -51,6 +56,10 @@ from .dpp_oracle import (  # noqa: F401
     conv3x3_halo_sampled,
     self_attn_displaced,
     cfg_combine_relmae,
+    silu,
+    groupnorm_silu_stale,
+    linear,
+    projected_attention,
     previous_step_state,
     displaced_block,
 )

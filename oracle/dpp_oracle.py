@@ -91,6 +91,20 @@ def groupnorm_stale(x_patch, stale_stats, gamma, beta, H: int, G: int, p: int, e
     return y, fresh
 
 
+def silu(z) -> np.ndarray:
+    """SiLU z * sigmoid(z) = z / (1 + exp(-z)), float64 (reading R12)."""
+    z = _f64(z)
+    with np.errstate(over="ignore"):
+        return z / (1.0 + np.exp(-z))
+
+
+def groupnorm_silu_stale(x_patch, stale_stats, gamma, beta, H: int, G: int, p: int, eps: float = 1e-5):
+    """SiLU of groupnorm_stale(...): the GroupNorm + SiLU pair that opens an
+    SDXL residual block (reading R12).  Returns (silu(y), fresh sums)."""
+    y, fresh = groupnorm_stale(x_patch, stale_stats, gamma, beta, H, G, p, eps)
+    return silu(y), fresh
+
+
 # ------------------------------------------------------------------ a3: conv with halos
 def _halo_band(x_patch, stale_full, row0: int) -> np.ndarray:
     """Rows [row0-1, row0+rows] of the spliced image, zero-padded by one at
@@ -196,6 +210,56 @@ def self_attn_displaced(q, k, v, heads: int, scale: float | None = None, rows=No
     if rows is None:
         return out.reshape(B, Nq, HD)
     return out
+
+
+# ------------------------------------------------------------------ projections
+def linear(x, w, bias=None) -> np.ndarray:
+    """y[..., n] = sum_k x[..., k] w[n, k] + bias[n] (float64 matmul).
+
+    The to_q / to_k / to_v / to_out projections of the wrapped attention
+    module (DistriSelfAttentionPP, DistriFusion architecture article,
+    attention section; reading R11).  w is [N, K] (output-major, as the
+    module stores it)."""
+    y = _f64(x) @ _f64(w).T
+    if bias is not None:
+        y = y + _f64(bias)
+    return y
+
+
+def projected_attention(x_patch_tokens, k_stale, v_stale, t0: int, wq, bq, wk, bk, wv, bv, wo, bo, heads: int,
+                        bf16: bool, rows=None):
+    """Displaced self-attention with its projections (reading R11).
+
+    x_patch_tokens [B,Nq,C]: the patch's input tokens (global tokens
+    t0 .. t0+Nq-1); k_stale, v_stale [B,N,C]: the previous step's projected
+    K and V of the whole image.  q = x Wq^T + bq; the fresh k, v of the patch
+    replace tokens t0 .. t0+Nq-1 of the stale K, V (the splice of the patch's
+    rows); o = attention(q, K, V); out = o Wo^T + bo.  bf16 storage rounding
+    of q, fresh k and v, and o where the configuration is bf16.  Returns dict
+    q, k, v (spliced), o, out as stored, plus q_exact, kv_exact fresh values
+    and out_exact (each from the stored previous stage)."""
+    x = _f64(x_patch_tokens)
+    B, Nq, C = x.shape
+    q_exact = linear(x, wq, bq)
+    k_exact = linear(x, wk, bk)
+    v_exact = linear(x, wv, bv)
+    q = _store(q_exact, bf16)
+    kf = _store(k_exact, bf16)
+    vf = _store(v_exact, bf16)
+    K = _f64(k_stale).copy()
+    V = _f64(v_stale).copy()
+    K[:, t0:t0 + Nq] = kf
+    V[:, t0:t0 + Nq] = vf
+    o_exact = self_attn_displaced(q, K, V, heads)
+    o = _store(o_exact, bf16)
+    out_exact = linear(o, wo, bo)
+    out = _store(out_exact, bf16)
+    res = {"q": q, "k": K, "v": V, "o": o, "out": out, "q_exact": q_exact, "k_exact": k_exact,
+           "v_exact": v_exact, "o_exact": o_exact, "out_exact": out_exact}
+    if rows is not None:
+        b_idx, q_idx = (np.asarray(r, dtype=np.int64) for r in rows)
+        res["out_rows_exact"] = out_exact[b_idx, q_idx]
+    return res
 
 
 # ------------------------------------------------------------------ a5: CFG combine

@@ -451,3 +451,78 @@ def test_half_ulp_helper_bounds_bf16_rounding():
     assert np.max(d / half_ulp_bf16(a)) > 0.99
     assert half_ulp_bf16(np.array([1.0]))[0] == 2.0 ** -8
     assert half_ulp_bf16(np.array([6.0]))[0] == 2.0 ** -6
+
+
+# ------------------------------------------------------------------ projections and SiLU
+def test_silu_closed_forms():
+    # z sigmoid(z): 0 -> 0; 1 -> 1/(1+e^-1); odd part: silu(z) - silu(-z) = z;
+    # large z -> z, large -z -> 0
+    assert oracle.silu(np.array([0.0]))[0] == 0.0
+    assert abs(oracle.silu(np.array([1.0]))[0] - 1.0 / (1.0 + math.exp(-1.0))) < 1e-15
+    assert abs(oracle.silu(np.array([-2.0]))[0] - (-2.0 / (1.0 + math.exp(2.0)))) < 1e-15
+    z = RNG.standard_normal(1000) * 4
+    np.testing.assert_allclose(oracle.silu(z) - oracle.silu(-z), z, rtol=0, atol=1e-12)
+    assert abs(oracle.silu(np.array([60.0]))[0] - 60.0) < 1e-12
+    assert abs(oracle.silu(np.array([-60.0]))[0]) < 1e-20
+    assert oracle.silu(np.array([-1000.0]))[0] == 0.0
+
+
+def test_gn_silu_is_silu_of_torch_group_norm(torch_cpu):
+    torch = torch_cpu
+    x = RNG.standard_normal((1, 6, 5, 8))
+    gamma, beta = 1 + 0.1 * RNG.standard_normal(8), 0.1 * RNG.standard_normal(8)
+    y, _ = oracle.groupnorm_silu_stale(x, None, gamma, beta, 6, 4, 0, 1e-5)
+    t = torch.nn.functional.group_norm(torch.from_numpy(x).permute(0, 3, 1, 2), 4, torch.from_numpy(gamma),
+                                       torch.from_numpy(beta), 1e-5)
+    want = torch.nn.functional.silu(t).permute(0, 2, 3, 1).numpy()
+    np.testing.assert_allclose(y, want, rtol=1e-12, atol=1e-12)
+
+
+def test_linear_bruteforce_and_torch(torch_cpu):
+    torch = torch_cpu
+    x = RNG.standard_normal((2, 3, 5))
+    w = RNG.standard_normal((4, 5))
+    b = RNG.standard_normal(4)
+    y = oracle.linear(x, w, b)
+    for bi in range(2):
+        for m in range(3):
+            for n in range(4):
+                acc = b[n]
+                for k in range(5):
+                    acc += x[bi, m, k] * w[n, k]
+                assert abs(y[bi, m, n] - acc) < 1e-12
+    want = torch.nn.functional.linear(torch.from_numpy(x), torch.from_numpy(w), torch.from_numpy(b)).numpy()
+    np.testing.assert_allclose(y, want, rtol=1e-13, atol=1e-13)
+    np.testing.assert_allclose(oracle.linear(x, w), y - b, rtol=1e-13, atol=1e-13)
+
+
+def test_projected_attention_identity_weights_reduce_to_plain():
+    # W = I, b = 0: the projections vanish and the result is the identity-
+    # projection attention of the spliced buffer (reading R6 as a special case)
+    B, N, Nq, C, heads, t0 = 1, 48, 12, 128, 2, 24
+    x = RNG.standard_normal((B, Nq, C))
+    ks, vs = RNG.standard_normal((B, N, C)), RNG.standard_normal((B, N, C))
+    I, z = np.eye(C), np.zeros(C)
+    r = oracle.projected_attention(x, ks, vs, t0, I, z, I, z, I, z, I, z, heads, bf16=False)
+    K, V = ks.copy(), vs.copy()
+    K[:, t0:t0 + Nq] = x
+    V[:, t0:t0 + Nq] = x
+    np.testing.assert_allclose(r["out"], oracle.self_attn_displaced(x, K, V, heads), rtol=1e-12, atol=1e-12)
+
+
+def test_projected_attention_splice_commutes_with_projection():
+    # projecting the spliced input equals splicing the projections (R11): the
+    # stale K/V are the projections of the stale hidden states
+    B, N, Nq, C, heads, t0 = 2, 40, 8, 64, 1, 16
+    xs = RNG.standard_normal((B, N, C))
+    x = RNG.standard_normal((B, Nq, C))
+    wq, wk, wv, wo = (RNG.standard_normal((C, C)) / 8 for _ in range(4))
+    bq, bk, bv, bo = (RNG.standard_normal(C) / 8 for _ in range(4))
+    r = oracle.projected_attention(x, oracle.linear(xs, wk, bk), oracle.linear(xs, wv, bv), t0, wq, bq, wk, bk, wv,
+                                   bv, wo, bo, heads, bf16=False)
+    xsp = xs.copy()
+    xsp[:, t0:t0 + Nq] = x
+    K, V = oracle.linear(xsp, wk, bk), oracle.linear(xsp, wv, bv)
+    want = oracle.linear(oracle.self_attn_displaced(oracle.linear(x, wq, bq), K, V, heads), wo, bo)
+    np.testing.assert_allclose(r["out"], want, rtol=1e-11, atol=1e-11)
+    np.testing.assert_allclose(r["k"], K, rtol=1e-12, atol=1e-12)
