@@ -172,8 +172,8 @@ def cpu_baseline(cfg, budget_s):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1 "
-                                   "(the multi-GPU exchange is designed, not built)"}))
+        print(json.dumps({"error": "this benchmark measures one GPU's share of the step; --gpus must be 1 "
+                                   "(the multi-GPU exchange is not implemented)"}))
         sys.exit(2)
     if args.calib_copy:
         calib_copy()

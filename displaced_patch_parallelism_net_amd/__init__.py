@@ -13,8 +13,10 @@ from ._lib import (  # noqa: F401
     dpp_cfg_combine_relmae,
     dpp_cfg_combine_workspace_bytes,
     dpp_conv3x3_halo,
+    dpp_groupnorm_silu_stale,
     dpp_groupnorm_stale,
     dpp_groupnorm_stale_workspace_bytes,
+    dpp_linear,
     dpp_self_attn_displaced,
     dpp_self_attn_workspace_bytes,
     dpp_splice_patch,

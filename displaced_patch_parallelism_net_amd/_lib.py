@@ -31,10 +31,13 @@ SIGNATURES = {
     "dpp_groupnorm_stale_workspace_bytes": (_sz, [_i64, _i64, _i64, _i64, _i64]),
     "dpp_groupnorm_stale": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _i64, _i64, _i64, _f,
                                  _vp, _sz, _i, _vp]),
+    "dpp_groupnorm_silu_stale": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _i64, _i64, _i64,
+                                      _f, _vp, _sz, _i, _vp]),
     "dpp_conv3x3_halo": (_i, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _i64, _i64, _i, _vp]),
     "dpp_self_attn_workspace_bytes": (_sz, [_i64, _i64, _i64, _i64, _i64, _i]),
     "dpp_self_attn_displaced": (_i, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _i64, _i64, _i64, _f, _vp, _sz,
                                      _i, _vp]),
+    "dpp_linear": (_i, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _i64, _i64, _i64, _i, _vp]),
     "dpp_cfg_combine_workspace_bytes": (_sz, [_i64]),
     "dpp_cfg_combine_relmae": (_i, [_vp, _vp, _vp, _vp, _i64, _f, _vp, _sz, _i, _vp]),
 }
@@ -53,7 +56,7 @@ def _load():
     # torch's streams and allocations would be foreign to libdpp's launches.
     import torch  # noqa: F401
     if not os.path.exists(LIB_PATH):
-        raise ImportError(f"libdpp.so not built at {LIB_PATH}: run `python -m displaced_patch_parallelism_net_amd.build`")
+        raise ImportError(f"libdpp.so not built at {LIB_PATH}: run `python displaced_patch_parallelism_net_amd/build.py`")
     lib = ctypes.CDLL(LIB_PATH)
     for name, (res, args) in SIGNATURES.items():
         fn = getattr(lib, name)
@@ -120,6 +123,34 @@ def dpp_groupnorm_stale(y, stats_out, x, stale_stats, gamma, beta, H: int, G: in
                                    W, C, G, P, p, rows, eps, _ptr(workspace),
                                    0 if workspace is None else workspace.numel() * workspace.element_size(),
                                    _dtype(x), _stream(stream)))
+
+
+def dpp_groupnorm_silu_stale(y, stats_out, x, stale_stats, gamma, beta, H: int, G: int, P: int, p: int, eps: float,
+                             workspace, stream=None):
+    _contig(y, stats_out, x, stale_stats, gamma, beta)
+    B, rows, W, C = x.shape
+    _check("dpp_groupnorm_silu_stale",
+           LIB.dpp_groupnorm_silu_stale(_ptr(y), _ptr(stats_out), _ptr(x), _ptr(stale_stats), _ptr(gamma), _ptr(beta),
+                                        B, H, W, C, G, P, p, rows, eps, _ptr(workspace),
+                                        0 if workspace is None else workspace.numel() * workspace.element_size(),
+                                        _dtype(x), _stream(stream)))
+
+
+def dpp_linear(y, x, w, bias=None, stream=None):
+    """y = x w^T + bias over the last dimension.  x [M,K] or [B,M,K] and y
+    [M,N] or [B,M,N] may be strided views (last dimension contiguous), e.g. y
+    a row band of a larger K/V buffer; w [N,K] contiguous; bias [N] float32."""
+    _contig(w, bias)
+    x3 = x if x.dim() == 3 else x.unsqueeze(0)
+    y3 = y if y.dim() == 3 else y.unsqueeze(0)
+    B, M, K = x3.shape
+    N = w.shape[0]
+    if tuple(y3.shape) != (B, M, N) or tuple(w.shape) != (N, K):
+        raise ValueError(f"shape mismatch: x {tuple(x3.shape)}, w {tuple(w.shape)}, y {tuple(y3.shape)}")
+    if x3.stride(2) != 1 or y3.stride(2) != 1:
+        raise ValueError("last dimension of x and y must be contiguous")
+    _check("dpp_linear", LIB.dpp_linear(_ptr(y3), _ptr(x3), _ptr(w), _ptr(bias), B, M, K, N, x3.stride(1),
+                                        x3.stride(0), y3.stride(1), y3.stride(0), _dtype(x), _stream(stream)))
 
 
 def dpp_conv3x3_halo(y, x, stale_full, weight, bias, H: int, row0: int, stream=None):

@@ -60,9 +60,13 @@ size_t dpp_groupnorm_stale_workspace_bytes(int64_t B, int64_t rows, int64_t W, i
   return dpp::gn_workspace_bytes(B, rows, W, C, G);
 }
 
-int dpp_groupnorm_stale(void* y, float* stats_out, const void* x, const float* stale_stats, const float* gamma,
-                        const float* beta, int64_t B, int64_t H, int64_t W, int64_t C, int64_t G, int64_t P, int64_t p,
-                        int64_t rows, float eps, void* workspace, size_t workspace_bytes, int dtype, void* stream) {
+}  // extern "C"
+
+namespace {
+int groupnorm_call(void* y, float* stats_out, const void* x, const float* stale_stats, const float* gamma,
+                   const float* beta, int64_t B, int64_t H, int64_t W, int64_t C, int64_t G, int64_t P, int64_t p,
+                   int64_t rows, float eps, void* workspace, size_t workspace_bytes, int dtype, bool silu,
+                   void* stream) {
   if (bad_dtype(dtype)) return DPP_ERR_DTYPE;
   if (!x || !stats_out) return DPP_ERR_NULL;
   if (y && (!gamma || !beta)) return DPP_ERR_NULL;
@@ -86,7 +90,25 @@ int dpp_groupnorm_stale(void* y, float* stats_out, const void* x, const float* s
       (y && overlap(workspace, static_cast<int64_t>(need), y, act)))
     return DPP_ERR_ALIAS;
   return launch_status(dpp::launch_groupnorm(y, stats_out, x, stale_stats, gamma, beta, B, H, W, C, G, P, p, rows, eps,
-                                             workspace, dtype == DPP_BF16, static_cast<hipStream_t>(stream)));
+                                             workspace, dtype == DPP_BF16, silu, static_cast<hipStream_t>(stream)));
+}
+}  // namespace
+
+extern "C" {
+
+int dpp_groupnorm_stale(void* y, float* stats_out, const void* x, const float* stale_stats, const float* gamma,
+                        const float* beta, int64_t B, int64_t H, int64_t W, int64_t C, int64_t G, int64_t P, int64_t p,
+                        int64_t rows, float eps, void* workspace, size_t workspace_bytes, int dtype, void* stream) {
+  return groupnorm_call(y, stats_out, x, stale_stats, gamma, beta, B, H, W, C, G, P, p, rows, eps, workspace,
+                        workspace_bytes, dtype, false, stream);
+}
+
+int dpp_groupnorm_silu_stale(void* y, float* stats_out, const void* x, const float* stale_stats, const float* gamma,
+                             const float* beta, int64_t B, int64_t H, int64_t W, int64_t C, int64_t G, int64_t P,
+                             int64_t p, int64_t rows, float eps, void* workspace, size_t workspace_bytes, int dtype,
+                             void* stream) {
+  return groupnorm_call(y, stats_out, x, stale_stats, gamma, beta, B, H, W, C, G, P, p, rows, eps, workspace,
+                        workspace_bytes, dtype, true, stream);
 }
 
 // ------------------------------------------------------------------ a3
@@ -153,6 +175,31 @@ int dpp_self_attn_displaced(void* o, const void* q, const void* k, const void* v
   return launch_status(dpp::launch_attention(o, q, k, v, B, n_q, n_kv, heads, head_dim, ld_q, ld_kv, ld_o, scale,
                                              workspace, workspace ? workspace_bytes : 0, dtype == DPP_BF16,
                                              static_cast<hipStream_t>(stream)));
+}
+
+// ------------------------------------------------------------------ projections
+int dpp_linear(void* y, const void* x, const void* w, const float* bias, int64_t B, int64_t M, int64_t K, int64_t N,
+               int64_t ld_x, int64_t bs_x, int64_t ld_y, int64_t bs_y, int dtype, void* stream) {
+  if (bad_dtype(dtype)) return DPP_ERR_DTYPE;
+  if (!y || !x || !w) return DPP_ERR_NULL;
+  if (B <= 0 || M <= 0 || K <= 0 || N <= 0 || ld_x < K || ld_y < N || bs_x < 0 || bs_y < 0) return DPP_ERR_SHAPE;
+  // batches of the output must not overlap one another
+  if (B > 1 && bs_y < (M - 1) * ld_y + N) return DPP_ERR_SHAPE;
+  if (B > 65535 || M > (1LL << 30) || N > (1LL << 30) || K > (1LL << 30)) return DPP_ERR_UNSUPPORTED;
+  if (dtype == DPP_BF16) {
+    if (K % 8 != 0 || N % 4 != 0) return DPP_ERR_UNSUPPORTED;
+    if (!aligned16(x) || !aligned16(w) || (reinterpret_cast<uintptr_t>(y) & 7u) || ld_x % 8 || bs_x % 8 ||
+        ld_y % 4 || bs_y % 4)
+      return DPP_ERR_ALIGN;
+  }
+  const int es = esize_of(dtype);
+  const int64_t xbytes = ((B - 1) * bs_x + (M - 1) * ld_x + K) * es;
+  const int64_t ybytes = ((B - 1) * bs_y + (M - 1) * ld_y + N) * es;
+  const int64_t wbytes = N * K * es;
+  if (overlap(y, ybytes, x, xbytes) || overlap(y, ybytes, w, wbytes) || (bias && overlap(y, ybytes, bias, N * 4)))
+    return DPP_ERR_ALIAS;
+  return launch_status(dpp::launch_linear(y, x, w, bias, B, M, K, N, ld_x, bs_x, ld_y, bs_y, dtype == DPP_BF16,
+                                          static_cast<hipStream_t>(stream)));
 }
 
 // ------------------------------------------------------------------ a5

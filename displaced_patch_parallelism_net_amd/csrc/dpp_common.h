@@ -114,7 +114,7 @@ size_t gn_workspace_bytes(int64_t B, int64_t rows, int64_t W, int64_t C, int64_t
 hipError_t launch_groupnorm(void* y, float* stats_out, const void* x, const float* stale_stats,
                             const float* gamma, const float* beta, int64_t B, int64_t H, int64_t W,
                             int64_t C, int64_t G, int64_t P, int64_t p, int64_t rows, float eps,
-                            void* ws, bool bf16, hipStream_t s);
+                            void* ws, bool bf16, bool silu, hipStream_t s);
 
 hipError_t launch_conv3x3(void* y, const void* x, const void* stale_full, const void* weight,
                           const float* bias, int64_t B, int64_t H, int64_t W, int64_t Cin,
@@ -125,6 +125,10 @@ hipError_t launch_attention(void* o, const void* q, const void* k, const void* v
                             int64_t n_q, int64_t n_kv, int64_t heads, int64_t D, int64_t ld_q,
                             int64_t ld_kv, int64_t ld_o, float scale, void* ws, size_t ws_bytes,
                             bool bf16, hipStream_t s);
+
+hipError_t launch_linear(void* y, const void* x, const void* w, const float* bias, int64_t B, int64_t M,
+                         int64_t K, int64_t N, int64_t ld_x, int64_t bs_x, int64_t ld_y, int64_t bs_y, bool bf16,
+                         hipStream_t s);
 
 size_t cfg_workspace_bytes(int64_t n);
 hipError_t launch_cfg(void* eps, float* relmae, const void* eps_c, const void* eps_u, int64_t n,

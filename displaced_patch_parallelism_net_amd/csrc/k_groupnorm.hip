@@ -14,7 +14,9 @@
 //      order), adds the other patches' stale sums, writes the fresh sums to
 //      stats_out[b,p] and mean/rstd to the workspace;
 //   3. apply: y = x * a_c + b_c with a_c = rstd_g gamma_c, b_c = beta_c -
-//      mean_g a_c; one 16-byte load and one streaming store per vector.
+//      mean_g a_c (then SiLU when asked: the GroupNorm + SiLU pair opening
+//      an SDXL residual block); one 16-byte load and one streaming store per
+//      vector.
 // The second read of x (step 3) normally hits the 256 MB last-level cache.
 #include "dpp_common.h"
 
@@ -194,7 +196,13 @@ __global__ __launch_bounds__(kGnFinThreads) void gn_finalize_kernel(
   }
 }
 
-template <typename T>
+// SiLU z sigmoid(z) = z / (1 + 2^(-z log2 e)): large negative z gives
+// z * (1/inf) = -0, large positive z gives z.
+__device__ __forceinline__ float silu_f(float z) {
+  return z * __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-1.4426950408889634f * z));
+}
+
+template <typename T, bool SILU>
 __global__ __launch_bounds__(kGnMaxThreads) void gn_apply_kernel(const T* __restrict__ x, T* __restrict__ y,
                                                                  const float* __restrict__ coef,
                                                                  const float* __restrict__ gamma,
@@ -230,7 +238,10 @@ __global__ __launch_bounds__(kGnMaxThreads) void gn_apply_kernel(const T* __rest
       float f[VEC];
       Elem<T>::unpack(u[q], f);
 #pragma unroll
-      for (int j = 0; j < VEC; ++j) f[j] = fmaf(f[j], a[j], sh[j]);
+      for (int j = 0; j < VEC; ++j) {
+        f[j] = fmaf(f[j], a[j], sh[j]);
+        if (SILU) f[j] = silu_f(f[j]);
+      }
       st_stream(yv + (pix + q * KP) * V + v, Elem<T>::pack(f));
     }
   }
@@ -238,7 +249,10 @@ __global__ __launch_bounds__(kGnMaxThreads) void gn_apply_kernel(const T* __rest
     float f0[VEC];
     Elem<T>::unpack(xv[pix * V + v], f0);
 #pragma unroll
-    for (int j = 0; j < VEC; ++j) f0[j] = fmaf(f0[j], a[j], sh[j]);
+    for (int j = 0; j < VEC; ++j) {
+      f0[j] = fmaf(f0[j], a[j], sh[j]);
+      if (SILU) f0[j] = silu_f(f0[j]);
+    }
     st_stream(yv + pix * V + v, Elem<T>::pack(f0));
   }
 }
@@ -246,7 +260,7 @@ __global__ __launch_bounds__(kGnMaxThreads) void gn_apply_kernel(const T* __rest
 template <typename T>
 static hipError_t gn_run(T* y, float* stats_out, const T* x, const float* stale, const float* gamma,
                          const float* beta, int64_t B, int64_t H, int64_t W, int64_t C, int64_t G, int64_t P,
-                         int64_t p, int64_t rows, float eps, void* ws, hipStream_t s) {
+                         int64_t p, int64_t rows, float eps, void* ws, bool silu, hipStream_t s) {
   const GnGeom g = gn_geom(B, rows, W, C, sizeof(T) == 2);
   float* partial = static_cast<float*>(ws);
   float* coef = partial + B * g.nstat * G * 2;
@@ -261,20 +275,24 @@ static hipError_t gn_run(T* y, float* stats_out, const T* x, const float* stale,
                      static_cast<int>(p), n, eps);
   err = hipGetLastError();
   if (err != hipSuccess || y == nullptr) return err;
-  hipLaunchKernelGGL(gn_apply_kernel<T>, dim3(static_cast<unsigned>(g.napply), static_cast<unsigned>(B)),
-                     dim3(g.threads), 0, s, x, y, coef, gamma, beta, g.npix, static_cast<int>(C), static_cast<int>(G),
-                     g.V, g.KP, g.apply_ppc);
+  const dim3 agrid(static_cast<unsigned>(g.napply), static_cast<unsigned>(B));
+  if (silu)
+    hipLaunchKernelGGL((gn_apply_kernel<T, true>), agrid, dim3(g.threads), 0, s, x, y, coef, gamma, beta, g.npix,
+                       static_cast<int>(C), static_cast<int>(G), g.V, g.KP, g.apply_ppc);
+  else
+    hipLaunchKernelGGL((gn_apply_kernel<T, false>), agrid, dim3(g.threads), 0, s, x, y, coef, gamma, beta, g.npix,
+                       static_cast<int>(C), static_cast<int>(G), g.V, g.KP, g.apply_ppc);
   return hipGetLastError();
 }
 
 hipError_t launch_groupnorm(void* y, float* stats_out, const void* x, const float* stale_stats, const float* gamma,
                             const float* beta, int64_t B, int64_t H, int64_t W, int64_t C, int64_t G, int64_t P,
-                            int64_t p, int64_t rows, float eps, void* ws, bool bf16, hipStream_t s) {
+                            int64_t p, int64_t rows, float eps, void* ws, bool bf16, bool silu, hipStream_t s) {
   if (bf16)
     return gn_run(static_cast<uint16_t*>(y), stats_out, static_cast<const uint16_t*>(x), stale_stats, gamma, beta, B,
-                  H, W, C, G, P, p, rows, eps, ws, s);
+                  H, W, C, G, P, p, rows, eps, ws, silu, s);
   return gn_run(static_cast<float*>(y), stats_out, static_cast<const float*>(x), stale_stats, gamma, beta, B, H, W, C,
-                G, P, p, rows, eps, ws, s);
+                G, P, p, rows, eps, ws, silu, s);
 }
 
 }  // namespace dpp

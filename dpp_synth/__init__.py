@@ -45,6 +45,12 @@ STREAMS = {
     "v_noise": 10,    # stale values = fresh + sigma * this
     "eps_u": 11,      # unconditional noise prediction
     "eps_c_noise": 12,  # conditional = unconditional + sigma_cfg * this
+    "w_q": 13,        # projection weights [C,C], N(0,1)/sqrt(C)
+    "w_k": 14,
+    "w_v": 15,
+    "w_o": 16,
+    "b_qkvo": 17,     # projection biases [4,C], weight_std * N(0,1)
+    "kv_stale": 18,   # the previous step's projected K and V of the image [B,N,2C]
 }
 
 
@@ -196,6 +202,24 @@ def attention_inputs(cfg: Config) -> dict:
     vs = v + np.float32(cfg.stale_sigma) * normal(s, "v_noise", (B, N, C))
     return {"q": store(cfg, q), "k": store(cfg, k), "v": store(cfg, v),
             "k_stale": store(cfg, ks), "v_stale": store(cfg, vs)}
+
+
+def projection_inputs(cfg: Config) -> dict:
+    """Weights of the attention module's projections and the previous step's
+    projected K/V buffer.
+
+    w_q, w_k, w_v, w_o: [C,C] storage format (output-major), N(0,1)/sqrt(C)
+    (unit-variance outputs for unit-variance inputs); b_q, b_k, b_v, b_o: [C]
+    float32, weight_std N(0,1); kv_stale: [B,N,2C] storage format, K in
+    channels [0,C), V in [C,2C), N(0,1)."""
+    s, B, N, C = cfg.seed, cfg.B, cfg.N, cfg.C
+    sc = np.float32(1.0 / np.sqrt(C))
+    out = {f"w_{n}": store(cfg, sc * normal(s, f"w_{n}", (C, C))) for n in "qkvo"}
+    b = (cfg.weight_std * normal(s, "b_qkvo", (4, C))).astype(np.float32)
+    for i, n in enumerate("qkvo"):
+        out[f"b_{n}"] = np.ascontiguousarray(b[i])
+    out["kv_stale"] = store(cfg, normal(s, "kv_stale", (B, N, 2 * C)))
+    return out
 
 
 def cfg_inputs(cfg: Config, latent: Optional[Tuple[int, int, int]] = None, n: Optional[int] = None) -> dict:

@@ -122,6 +122,22 @@ int dpp_groupnorm_stale(void* y, float* stats_out, const void* x,
                         size_t workspace_bytes, int dtype, void* stream);
 
 /*
+ * GroupNorm with stale statistics followed by SiLU, y = z * sigmoid(z) of
+ * the dpp_groupnorm_stale output z: the GroupNorm + SiLU pair that opens an
+ * SDXL residual block (the normalisation layer wrapped by DistriGroupNorm,
+ * DistriFusion architecture article, normalisation section).  Arguments,
+ * statistics, requirements and workspace exactly as dpp_groupnorm_stale;
+ * stats_out holds the sums of x (before normalisation).
+ */
+int dpp_groupnorm_silu_stale(void* y, float* stats_out, const void* x,
+                             const float* stale_stats, const float* gamma,
+                             const float* beta, int64_t B, int64_t H,
+                             int64_t W, int64_t C, int64_t G, int64_t P,
+                             int64_t p, int64_t rows, float eps,
+                             void* workspace, size_t workspace_bytes,
+                             int dtype, void* stream);
+
+/*
  * a3 -- 3x3 convolution of the patch rows with halo rows from the stale image
  * (DistriConv2dPP; DistriFusion architecture article, conv section; only the
  * own region is computed: DistriFusion reading notes, Introduction, fourth
@@ -173,6 +189,27 @@ int dpp_self_attn_displaced(void* o, const void* q, const void* k,
                             int64_t ld_q, int64_t ld_kv, int64_t ld_o,
                             float scale, void* workspace,
                             size_t workspace_bytes, int dtype, void* stream);
+
+/*
+ * Projection: y[b,m,n] = sum_k x[b,m,k] * w[n,k] + bias[n].  The to_q, to_k,
+ * to_v and to_out projections of the self-attention module that
+ * DistriSelfAttentionPP wraps (DistriFusion architecture article, attention
+ * section).  Element (b,m,k) of x is x[b*bs_x + m*ld_x + k]; element (b,m,n)
+ * of y is y[b*bs_y + m*ld_y + n] (strides in elements).  Free strides let the
+ * K/V projection of the fresh patch write straight into its rows of the
+ * private full-image K/V buffer: y = buffer + row0*W*ld_y with bs_y the
+ * buffer's batch stride -- the splice fused into the projection.
+ *   x [B,M,K] (dtype), w [N,K] (dtype, output-major), bias [N] float32 or
+ *   NULL, y [B,M,N] (dtype); y must not overlap x, w or bias, and output
+ *   batches must not overlap (bs_y >= (M-1)*ld_y + N when B > 1).
+ *   Requires ld_x >= K, ld_y >= N.  bf16 requires K % 8 == 0, N % 4 == 0,
+ *   x and w 16-byte aligned, ld_x and bs_x multiples of 8, y 8-byte aligned,
+ *   ld_y and bs_y multiples of 4.  Float32 accumulation, one rounding.
+ */
+int dpp_linear(void* y, const void* x, const void* w, const float* bias,
+               int64_t B, int64_t M, int64_t K, int64_t N, int64_t ld_x,
+               int64_t bs_x, int64_t ld_y, int64_t bs_y, int dtype,
+               void* stream);
 
 /*
  * a5 -- classifier-free guidance combine and denoising discrepancy

@@ -31,7 +31,7 @@ def header_symbols():
 
 def test_header_symbols_exported_and_bound():
     syms = header_symbols()
-    assert len(syms) == 10, syms
+    assert len(syms) == 12, syms
     for s in syms:
         assert hasattr(L, s), s
         assert s in _lib.SIGNATURES, s
@@ -188,3 +188,46 @@ def test_binding_raises_on_error_status():
     with pytest.raises(dpp.DppError) as ei:
         _lib._check("dpp_splice_patch", -2)
     assert ei.value.status == -2
+
+
+# ----------------------------------------------------------------- GroupNorm + SiLU
+def test_groupnorm_silu_validation_matches_groupnorm():
+    def gs(**kw):
+        args = dict(y=A, so=Bp, x=Cp, st=Dp, gamma=Ep, beta=Ep + 4096, B=1, H=8, W=4, C=64, G=8, P=2, p=0, rows=4,
+                    eps=1e-5, ws=WSP, wsb=1 << 20, dtype=BF16)
+        args.update(kw)
+        a = args
+        return L.dpp_groupnorm_silu_stale(a["y"], a["so"], a["x"], a["st"], a["gamma"], a["beta"], a["B"], a["H"],
+                                          a["W"], a["C"], a["G"], a["P"], a["p"], a["rows"], a["eps"], a["ws"],
+                                          a["wsb"], a["dtype"], None)
+    for kw, code in [(dict(dtype=2), DTYPE), (dict(x=None), NULL), (dict(gamma=None), NULL), (dict(C=60), SHAPE),
+                     (dict(C=20, G=4), UNSUP), (dict(x=Cp + 2), ALIGN), (dict(y=Cp), ALIAS), (dict(ws=None), WS)]:
+        assert gs(**kw) == code, kw
+        assert gn(**kw) == code, kw
+
+
+# ----------------------------------------------------------------- projections
+def lin(y=A, x=Bp, w=Cp, bias=Dp, B=1, M=100, K=64, N=64, ldx=64, bsx=6400, ldy=64, bsy=6400, dtype=BF16):
+    return L.dpp_linear(y, x, w, bias, B, M, K, N, ldx, bsx, ldy, bsy, dtype, None)
+
+
+def test_linear_validation():
+    assert lin(dtype=3) == DTYPE
+    assert lin(y=None) == NULL
+    assert lin(x=None) == NULL
+    assert lin(w=None) == NULL
+    assert lin(bias=None, x=None) == NULL          # bias is optional; x is not
+    assert lin(M=0) == SHAPE
+    assert lin(ldx=32) == SHAPE                    # ld_x < K
+    assert lin(ldy=32) == SHAPE                    # ld_y < N
+    assert lin(B=2, bsy=64) == SHAPE               # output batches overlap
+    assert lin(B=70000, bsy=1 << 20) == UNSUP
+    assert lin(K=60, ldx=64) == UNSUP              # bf16 needs K % 8
+    assert lin(N=62, ldy=64) == UNSUP              # bf16 needs N % 4
+    assert lin(x=Bp + 8) == ALIGN
+    assert lin(ldx=68) == ALIGN                    # row stride not a multiple of 8 elements
+    assert lin(y=A + 2) == ALIGN
+    assert lin(y=Bp) == ALIAS                      # in place
+    assert lin(y=Cp + 64) == ALIAS                 # inside the weights
+    # f32: no divisibility or alignment requirement beyond the shapes
+    assert lin(K=60, ldx=60, N=62, ldy=62, bsx=6000, bsy=6200, dtype=F32, w=None) == NULL
