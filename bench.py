@@ -250,6 +250,8 @@ def main():
     kernels = None
     if args.kernels:
         kernels = time_kernels(cfg, layer, x_patches, gamma, beta, w, b, eps, rel, eps_c, eps_u, cfg_ws, dpp, torch)
+        if cfg.dtype == "bf16":
+            kernels.update(time_projections(cfg, layer, x_patches, gamma, beta, dpp, torch))
 
     out = {
         "metric": "displaced-attn + halo-conv TFLOP/s (% bf16 MFMA peak); ms per patch-layer step",
@@ -339,6 +341,63 @@ def time_kernels(cfg, layer, x_patches, gamma, beta, w, b, eps, rel, eps_c, eps_
         rate = amount / (ms * 1e-3) / (1e12 if unit == "TFLOP/s" else 1e9)
         res[k] = {"avg_ms": round(ms, 5), unit: round(rate, 2), "frac_peak": round(rate / peak, 4),
                   "work": amount}
+    return res
+
+
+def time_projections(cfg, layer, x_patches, gamma, beta, dpp, torch, reps=10):
+    """The projection calls of the attention module and GroupNorm + SiLU at
+    the workload's patch size (not part of the headline step): q = x Wq^T +
+    bq, the fresh K/V projection written into the patch's rows of a [B,N,2C]
+    K/V buffer, out = o Wo^T + bo.  Seeded weights (projection_inputs)."""
+    from dpp_synth import projection_inputs
+    pi = projection_inputs(cfg)
+    dev = "cuda"
+
+    def bf(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    C, M = cfg.C, cfg.Nq
+    wq, wo = bf(pi["w_q"]), bf(pi["w_o"])
+    wkv = bf(np.concatenate([pi["w_k"], pi["w_v"]], axis=0))
+    bq, bo = torch.from_numpy(pi["b_q"]).to(dev), torch.from_numpy(pi["b_o"]).to(dev)
+    bkv = torch.from_numpy(np.concatenate([pi["b_k"], pi["b_v"]])).to(dev)
+    kv2 = bf(pi["kv_stale"])
+    xq = layer.y2.view(cfg.B, M, C)
+    q = torch.empty(cfg.B, M, C, dtype=torch.bfloat16, device=dev)
+    out = torch.empty_like(q)
+    o = layer.o.view(cfg.B, M, C)
+    ev = {k: [] for k in ("linear_q", "linear_kv_into_buffer", "linear_out", "groupnorm_silu")}
+
+    def timed(name, fn):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        fn()
+        e1.record()
+        ev[name].append((e0, e1))
+
+    for _ in range(reps):
+        for p in range(cfg.P):
+            t0 = p * M
+            timed("groupnorm_silu", lambda: dpp.dpp_groupnorm_silu_stale(layer.y1, layer.stats_next, x_patches[p],
+                                                                         layer.stats_prev, gamma, beta, cfg.H, cfg.G,
+                                                                         cfg.P, p, cfg.gn_eps, layer.gn_ws))
+            timed("linear_q", lambda: dpp.dpp_linear(q, xq, wq, bq))
+            timed("linear_kv_into_buffer", lambda: dpp.dpp_linear(kv2[:, t0:t0 + M, :], xq, wkv, bkv))
+            timed("linear_out", lambda: dpp.dpp_linear(out, o, wo, bo))
+    torch.cuda.synchronize()
+    act = cfg.B * M * C * 2
+    work = {
+        "linear_q": (2.0 * cfg.B * M * C * C, "TFLOP/s", PEAK_BF16_TFLOPS),
+        "linear_kv_into_buffer": (2.0 * cfg.B * M * C * 2 * C, "TFLOP/s", PEAK_BF16_TFLOPS),
+        "linear_out": (2.0 * cfg.B * M * C * C, "TFLOP/s", PEAK_BF16_TFLOPS),
+        "groupnorm_silu": (2.0 * act + 2 * 4 * cfg.B * cfg.G * (cfg.P + 1), "GB/s", PEAK_HBM_GBS),
+    }
+    res = {}
+    for k, lst in ev.items():
+        ms = float(np.median([a.elapsed_time(b_) for a, b_ in lst]))
+        amount, unit, peak = work[k]
+        rate = amount / (ms * 1e-3) / (1e12 if unit == "TFLOP/s" else 1e9)
+        res[k] = {"median_ms": round(ms, 5), unit: round(rate, 2), "frac_peak": round(rate / peak, 4), "work": amount}
     return res
 
 

@@ -8,10 +8,12 @@
 //
 // bf16 path: MFMA v_mfma_f32_16x16x32_bf16 with A = weight rows (output
 // channels, K-contiguous) and B = token rows (K-contiguous).  A workgroup owns
-// 128 channels x 128 tokens; eight waves, each 32 channels x 64 tokens (2 x 4
+// 128 channels x 160 tokens (7200 tokens x 640 channels: 225 workgroups, one
+// round on 256 CUs); eight waves, each 32 channels x 80 tokens (2 x 5
 // accumulator tiles).  K is walked in 64-wide slices staged in LDS (XOR-
-// swizzled rows, double-buffered), the next slice fetched into registers
-// during the current one's MFMAs; one barrier per slice.  Each lane's
+// swizzled rows, double-buffered); for K = 320, 640, 1280 the slice loop is
+// unrolled and the global loads run four slices ahead (their latency is long
+// against one slice's MFMAs at these sizes); one barrier per slice.  Each lane's
 // accumulator holds four consecutive channels of one token: one 8-byte store.
 //
 // f32 path: one thread per output, direct loop (small shapes).
@@ -36,12 +38,13 @@ __global__ __launch_bounds__(256) void linear_f32_kernel(float* __restrict__ y, 
 }
 
 constexpr int kLinBN = 128;   // output channels per workgroup
-constexpr int kLinBM = 128;   // tokens per workgroup
+constexpr int kLinBM = 160;   // tokens per workgroup
 constexpr int kLinKC = 64;    // K slice (8 x 16-byte vectors per row)
 constexpr int kLinThreads = 512;
 constexpr int kLinCG = 2;     // 16-channel MFMA groups per wave
-constexpr int kLinTG = 4;     // 16-token MFMA groups per wave
-constexpr int kLinIters = kLinBN * 8 / kLinThreads;  // staged vectors per thread per operand
+constexpr int kLinTG = 5;     // 16-token MFMA groups per wave
+constexpr int kLinItersA = kLinBN * 8 / kLinThreads;                      // weight vectors per thread
+constexpr int kLinItersB = (kLinBM * 8 + kLinThreads - 1) / kLinThreads;  // token vectors per thread
 
 struct LinArgs {
   const uint16_t* x;
@@ -54,7 +57,19 @@ struct LinArgs {
 // LDS row of 8 x 16-byte slots, slot XOR-swizzled by the row index.
 __device__ __forceinline__ int lin_swz(int row, int slot) { return row * 8 + (slot ^ (row & 7)); }
 
+constexpr int kLinBufWord3 = 0x00020000;  // raw 32-bit buffer access, no swizzle
+constexpr int kLinAhead = 4;              // K slices in flight (fully unrolled instantiations)
+
+// NSL > 0: the K loop has exactly NSL slices and is fully unrolled, with the
+// global loads kLinAhead slices ahead in a ring of registers (every count is
+// a constant, so each wait covers exactly the slice it needs).  NSL == 0:
+// any K, loads one slice ahead.  Loads are raw buffer loads against
+// resources that end at the last element of w and of x's batch entry: rows
+// past N or M read as zero, so no load is predicated; the K tail (k >= K in
+// the last slice) is zeroed by a select.
+template <int NSL>
 __global__ __launch_bounds__(kLinThreads) void linear_bf16_mfma_kernel(LinArgs a) {
+  constexpr int AHEAD = NSL > 0 ? (NSL < kLinAhead ? NSL : kLinAhead) : 1;
   __shared__ uint4 As[2][kLinBN * 8];
   __shared__ uint4 Bs[2][kLinBM * 8];
   const int tid = threadIdx.x;
@@ -63,34 +78,52 @@ __global__ __launch_bounds__(kLinThreads) void linear_bf16_mfma_kernel(LinArgs a
   const int64_t b = blockIdx.z;
   const int64_t n0 = static_cast<int64_t>(blockIdx.y) * kLinBN;
   const int64_t m0 = static_cast<int64_t>(blockIdx.x) * kLinBM;
-  const uint16_t* xb = a.x + b * a.bs_x;
+  const int nslices = NSL > 0 ? NSL : static_cast<int>((a.K + kLinKC - 1) / kLinKC);
 
-  // staging map: vector id -> (row, 16-byte slot) of a 128 x 64 slice
-  const uint16_t* a_src[kLinIters];
-  const uint16_t* b_src[kLinIters];
+  const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(a.w), 0, static_cast<int>(a.N * a.K * 2), kLinBufWord3);
+  const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(a.x + b * a.bs_x), 0, static_cast<int>(((a.M - 1) * a.ld_x + a.K) * 2), kLinBufWord3);
+  // staging map: vector id -> (row, 16-byte slot) of a slice (rows x 64);
+  // byte offsets of the slice at k = 0
+  const int slot8 = tid & 7;  // the same for every staged vector of a thread
+  int a_off[kLinItersA], b_off[kLinItersB];
 #pragma unroll
-  for (int u = 0; u < kLinIters; ++u) {
-    const int id = tid + u * kLinThreads;
-    const int row = id >> 3, slot = id & 7;
-    a_src[u] = (n0 + row < a.N) ? a.w + (n0 + row) * a.K + slot * 8 : nullptr;
-    b_src[u] = (m0 + row < a.M) ? xb + (m0 + row) * a.ld_x + slot * 8 : nullptr;
+  for (int u = 0; u < kLinItersA; ++u) {
+    const int row = (tid + u * kLinThreads) >> 3;
+    a_off[u] = static_cast<int>(((n0 + row) * a.K + slot8 * 8) * 2);
   }
-  uint4 a_reg[kLinIters], b_reg[kLinIters];
-  auto load = [&](int64_t k0) {
 #pragma unroll
-    for (int u = 0; u < kLinIters; ++u) {
-      const int slot = (tid + u * kLinThreads) & 7;
-      const bool in_k = k0 + slot * 8 < a.K;  // K % 8 == 0: a vector is wholly in or out
-      a_reg[u] = (a_src[u] != nullptr && in_k) ? *reinterpret_cast<const uint4*>(a_src[u] + k0) : make_uint4(0, 0, 0, 0);
-      b_reg[u] = (b_src[u] != nullptr && in_k) ? *reinterpret_cast<const uint4*>(b_src[u] + k0) : make_uint4(0, 0, 0, 0);
-    }
+  for (int u = 0; u < kLinItersB; ++u) {
+    const int row = (tid + u * kLinThreads) >> 3;
+    b_off[u] = row < kLinBM ? static_cast<int>(((m0 + row) * a.ld_x + slot8 * 8) * 2) : 0x7ffffff0;
+  }
+  // Loaded values are not touched until they are staged (a select right
+  // after a load would make the wave wait for it there).
+  uint4 a_reg[AHEAD][kLinItersA], b_reg[AHEAD][kLinItersB];
+  auto load = [&](int r, int s) {
+    const int kb = s * kLinKC * 2;
+#pragma unroll
+    for (int u = 0; u < kLinItersA; ++u)
+      a_reg[r][u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rw, a_off[u] + kb, 0, 0));
+#pragma unroll
+    for (int u = 0; u < kLinItersB; ++u)
+      b_reg[r][u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rx, b_off[u] + kb, 0, 0));
   };
-  auto store = [&](int buf) {
+  // stage slice s from ring slot r; vectors past K (last slice only) are
+  // masked to zero (a bit mask, not a branch, keeps the ring in registers)
+  auto masked = [](const uint4& v, unsigned m) { return make_uint4(v.x & m, v.y & m, v.z & m, v.w & m); };
+  auto store = [&](int r, int s, int buf) {
+    const unsigned m = (s * kLinKC + slot8 * 8 < a.K) ? 0xffffffffu : 0u;  // K % 8 == 0: whole vectors
 #pragma unroll
-    for (int u = 0; u < kLinIters; ++u) {
+    for (int u = 0; u < kLinItersA; ++u) {
       const int id = tid + u * kLinThreads;
-      As[buf][lin_swz(id >> 3, id & 7)] = a_reg[u];
-      Bs[buf][lin_swz(id >> 3, id & 7)] = b_reg[u];
+      As[buf][lin_swz(id >> 3, id & 7)] = masked(a_reg[r][u], m);
+    }
+#pragma unroll
+    for (int u = 0; u < kLinItersB; ++u) {
+      const int id = tid + u * kLinThreads;
+      if (id < kLinBM * 8) Bs[buf][lin_swz(id >> 3, id & 7)] = masked(b_reg[r][u], m);
     }
   };
 
@@ -102,14 +135,8 @@ __global__ __launch_bounds__(kLinThreads) void linear_bf16_mfma_kernel(LinArgs a
 
   const int kg = lane >> 4, pl = lane & 15;
   // fragment rows r = base + 16 i + pl share (r & 7) = (pl & 7)
-  const int a_row0 = wn * 32 + pl, b_row0 = wm * 64 + pl;
-  const int nslices = static_cast<int>((a.K + kLinKC - 1) / kLinKC);
-  load(0);
-  store(0);
-  if (nslices > 1) load(kLinKC);
-  __syncthreads();
-  for (int s = 0; s < nslices; ++s) {
-    const int buf = s & 1;
+  const int a_row0 = wn * 32 + pl, b_row0 = wm * (16 * kLinTG) + pl;
+  auto compute = [&](int buf) {
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       const int slot = (ks * 4 + kg) ^ (pl & 7);
@@ -123,17 +150,45 @@ __global__ __launch_bounds__(kLinThreads) void linear_bf16_mfma_kernel(LinArgs a
 #pragma unroll
         for (int j = 0; j < kLinTG; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
     }
-    // stage slice s+1 (in registers) into the other buffer, last read before
-    // the previous barrier; then fetch slice s+2
-    if (s + 1 < nslices) store(buf ^ 1);
+  };
+
+  if constexpr (NSL > 0) {
+    // prologue: slices 0 .. AHEAD-1 requested, slice 0 staged, slice AHEAD
+    // requested into the freed ring slot
+#pragma unroll
+    for (int r = 0; r < AHEAD; ++r) load(r, r);
+    store(0, 0, 0);
+    if (AHEAD < NSL) load(0, AHEAD);
     __syncthreads();
-    if (s + 2 < nslices) load(static_cast<int64_t>(s + 2) * kLinKC);
+    // slice s: MFMAs from buffer s & 1; slice s+1 (ring slot (s+1) % AHEAD)
+    // into the other buffer, last read before the previous barrier; slice
+    // s+1+AHEAD requested into the freed slot
+#pragma unroll
+    for (int s = 0; s < NSL; ++s) {
+      compute(s & 1);
+      if (s + 1 < NSL) {
+        store((s + 1) % AHEAD, s + 1, (s + 1) & 1);
+        if (s + 1 + AHEAD < NSL) load((s + 1) % AHEAD, s + 1 + AHEAD);
+      }
+      __syncthreads();
+    }
+  } else {
+    load(0, 0);
+    store(0, 0, 0);
+    if (nslices > 1) load(0, 1);
+    __syncthreads();
+    for (int s = 0; s < nslices; ++s) {
+      compute(s & 1);
+      if (s + 1 < nslices) store(0, s + 1, (s + 1) & 1);
+      __syncthreads();
+      if (s + 2 < nslices) load(0, s + 2);
+    }
   }
 
-  // epilogue: lane holds channels n0 + wn*32 + 16 i + 4 kg + 0..3 of token m0 + wm*64 + 16 j + pl
+  // epilogue: lane holds channels n0 + wn*32 + 16 i + 4 kg + 0..3 of token m0 + wm*80 + 16 j + pl
 #pragma unroll
   for (int j = 0; j < kLinTG; ++j) {
-    const int64_t m = m0 + wm * 64 + 16 * j + pl;
+    const int64_t m = m0 + wm * (16 * kLinTG) + 16 * j + pl;
     if (m >= a.M) continue;
     uint16_t* yp = a.y + b * a.bs_y + m * a.ld_y;
 #pragma unroll
@@ -174,7 +229,12 @@ hipError_t launch_linear(void* y, const void* x, const void* w, const float* bia
   a.bs_y = bs_y;
   dim3 grid(static_cast<unsigned>(ceil_div(M, kLinBM)), static_cast<unsigned>(ceil_div(N, kLinBN)),
             static_cast<unsigned>(B));
-  hipLaunchKernelGGL(linear_bf16_mfma_kernel, grid, dim3(kLinThreads), 0, s, a);
+  switch (ceil_div(K, kLinKC)) {
+    case 5: hipLaunchKernelGGL(linear_bf16_mfma_kernel<5>, grid, dim3(kLinThreads), 0, s, a); break;
+    case 10: hipLaunchKernelGGL(linear_bf16_mfma_kernel<10>, grid, dim3(kLinThreads), 0, s, a); break;
+    case 20: hipLaunchKernelGGL(linear_bf16_mfma_kernel<20>, grid, dim3(kLinThreads), 0, s, a); break;
+    default: hipLaunchKernelGGL(linear_bf16_mfma_kernel<0>, grid, dim3(kLinThreads), 0, s, a); break;
+  }
   return hipGetLastError();
 }
 
