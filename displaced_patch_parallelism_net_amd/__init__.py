@@ -16,6 +16,7 @@ from ._lib import (  # noqa: F401
     dpp_groupnorm_silu_stale,
     dpp_groupnorm_stale,
     dpp_groupnorm_stale_workspace_bytes,
+    dpp_hybrid_schedule,
     dpp_linear,
     dpp_self_attn_displaced,
     dpp_self_attn_workspace_bytes,

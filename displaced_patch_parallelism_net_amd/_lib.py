@@ -40,6 +40,7 @@ SIGNATURES = {
     "dpp_linear": (_i, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _i64, _i64, _i64, _i, _vp]),
     "dpp_cfg_combine_workspace_bytes": (_sz, [_i64]),
     "dpp_cfg_combine_relmae": (_i, [_vp, _vp, _vp, _vp, _i64, _f, _vp, _sz, _i, _vp]),
+    "dpp_hybrid_schedule": (_i, [_vp, _i64, _f, _f, _i64, _vp, _vp, _vp]),
 }
 
 
@@ -193,6 +194,21 @@ def dpp_cfg_combine_relmae(eps, relmae, eps_c, eps_u, guidance: float, workspace
            LIB.dpp_cfg_combine_relmae(_ptr(eps), _ptr(relmae), _ptr(eps_c), _ptr(eps_u), n, guidance, _ptr(workspace),
                                       0 if workspace is None else workspace.numel() * workspace.element_size(),
                                       _dtype(eps_c), _stream(stream)))
+
+
+def dpp_hybrid_schedule(relmae, rho: float = 0.25, eps: float = 0.02, min_warmup: int = 1):
+    """Stages (0 warm-up, 1 parallel, 2 fully-connecting) for a host
+    sequence of per-step rel-MAE values; returns (stage int32 array, tau1,
+    tau2).  Host-only call."""
+    import numpy as np
+    d = np.ascontiguousarray(relmae, dtype=np.float32)
+    T = d.shape[0]
+    stage = np.empty(T, dtype=np.int32)
+    t1, t2 = ctypes.c_int64(), ctypes.c_int64()
+    _check("dpp_hybrid_schedule", LIB.dpp_hybrid_schedule(d.ctypes.data_as(ctypes.c_void_p), T, rho, eps, min_warmup,
+                                                          stage.ctypes.data_as(ctypes.c_void_p), ctypes.byref(t1),
+                                                          ctypes.byref(t2)))
+    return stage, t1.value, t2.value
 
 
 def dpp_strerror(status: int) -> str:

@@ -51,6 +51,7 @@ STREAMS = {
     "w_o": 16,
     "b_qkvo": 17,     # projection biases [4,C], weight_std * N(0,1)
     "kv_stale": 18,   # the previous step's projected K and V of the image [B,N,2C]
+    "relmae_trace": 19,  # per-step discrepancy trace: shape draws and noise
 }
 
 
@@ -236,6 +237,27 @@ def cfg_inputs(cfg: Config, latent: Optional[Tuple[int, int, int]] = None, n: Op
     u = normal(cfg.seed, "eps_u", (n,))
     c = u + np.float32(cfg.cfg_sigma) * normal(cfg.seed, "eps_c_noise", (n,))
     return {"eps_u": store(cfg, u), "eps_c": store(cfg, c)}
+
+
+def relmae_trace(seed: int, T: int, noise: float = 0.0) -> np.ndarray:
+    """Synthetic per-step discrepancy trace [T] float32 in denoising order.
+
+    The shape the condition-split scheduling pages describe: large at the
+    start, falling fast, flattening in the middle and rising towards the end.
+    d(t) = base + amp exp(-t / decay) + rise max(0, t - t_rise)^2 / T^2, with
+    decay, t_rise and the three scales drawn per seed, times (1 + noise N(0,1)).
+    """
+    g = stream(seed, "relmae_trace")
+    base = g.uniform(0.05, 0.2)
+    amp = g.uniform(0.5, 2.0)
+    decay = g.uniform(0.04, 0.15) * T
+    t_rise = g.uniform(0.55, 0.8) * T
+    rise = g.uniform(0.5, 3.0)
+    t = np.arange(T, dtype=np.float64)
+    d = base + amp * np.exp(-t / decay) + rise * np.maximum(0.0, t - t_rise) ** 2 / float(T) ** 2
+    if noise:
+        d = d * (1.0 + noise * g.standard_normal(T))
+    return d.astype(np.float32)
 
 
 def rows_of(a: np.ndarray, row0: int, rows: int) -> np.ndarray:

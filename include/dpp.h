@@ -230,6 +230,33 @@ int dpp_cfg_combine_relmae(void* eps, float* relmae, const void* eps_c,
                            void* workspace, size_t workspace_bytes, int dtype,
                            void* stream);
 
+/*
+ * Adaptive parallelism switching (Hybridiff technical summary, section 2B):
+ * the per-step denoising discrepancy (the rel-MAE of
+ * dpp_cfg_combine_relmae) selects, for each denoising step, the warm-up
+ * stage (0: branches run serially), the parallel stage (1: conditional and
+ * unconditional branches on two devices) or the fully-connecting stage (2).
+ * The stage boundaries are where the discrepancy's decline slows (tau1) and
+ * where it starts to rise again (tau2); the pages give no thresholds, so the
+ * rule is:
+ *   drop[i]  = relmae[i-1] - relmae[i],  maxdrop[i] = max(drop[1..i], 0)
+ *   tau1     = first i >= min_warmup with maxdrop[i] > 0 and
+ *              drop[i] <= rho * maxdrop[i]
+ *   tau2     = first i > tau1 with relmae[i] > (1 + eps) *
+ *              min(relmae[tau1..i-1])
+ *   stage[i] = 0 for i < tau1, 1 for tau1 <= i < tau2, 2 for i >= tau2
+ * (T when a boundary never comes).  float32 arithmetic; NaN entries (0/0
+ * discrepancy) never trigger a boundary.  Causal: stage[i] depends on
+ * relmae[0..i] only, so the call can be repeated on the growing trace.
+ *   relmae [T] host float32, in denoising order (index 0 = the first step);
+ *   stage  [T] host int32 out; tau1, tau2 host int64 out.
+ *   Requires T >= 1, min_warmup >= 1, 0 <= rho <= 1, eps >= 0.  Host code:
+ *   no device work, no stream.  Typical rho = 0.25, eps = 0.02.
+ */
+int dpp_hybrid_schedule(const float* relmae, int64_t T, float rho, float eps,
+                        int64_t min_warmup, int32_t* stage, int64_t* tau1,
+                        int64_t* tau2);
+
 #ifdef __cplusplus
 }
 #endif

@@ -46,6 +46,11 @@ Readings where the pages are silent (each also listed in the design notes):
       previous step's projected K and V (splicing rows commutes with a
       row-wise linear map, so this equals projecting the spliced input);
   R12 GroupNorm + SiLU: z * sigmoid(z) applied to the GroupNorm output.
+  R13 stage switching: the warm-up ends at the first step (at or after a
+      minimum warm-up) whose decline d[i-1] - d[i] is at most rho times the
+      fastest decline so far; the parallel stage ends at the first later step
+      whose discrepancy exceeds (1 + eps) times that stage's running minimum
+      (rho = 0.25, eps = 0.02 by default).
 """
 from .dpp_oracle import (  # noqa: F401
     bf16_round,
@@ -56,6 +61,7 @@ from .dpp_oracle import (  # noqa: F401
     conv3x3_halo_sampled,
     self_attn_displaced,
     cfg_combine_relmae,
+    hybrid_schedule,
     silu,
     groupnorm_silu_stale,
     linear,

@@ -278,6 +278,54 @@ def cfg_combine_relmae(eps_c, eps_u, guidance: float):
     return eps, float(rel)
 
 
+# ------------------------------------------------------------------ next-2: stage switching
+def hybrid_schedule(relmae, rho: float = 0.25, eps: float = 0.02, min_warmup: int = 1):
+    """Warm-up / parallel / fully-connecting stages from the discrepancy trace.
+
+    Hybridiff technical summary, section 2B: the denoising steps split into a
+    warm-up stage (before tau1), a parallelism stage (tau1 up to tau2) and a
+    fully-connecting stage (from tau2); tau1 is where the discrepancy's
+    decline flattens and tau2 where it starts to rise, both found from the
+    live trace.  Reading R13 makes the two points concrete:
+      * the decline at step i is d[i-1] - d[i]; the warm-up ends at the first
+        step i >= min_warmup whose decline is at most rho times the largest
+        decline so far (which must be positive);
+      * the parallel stage ends at the first later step whose discrepancy
+        exceeds (1 + eps) times the smallest discrepancy of the parallel stage
+        so far.
+    Comparisons in float32, the precision the trace is kept in; a NaN step
+    (0/0 discrepancy) never ends a stage.  Returns (stage int32 [T], tau1,
+    tau2) with T for a boundary that never comes."""
+    d = np.asarray(relmae, dtype=np.float32)
+    T = d.shape[0]
+    rho32 = np.float32(rho)
+    grow = np.float32(1) + np.float32(eps)
+    stage = np.zeros(T, dtype=np.int32)
+    tau1 = tau2 = T
+    fastest = np.float32(0)
+    with np.errstate(invalid="ignore", over="ignore"):
+        # warm-up: look for the flattening point
+        for i in range(1, T):
+            decline = np.float32(d[i - 1] - d[i])
+            if decline > fastest:
+                fastest = decline
+            if i >= min_warmup and fastest > 0 and decline <= rho32 * fastest:
+                tau1 = i
+                break
+        # parallel stage: look for the rise above its running minimum
+        if tau1 < T:
+            lowest = d[tau1]
+            for i in range(tau1 + 1, T):
+                if d[i] > grow * lowest:
+                    tau2 = i
+                    break
+                if d[i] < lowest:
+                    lowest = d[i]
+    stage[tau1:tau2] = 1
+    stage[tau2:] = 2
+    return stage, int(tau1), int(tau2)
+
+
 # ------------------------------------------------------------------ chained block
 def _store(a, bf16: bool):
     return bf16_round(a) if bf16 else _f64(a)

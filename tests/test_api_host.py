@@ -31,7 +31,7 @@ def header_symbols():
 
 def test_header_symbols_exported_and_bound():
     syms = header_symbols()
-    assert len(syms) == 12, syms
+    assert len(syms) == 13, syms
     for s in syms:
         assert hasattr(L, s), s
         assert s in _lib.SIGNATURES, s

@@ -526,3 +526,95 @@ def test_projected_attention_splice_commutes_with_projection():
     want = oracle.linear(oracle.self_attn_displaced(oracle.linear(x, wq, bq), K, V, heads), wo, bo)
     np.testing.assert_allclose(r["out"], want, rtol=1e-11, atol=1e-11)
     np.testing.assert_allclose(r["k"], K, rtol=1e-12, atol=1e-12)
+
+
+# ----------------------------------------------------------------- stage switching (R13)
+U_TRACE = [0.5, 0.3, 0.2, 0.17, 0.16, 0.155, 0.15, 0.16, 0.2, 0.3]
+
+
+def test_schedule_hand_worked_u_trace():
+    # declines 0.2, 0.1, 0.03: the fastest is 0.2, so the first decline at or
+    # below 0.05 (step 3) ends the warm-up; the minimum of the parallel stage
+    # reaches 0.15 at step 6 and 0.16 > 1.02 * 0.15 at step 7 ends it
+    st, t1, t2 = oracle.hybrid_schedule(U_TRACE)
+    assert (t1, t2) == (3, 7)
+    assert st.tolist() == [0, 0, 0, 1, 1, 1, 1, 2, 2, 2]
+    # a longer warm-up floor moves tau1 only
+    assert oracle.hybrid_schedule(U_TRACE, min_warmup=5)[1:] == (5, 7)
+    # rho = 0.1 needs a decline <= 0.02: step 4 (0.01)
+    assert oracle.hybrid_schedule(U_TRACE, rho=0.1)[1:] == (4, 7)
+    # eps = 0.1: 0.16 <= 0.165 keeps step 7 parallel; 0.2 > 0.165 ends it at 8
+    assert oracle.hybrid_schedule(U_TRACE, eps=0.1)[1:] == (3, 8)
+
+
+@pytest.mark.parametrize("r,rho", [(0.8, 0.25), (0.9, 0.25), (0.7, 0.1), (0.95, 0.5)])
+def test_schedule_geometric_decay_closed_form(r, rho):
+    # d_i = r^i: decline_i = r^(i-1) (1 - r), largest at i = 1, so the warm-up
+    # ends at the first i with r^(i-1) <= rho: i = 1 + ceil(ln rho / ln r);
+    # a strictly falling trace never starts the fully-connecting stage
+    x = math.log(rho) / math.log(r)
+    assert abs(x - round(x)) > 1e-3
+    T = 80
+    d = r ** np.arange(T)
+    st, t1, t2 = oracle.hybrid_schedule(d, rho=rho)
+    assert t1 == 1 + math.ceil(x)
+    assert t2 == T
+    assert (st[:t1] == 0).all() and (st[t1:] == 1).all()
+
+
+@pytest.mark.parametrize("g", [1.5, 1.005, 1.0013])
+def test_schedule_decay_then_growth_closed_form(g):
+    # r^i down to step m, then r^m g^(i-m): the parallel stage's minimum is r^m
+    # and it ends at the first i with g^(i-m) > 1 + eps, i.e.
+    # i = m + floor(ln(1 + eps) / ln g) + 1
+    r, m, T, eps = 0.8, 30, 200, 0.02
+    x = math.log(1 + eps) / math.log(g)
+    assert abs(x - round(x)) > 1e-2
+    i = np.arange(T)
+    d = np.where(i <= m, r ** i, r ** m * g ** (i - m))
+    st, t1, t2 = oracle.hybrid_schedule(d, eps=eps)
+    assert t1 == 8
+    assert t2 == m + math.floor(x) + 1
+    assert st.tolist() == [0] * t1 + [1] * (t2 - t1) + [2] * (T - t2)
+
+
+def test_schedule_degenerate_traces():
+    T = 12
+    # a constant-rate decline never flattens (exact binary steps)
+    lin = (T - np.arange(T)) * 0.125
+    assert oracle.hybrid_schedule(lin)[1:] == (T, T)
+    # ... unless rho = 1: then the first allowed step ends the warm-up
+    assert oracle.hybrid_schedule(lin, rho=1.0)[1:] == (1, T)
+    assert oracle.hybrid_schedule(lin, rho=1.0, min_warmup=4)[1:] == (4, T)
+    # a flat trace has no positive decline: the warm-up never ends
+    st, t1, t2 = oracle.hybrid_schedule(np.full(T, 0.3))
+    assert (t1, t2) == (T, T) and not st.any()
+    # a single step and a rising trace stay in the warm-up
+    assert oracle.hybrid_schedule([0.4])[1:] == (1, 1)
+    assert oracle.hybrid_schedule(np.arange(1, T + 1) * 0.1)[1:] == (T, T)
+    # rho = 0: only a non-falling step ends the warm-up (step 7, 0.16 after
+    # 0.15); the parallel stage then starts at 0.16 and 0.2 ends it at step 8
+    assert oracle.hybrid_schedule(U_TRACE, rho=0.0)[1:] == (7, 8)
+
+
+def test_schedule_nan_steps_never_switch():
+    # 0/0 discrepancies (NaN) neither end the warm-up nor the parallel stage
+    d = list(U_TRACE)
+    d[3] = float("nan")          # would have ended the warm-up
+    # step 3: NaN decline; step 4: NaN decline; step 5: 0.005 <= 0.05
+    assert oracle.hybrid_schedule(d)[1:] == (5, 7)
+    d = list(U_TRACE)
+    d[7] = float("nan")          # would have ended the parallel stage
+    assert oracle.hybrid_schedule(d)[1:] == (3, 8)
+
+
+def test_schedule_is_causal():
+    # the stage of step i depends on steps 0..i only: scheduling a prefix of
+    # the trace gives the prefix of the full schedule
+    from dpp_synth import relmae_trace
+    for seed in range(6):
+        d = relmae_trace(seed, 60, noise=0.005)
+        full = oracle.hybrid_schedule(d)[0]
+        for n in (1, 7, 23, 41, 60):
+            assert (oracle.hybrid_schedule(d[:n])[0] == full[:n]).all()
+        assert (np.diff(full) >= 0).all()
