@@ -124,6 +124,8 @@ int dpp_conv3x3_halo(void* y, const void* x, const void* stale_full, const void*
   if (B > 65535 || W > (1 << 24) || H > (1 << 24) || Cin > (1 << 20) || Cout > (1 << 20)) return DPP_ERR_UNSUPPORTED;
   if (dtype == DPP_BF16) {
     if (Cin % 64 != 0 || Cout % 16 != 0) return DPP_ERR_UNSUPPORTED;
+    // weight byte offsets (rows padded to a multiple of 128) are 32-bit
+    if ((Cout + 128) * 9 * Cin * 2 > 0x7fffffffLL) return DPP_ERR_UNSUPPORTED;
     if (!aligned16(x) || !aligned16(y) || !aligned16(weight) || (stale_full && !aligned16(stale_full)))
       return DPP_ERR_ALIGN;
   }

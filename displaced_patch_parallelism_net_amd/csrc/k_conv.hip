@@ -65,11 +65,19 @@ __global__ __launch_bounds__(256) void conv3x3_f32_kernel(float* __restrict__ y,
 // (1..5) so that the tiles cover the row width with the least waste and the
 // workgroup count fills the 256 CUs in whole rounds (e.g. 240 columns ->
 // TG 5: three tiles per row pair).
-// K loop: step = (64-channel slice, tap).  The (2+2) x (16 TG + 2) halo band
-// of a slice is staged once and reused by its nine taps; the weights of one
-// tap (128 x 64) per step.  Both are double-buffered in LDS; weights are
-// fetched into registers two steps ahead, right after a step's single
-// barrier.
+//
+// K loop: step = (64-channel slice, kernel row dy), three taps (dx = 0..2)
+// each, one barrier per step.  The weights of a step (3 x 128 x 64) are
+// double-buffered in LDS and fetched into registers two steps ahead.  The
+// (2+2) x (16 TG + 2) halo band of a slice has one LDS buffer: step dy reads
+// band rows dy and dy+1 only, so rows 0-1 of the next slice's band are
+// written during its dy = 2 step (they were last read at dy = 1) and rows 2-3
+// during the next slice's dy = 0 step; each half is fetched into registers
+// two steps before it is written.  Every global load is unconditional (weight
+// rows past Cout read zero through the buffer resource's range check; band
+// vectors in the zero padding load a valid address and are zeroed when
+// staged), and a pair of slices is one straight-line loop body, so each wait
+// before a staging store covers only the loads it needs.
 constexpr int kConvWN = 4;                      // waves across the 128 output channels
 constexpr int kConvCW = 128 / kConvWN;          // output channels per wave
 constexpr int kConvCG = kConvCW / 16;           // 16-channel MFMA groups per wave
@@ -77,7 +85,7 @@ constexpr int kConvThreads = 2 * kConvWN * 64;  // 2 tile rows x kConvWN
 constexpr int kConvBM = 128;  // output channels per workgroup
 constexpr int kConvKC = 64;   // input channels per slice (8 x 16-byte vectors)
 constexpr int kConvTR = 2;    // patch rows per workgroup
-constexpr int kConvTPS = 2;   // taps per barrier step
+constexpr int kConvBufWord3 = 0x00020000;  // raw 32-bit buffer access, no swizzle
 
 struct ConvArgs {
   const uint16_t* x;
@@ -96,15 +104,16 @@ __device__ __forceinline__ int swz(int row, int slot) { return row * 8 + (slot ^
 
 template <int TG>
 __global__ __launch_bounds__(kConvThreads, 1) void conv3x3_bf16_mfma_kernel(ConvArgs a) {
-  constexpr int TC = 16 * TG;           // output columns per tile
-  constexpr int BW = TC + 2;            // band columns
-  constexpr int BPIX = (kConvTR + 2) * BW;
-  constexpr int BAND_VEC = BPIX * 8;    // 16-byte vectors per band
-  constexpr int BAND_ITERS = (BAND_VEC + kConvThreads - 1) / kConvThreads;
+  constexpr int TC = 16 * TG;              // output columns per tile
+  constexpr int BW = TC + 2;               // band columns
+  constexpr int HALF_VEC = 2 * BW * 8;     // 16-byte vectors in two band rows
+  constexpr int HB_ITERS = (HALF_VEC + kConvThreads - 1) / kConvThreads;
   constexpr int W_ITERS = kConvBM * 8 / kConvThreads;
 
-  __shared__ uint4 band[2][BPIX * 8];
-  __shared__ uint4 wts[2][kConvTPS][kConvBM * 8];
+  // band: 4 rows x BW pixels x 8 slots, plus one dummy slot that absorbs the
+  // stores of the threads past the last vector of a half
+  __shared__ uint4 band[2 * HALF_VEC + 1];
+  __shared__ uint4 wts[2][3][kConvBM * 8];
 
   const int tid = threadIdx.x;
   const int wave = tid / kWave, lane = tid % kWave;
@@ -114,78 +123,84 @@ __global__ __launch_bounds__(kConvThreads, 1) void conv3x3_bf16_mfma_kernel(Conv
   const int tile_r = blockIdx.x / a.tiles_c, tile_c = blockIdx.x % a.tiles_c;
   const int pr0 = tile_r * kConvTR, pc0 = tile_c * TC;  // patch-relative origin of the pixel tile
   const int H = a.H, W = a.W, Cin = a.Cin;
-  const int64_t ktot = 9LL * Cin;
+  const int nslices = Cin / kConvKC;
+  const int nsteps = nslices * 3;
 
-  uint4 band_reg[BAND_ITERS];
-  uint4 w_regA[kConvTPS][W_ITERS], w_regB[kConvTPS][W_ITERS];  // weights of the next two steps
-
-  // Per-thread source pointers, computed once: band vector u of the first
-  // slice (x for patch rows, the stale image for halo rows; nullptr = zero
-  // padding) and the four weight rows.  Each step only adds a uniform offset.
-  const uint16_t* band_src[BAND_ITERS];
+  // Band staging map, fixed for the kernel: vector u of half hf (rows 2hf,
+  // 2hf+1) -> source address of the first slice (x for patch rows, the stale
+  // image for halo rows; zero padding loads x and is masked) and LDS slot.
+  const uint16_t* band_src[2][HB_ITERS];
+  int band_dst[2][HB_ITERS];
+  uint32_t band_ok = 0;  // bit hf*HB_ITERS+u: the vector is inside the image
 #pragma unroll
-  for (int u = 0; u < BAND_ITERS; ++u) {
-    const int id = tid + u * kConvThreads;
-    band_src[u] = nullptr;
-    if (id < BAND_VEC) {
-      const int pix = id >> 3, slot = id & 7;
+  for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+    for (int u = 0; u < HB_ITERS; ++u) {
+      const int id = tid + u * kConvThreads;
+      const int pix = hf * 2 * BW + (id >> 3), slot = id & 7;
       const int br = pix / BW, bc = pix % BW;
       const int r = pr0 - 1 + br;  // patch-relative
       const int ir = a.row0 + r;   // image row
       const int col = pc0 - 1 + bc;
-      if (ir >= 0 && ir < H && col >= 0 && col < W)
-        band_src[u] = ((r >= 0 && r < a.rows) ? a.x + ((static_cast<int64_t>(b) * a.rows + r) * W + col) * Cin
-                                              : a.stale + ((static_cast<int64_t>(b) * H + ir) * W + col) * Cin) +
-                      slot * 8;
+      band_src[hf][u] = a.x + slot * 8;
+      band_dst[hf][u] = 2 * HALF_VEC;
+      if (id < HALF_VEC) {
+        band_dst[hf][u] = swz(pix, slot);
+        if (ir >= 0 && ir < H && col >= 0 && col < W) {
+          band_src[hf][u] = ((r >= 0 && r < a.rows) ? a.x + ((static_cast<int64_t>(b) * a.rows + r) * W + col) * Cin
+                                                    : a.stale + ((static_cast<int64_t>(b) * H + ir) * W + col) * Cin) +
+                            slot * 8;
+          band_ok |= 1u << (hf * HB_ITERS + u);
+        }
+      }
     }
-  }
-  const uint16_t* w_src[W_ITERS];
+  // Weight staging map: vector u -> byte offset of row m0 + m, slot, at tap 0
+  // of slice 0; rows past Cout lie beyond the resource and read zero.
+  const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(a.w), 0, a.Cout * 9 * Cin * 2, kConvBufWord3);
+  int w_off[W_ITERS];
 #pragma unroll
   for (int u = 0; u < W_ITERS; ++u) {
     const int id = tid + u * kConvThreads;
-    const int m = id >> 3, slot = id & 7;
-    w_src[u] = (m0 + m < a.Cout) ? a.w + (m0 + m) * ktot + slot * 8 : nullptr;
+    w_off[u] = ((m0 + (id >> 3)) * 9 * Cin + (id & 7) * 8) * 2;
   }
 
-  auto load_band = [&](int c0) {
+  uint4 band_lo[HB_ITERS], band_hi[HB_ITERS];
+  uint4 w_regA[3][W_ITERS], w_regB[3][W_ITERS];  // weights of the next two steps
+  // Loads never touch their results until the staging store.
+  auto load_half = [&](uint4 (&reg)[HB_ITERS], int hf, int slice) {
+    const int c0 = min(slice, nslices - 1) * kConvKC;
 #pragma unroll
-    for (int u = 0; u < BAND_ITERS; ++u) {
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (band_src[u] != nullptr) v = *reinterpret_cast<const uint4*>(band_src[u] + c0);
-      band_reg[u] = v;
+    for (int u = 0; u < HB_ITERS; ++u) reg[u] = *reinterpret_cast<const uint4*>(band_src[hf][u] + c0);
+  };
+  auto store_half = [&](uint4 (&reg)[HB_ITERS], int hf) {
+#pragma unroll
+    for (int u = 0; u < HB_ITERS; ++u) {
+      const uint32_t keep = 0u - ((band_ok >> (hf * HB_ITERS + u)) & 1u);
+      // pins the mask here: hoisted next to the load, it would make the
+      // wave wait for the load there
+      asm volatile("" : "+v"(reg[u].x), "+v"(reg[u].y), "+v"(reg[u].z), "+v"(reg[u].w));
+      band[band_dst[hf][u]] = make_uint4(reg[u].x & keep, reg[u].y & keep, reg[u].z & keep, reg[u].w & keep);
     }
   };
-  const int nslices = Cin / kConvKC;
-  const int nflat = nslices * 9;  // (slice, tap) pairs
-  const int nsteps = (nflat + kConvTPS - 1) / kConvTPS;
-  auto load_w = [&](uint4 (&w_reg)[kConvTPS][W_ITERS], int step) {
+  auto load_w = [&](uint4 (&reg)[3][W_ITERS], int step) {
+    const int st = min(step, nsteps - 1);
+    const int sl = st / 3, dy = st - sl * 3;
 #pragma unroll
-    for (int i = 0; i < kConvTPS; ++i) {
-      const int f = step * kConvTPS + i;
-      const int sl = f / 9;
-      const int off = (f - sl * 9) * Cin + sl * kConvKC;
+    for (int dx = 0; dx < 3; ++dx) {
+      const int soff = ((dy * 3 + dx) * Cin + sl * kConvKC) * 2;
 #pragma unroll
-      for (int u = 0; u < W_ITERS; ++u) {
-        uint4 v = make_uint4(0, 0, 0, 0);
-        if (w_src[u] != nullptr && f < nflat) v = *reinterpret_cast<const uint4*>(w_src[u] + off);
-        w_reg[i][u] = v;
-      }
+      for (int u = 0; u < W_ITERS; ++u)
+        reg[dx][u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rw, w_off[u] + soff, 0, 0));
     }
   };
-  auto store_band = [&](int buf) {
+  auto store_w = [&](const uint4 (&reg)[3][W_ITERS], int buf) {
 #pragma unroll
-    for (int u = 0; u < BAND_ITERS; ++u) {
-      const int id = tid + u * kConvThreads;
-      if (id < BAND_VEC) band[buf][swz(id >> 3, id & 7)] = band_reg[u];
-    }
-  };
-  auto store_w = [&](const uint4 (&w_reg)[kConvTPS][W_ITERS], int buf) {
-#pragma unroll
-    for (int i = 0; i < kConvTPS; ++i)
+    for (int dx = 0; dx < 3; ++dx)
 #pragma unroll
       for (int u = 0; u < W_ITERS; ++u) {
         const int id = tid + u * kConvThreads;
-        wts[buf][i][swz(id >> 3, id & 7)] = w_reg[i][u];
+        wts[buf][dx][swz(id >> 3, id & 7)] = reg[dx][u];
       }
   };
 
@@ -201,64 +216,78 @@ __global__ __launch_bounds__(kConvThreads, 1) void conv3x3_bf16_mfma_kernel(Conv
   // slot per k step, fragment i at a fixed +16 rows.
   const int a_row0 = wn * kConvCW + pl;
   const int a_slot[2] = {(0 + kg) ^ (pl & 7), (4 + kg) ^ (pl & 7)};
-  // One step = kConvTPS consecutive (slice, tap) pairs f: MFMAs on the
-  // staged weights of the step and the band of each f's slice; then stage
-  // the weights of step+1 (held in wnext) and, once per slice (at its tap
-  // 6, at least a step before the slice's end), the next slice's band into
-  // the other band buffer, which the previous slice last used before an
-  // earlier barrier; barrier; then fetch the weights of step+3 into wnext
-  // (two steps of latency cover).
-  auto do_step = [&](int step, uint4 (&wnext)[kConvTPS][W_ITERS]) {
-    const int wb = step & 1;
-    int next_band = -1;  // slice whose band is stored at this step's end
+
+  // The three taps of kernel row dy on the staged weights of buffer wb.
+  auto compute = [&](int dy, int wb) {
 #pragma unroll
-    for (int sub = 0; sub < kConvTPS; ++sub) {
-      const int f = step * kConvTPS + sub;
-      if (f < nflat) {
-        const int slice = f / 9, tap = f - slice * 9;
-        const int bb = slice & 1;
-        if (tap == 0 && slice + 1 < nslices) load_band((slice + 1) * kConvKC);
-        if (tap == 6 && slice + 1 < nslices) next_band = slice + 1;
-        const int dy = tap / 3, dx = tap - dy * 3;
-        // B fragment rows bp = (wr + dy) * BW + dx + 16 j + pl: all fragments
-        // of a tap share (bp & 7), so one swizzled slot per k step serves all j
-        const int bp0 = (wr + dy) * BW + dx + pl;
-        const int b_x = bp0 & 7;
+    for (int dx = 0; dx < 3; ++dx) {
+      // B fragment rows bp = (wr + dy) * BW + dx + 16 j + pl: all fragments
+      // of a tap share (bp & 7), so one swizzled slot per k step serves all j
+      const int bp0 = (wr + dy) * BW + dx + pl;
+      const int b_x = bp0 & 7;
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          bf16x8 af[kConvCG], bfr[TG];
-          const int bslot = (ks * 4 + kg) ^ b_x;
+      for (int ks = 0; ks < 2; ++ks) {
+        bf16x8 af[kConvCG], bfr[TG];
+        const int bslot = (ks * 4 + kg) ^ b_x;
 #pragma unroll
-          for (int i = 0; i < kConvCG; ++i)
-            af[i] = __builtin_bit_cast(bf16x8, wts[wb][sub][(a_row0 + 16 * i) * 8 + a_slot[ks]]);
+        for (int i = 0; i < kConvCG; ++i)
+          af[i] = __builtin_bit_cast(bf16x8, wts[wb][dx][(a_row0 + 16 * i) * 8 + a_slot[ks]]);
 #pragma unroll
-          for (int j = 0; j < TG; ++j) bfr[j] = __builtin_bit_cast(bf16x8, band[bb][(bp0 + 16 * j) * 8 + bslot]);
+        for (int j = 0; j < TG; ++j) bfr[j] = __builtin_bit_cast(bf16x8, band[(bp0 + 16 * j) * 8 + bslot]);
 #pragma unroll
-          for (int i = 0; i < kConvCG; ++i)
+        for (int i = 0; i < kConvCG; ++i)
 #pragma unroll
-            for (int j = 0; j < TG; ++j)
-              acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
-        }
+          for (int j = 0; j < TG; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
       }
     }
-    if (step + 1 < nsteps) store_w(wnext, wb ^ 1);
-    if (next_band >= 0) store_band(next_band & 1);
+  };
+  // Step st = 3 slice + dy (st & 1 == P): compute on weight buffer P, stage
+  // the weights of st+1 (held in wnext) into the other buffer, barrier, fetch
+  // the weights of st+3 into wnext.  Around it, the band halves of the next
+  // slice: loads at dy = 0 (rows 0-1) and dy = 1 (rows 2-3); rows 0-1 are
+  // staged at dy = 2, rows 2-3 at the next slice's dy = 0.
+  auto slice_steps = [&](int slice, uint4 (&w0)[3][W_ITERS], uint4 (&w1)[3][W_ITERS], int p) {
+    const int st = slice * 3;
+    // dy = 0
+    store_half(band_hi, 1);
+    load_half(band_lo, 0, slice + 1);
+    compute(0, p);
+    store_w(w0, p ^ 1);
     __syncthreads();
-    if (step + 3 < nsteps) load_w(wnext, step + 3);
+    load_w(w0, st + 3);
+    // dy = 1
+    load_half(band_hi, 1, slice + 1);
+    compute(1, p ^ 1);
+    store_w(w1, p);
+    __syncthreads();
+    load_w(w1, st + 4);
+    // dy = 2
+    compute(2, p);
+    store_half(band_lo, 0);
+    store_w(w0, p ^ 1);
+    __syncthreads();
+    load_w(w0, st + 5);
   };
 
-  // prologue: step 0 staged; steps 1 and 2 in registers
-  load_band(0);
+  // prologue: band rows 0-1 and the weights of step 0 staged; rows 2-3 in
+  // registers (staged at the first step); steps 1 and 2 in registers
+  load_half(band_lo, 0, 0);
+  load_half(band_hi, 1, 0);
   load_w(w_regB, 0);
-  store_band(0);
+  store_half(band_lo, 0);
   store_w(w_regB, 0);
-  if (nsteps > 1) load_w(w_regA, 1);
-  if (nsteps > 2) load_w(w_regB, 2);
+  load_w(w_regA, 1);
+  load_w(w_regB, 2);
   __syncthreads();
-  for (int step = 0; step < nsteps; step += 2) {
-    do_step(step, w_regA);
-    if (step + 1 < nsteps) do_step(step + 1, w_regB);
+  // slice pairs: the first slice of a pair starts at an even step (weights
+  // of its steps st+1, st+3 in A; st+2 in B), the second at an odd one
+  int slice = 0;
+  for (; slice + 1 < nslices; slice += 2) {
+    slice_steps(slice, w_regA, w_regB, 0);
+    slice_steps(slice + 1, w_regB, w_regA, 1);
   }
+  if (slice < nslices) slice_steps(slice, w_regA, w_regB, 0);
 
   // -------- epilogue: lane holds channels m0 + wn*CW + i*16 + 4*(lane/16) + 0..3 of one pixel
   const int r = pr0 + wr;

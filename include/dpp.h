@@ -154,7 +154,9 @@ int dpp_groupnorm_silu_stale(void* y, float* stats_out, const void* x,
  *   weight     [Cout,3,3,Cin] (dtype)   bias [Cout] float32 or NULL
  *   y          [B,rows,W,Cout]; must not overlap any input
  *   bf16 requires Cin % 64 == 0, Cout % 16 == 0 and 16-byte aligned x,
- *   stale_full, weight, y.  f32 has no divisibility requirement.
+ *   stale_full, weight, y (else DPP_ERR_UNSUPPORTED / DPP_ERR_ALIGN), and
+ *   (Cout + 128) * 9 * Cin * 2 < 2^31 (32-bit weight offsets; else
+ *   DPP_ERR_UNSUPPORTED).  f32 has no divisibility requirement.
  */
 int dpp_conv3x3_halo(void* y, const void* x, const void* stale_full,
                      const void* weight, const float* bias, int64_t B,

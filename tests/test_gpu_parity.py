@@ -186,6 +186,7 @@ RAGGED_CONV = [
     Config("cv_w37", B=2, H=12, W=37, C=192, P=4, G=8, heads=3, D=64),  # 64-column tiles + tail, 192 channels
     Config("cv_f32", B=2, H=6, W=7, C=12, P=3, G=3, heads=1, D=12, dtype="f32"),
     Config("cv_one", B=1, H=5, W=9, C=64, P=1, G=8, heads=1, D=64),     # whole image, no stale
+    Config("cv_c320", B=1, H=8, W=48, C=320, P=2, G=32, heads=5, D=64),  # 5 input slices (odd), 48-column tiles
 ]
 
 
