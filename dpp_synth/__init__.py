@@ -52,6 +52,7 @@ STREAMS = {
     "b_qkvo": 17,     # projection biases [4,C], weight_std * N(0,1)
     "kv_stale": 18,   # the previous step's projected K and V of the image [B,N,2C]
     "relmae_trace": 19,  # per-step discrepancy trace: shape draws and noise
+    "x_steps": 20,    # per-step drift of the component chain's input
 }
 
 
@@ -237,6 +238,24 @@ def cfg_inputs(cfg: Config, latent: Optional[Tuple[int, int, int]] = None, n: Op
     u = normal(cfg.seed, "eps_u", (n,))
     c = u + np.float32(cfg.cfg_sigma) * normal(cfg.seed, "eps_c_noise", (n,))
     return {"eps_u": store(cfg, u), "eps_c": store(cfg, c)}
+
+
+def component_chain_inputs(cfg: Config, K: int, T: int) -> dict:
+    """Inputs of a chain of K full-image components over T denoising steps.
+
+    xs: T inputs [B,H,W,C] of the first component, x_t = x + stale_sigma * t *
+    N(0,1) (consecutive steps close, as the component scheme assumes); params:
+    per component the GroupNorm affine and conv weights of layer_inputs with
+    seed cfg.seed + k + 1.  Storage format."""
+    B, H, W, C = cfg.B, cfg.H, cfg.W, cfg.C
+    x = normal(cfg.seed, "x", (B, H, W, C))
+    d = normal(cfg.seed, "x_steps", (B, H, W, C))
+    xs = [store(cfg, x + np.float32(cfg.stale_sigma * t) * d) for t in range(T)]
+    params = []
+    for k in range(K):
+        li = layer_inputs(cfg.replace(seed=cfg.seed + k + 1))
+        params.append({n: li[n] for n in ("gamma", "beta", "conv_w", "conv_b")})
+    return {"xs": xs, "params": params}
 
 
 def relmae_trace(seed: int, T: int, noise: float = 0.0) -> np.ndarray:

@@ -19,6 +19,9 @@ page titles are those of the reference pages):
   and DistriGroupNorm (sections on conv, attention and normalisation layer
   splitting), and the gather of patch outputs concatenated along the height
   axis into a reused full-image buffer (section on communication).
+* "AsyncDiff abstract" -- arxivdaily.com summary and abstract of arXiv 2406.06911:
+  the noise-prediction model split into components on separate devices, each
+  fed the previous step's hidden state of the component before it.
 * "Hybridiff technical summary" -- gist.science summary of arXiv 2602.21760,
   section 2A (conditional and unconditional CFG branches as parallel units) and
   2B (denoising discrepancy: relative error rel-MAE between the conditional and
@@ -51,6 +54,9 @@ Readings where the pages are silent (each also listed in the design notes):
       fastest decline so far; the parallel stage ends at the first later step
       whose discrepancy exceeds (1 + eps) times that stage's running minimum
       (rho = 0.25, eps = 0.02 by default).
+  R14 component step: a component is the full-image block (P = 1) GN -> conv
+      -> attention with identity projections; its input after the warm-up is
+      the previous step's stored output of the component before it.
 """
 from .dpp_oracle import (  # noqa: F401
     bf16_round,
@@ -68,4 +74,6 @@ from .dpp_oracle import (  # noqa: F401
     projected_attention,
     previous_step_state,
     displaced_block,
+    component_block,
+    async_component_chain,
 )

@@ -379,3 +379,51 @@ def displaced_block(x_fresh, state, gamma, beta, weight, bias, P: int, p: int, G
     o = self_attn_displaced(q, kvt, kvt, heads, rows=attn_rows)
     return {"y1": y1, "y2": y2, "kv": kv, "y1_exact": y1_exact, "y2_exact": y2_exact, "kv_exact": kv_exact,
             "o": o, "stats": fresh}
+
+
+# ------------------------------------------------------------------ next-4: component steps
+def component_block(x, gamma, beta, weight, bias, G: int, heads: int, eps: float, bf16: bool):
+    """One full-image component (one patch, P = 1): GroupNorm -> conv ->
+    self-attention with identity projections, Q = K = V = the conv output.
+
+    x [B,H,W,C].  Each stored layer output is rounded to bf16 for bf16
+    configurations (reading R6); each stage is computed from the previous
+    stage's stored values.  Returns y1, y2, o (stored; o as [B,H,W,C]) and
+    y1_exact, y2_exact, o_exact."""
+    xv = _f64(x)
+    B, H, W, C = xv.shape
+    y1_exact, _ = groupnorm_stale(xv, None, gamma, beta, H, G, 0, eps)
+    y1 = _store(y1_exact, bf16)
+    y2_exact = conv3x3_halo(y1, None, weight, bias, 0)
+    y2 = _store(y2_exact, bf16)
+    t = y2.reshape(B, H * W, C)
+    o_exact = self_attn_displaced(t, t, t, heads).reshape(B, H, W, C)
+    o = _store(o_exact, bf16)
+    return {"y1": y1, "y2": y2, "o": o, "y1_exact": y1_exact, "y2_exact": y2_exact, "o_exact": o_exact}
+
+
+def async_component_chain(xs, params, G: int, heads: int, eps: float, bf16: bool, warmup: int = 1):
+    """Asynchronous denoising over a chain of components (AsyncDiff abstract):
+    the noise-prediction model is cut into K components, one
+    per device, and from the end of the warm-up on, component k at step t
+    takes the output component k-1 produced at step t-1 (consecutive steps'
+    hidden states being close), so all components run at once.  During the
+    first `warmup` steps the chain runs in order within the step.
+
+    xs: T inputs of component 0; params: K dicts gamma, beta, conv_w, conv_b.
+    Returns outs[t][k] = component_block(...) of component k at step t."""
+    T, K = len(xs), len(params)
+    outs = []
+    for t in range(T):
+        row = []
+        for k in range(K):
+            if k == 0:
+                src = xs[t]
+            elif t < warmup:
+                src = row[k - 1]["o"]
+            else:
+                src = outs[t - 1][k - 1]["o"]
+            p = params[k]
+            row.append(component_block(src, p["gamma"], p["beta"], p["conv_w"], p["conv_b"], G, heads, eps, bf16))
+        outs.append(row)
+    return outs

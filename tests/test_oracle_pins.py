@@ -618,3 +618,65 @@ def test_schedule_is_causal():
         for n in (1, 7, 23, 41, 60):
             assert (oracle.hybrid_schedule(d[:n])[0] == full[:n]).all()
         assert (np.diff(full) >= 0).all()
+
+
+# ----------------------------------------------------------------- component steps (R14)
+def _chain_params(K, C, rng):
+    return [{"gamma": 1 + 0.1 * rng.standard_normal(C), "beta": 0.1 * rng.standard_normal(C),
+             "conv_w": 0.2 * rng.standard_normal((C, 3, 3, C)), "conv_b": 0.1 * rng.standard_normal(C)}
+            for _ in range(K)]
+
+
+def _torch_seq(torch, x, params, k, G, heads):
+    # components 0..k applied in order with torch's own layers, as [B,H,W,C]
+    B, H, W, C = x.shape
+    for p in params[:k + 1]:
+        _, _, o = _torch_block_full(torch, x, p["gamma"], p["beta"], p["conv_w"], p["conv_b"], G, heads, 1e-5)
+        x = o.reshape(B, H, W, C)
+    return x
+
+
+def test_component_block_is_torch_block(torch_cpu):
+    B, H, W, C, G, heads = 2, 6, 5, 8, 4, 2
+    x = RNG.standard_normal((B, H, W, C))
+    p = _chain_params(1, C, RNG)[0]
+    a1, a2, o = _torch_block_full(torch_cpu, x, p["gamma"], p["beta"], p["conv_w"], p["conv_b"], G, heads, 1e-5)
+    r = oracle.component_block(x, p["gamma"], p["beta"], p["conv_w"], p["conv_b"], G, heads, 1e-5, bf16=False)
+    np.testing.assert_allclose(r["y1"], a1, rtol=0, atol=1e-11)
+    np.testing.assert_allclose(r["y2"], a2, rtol=0, atol=1e-10)
+    np.testing.assert_allclose(r["o"], o.reshape(B, H, W, C), rtol=0, atol=1e-10)
+
+
+@pytest.mark.parametrize("warmup", [1, 2, 5])
+def test_async_chain_closed_form(torch_cpu, warmup):
+    # Component k at step t sees the input of step s = t while t < warmup and
+    # s = max(t - k, warmup - 1) afterwards: the chain's output equals the
+    # ordinary model (components 0..k in order, torch layers) applied to x_s.
+    # warmup >= T is the synchronous model at every step.
+    B, H, W, C, G, heads, K, T = 1, 5, 4, 8, 4, 2, 3, 5
+    base = RNG.standard_normal((B, H, W, C))
+    xs = [base + 0.3 * t * RNG.standard_normal((B, H, W, C)) for t in range(T)]
+    params = _chain_params(K, C, RNG)
+    outs = oracle.async_component_chain(xs, params, G, heads, 1e-5, bf16=False, warmup=warmup)
+    for t in range(T):
+        for k in range(K):
+            s = t if t < warmup else max(t - k, warmup - 1)
+            want = _torch_seq(torch_cpu, xs[s], params, k, G, heads)
+            np.testing.assert_allclose(outs[t][k]["o"], want, rtol=0, atol=1e-9, err_msg=f"t={t} k={k}")
+    # the inputs really differ from step to step, so the pin sees the shift
+    assert np.abs(_torch_seq(torch_cpu, xs[1], params, 2, G, heads)
+                  - _torch_seq(torch_cpu, xs[0], params, 2, G, heads)).max() > 1e-3
+
+
+def test_async_chain_bf16_rounds_every_stored_output():
+    B, H, W, C, G, heads = 1, 4, 4, 64, 8, 1
+    xs = [oracle.bf16_round(RNG.standard_normal((B, H, W, C))) for _ in range(2)]
+    params = _chain_params(2, C, RNG)
+    for p in params:
+        p["conv_w"] = p["conv_w"] / 20     # soft attention weights: outputs are not single V rows
+    outs = oracle.async_component_chain(xs, params, G, heads, 1e-5, bf16=True)
+    for row in outs:
+        for r in row:
+            for n in ("y1", "y2", "o"):
+                assert np.array_equal(r[n], oracle.bf16_round(r[n]))
+                assert np.abs(r[n] - r[n + "_exact"]).max() > 0
