@@ -252,6 +252,7 @@ def main():
         kernels = time_kernels(cfg, layer, x_patches, gamma, beta, w, b, eps, rel, eps_c, eps_u, cfg_ws, dpp, torch)
         if cfg.dtype == "bf16":
             kernels.update(time_projections(cfg, layer, x_patches, gamma, beta, dpp, torch))
+            kernels.update(time_component(dpp, torch))
 
     out = {
         "metric": "displaced-attn + halo-conv TFLOP/s (% bf16 MFMA peak); ms per patch-layer step",
@@ -399,6 +400,44 @@ def time_projections(cfg, layer, x_patches, gamma, beta, dpp, torch, reps=10):
         rate = amount / (ms * 1e-3) / (1e12 if unit == "TFLOP/s" else 1e9)
         res[k] = {"median_ms": round(ms, 5), unit: round(rate, 2), "frac_peak": round(rate / peak, 4), "work": amount}
     return res
+
+
+def time_component(dpp, torch, reps=10):
+    """One full-image component of the asynchronous component chain (one
+    device's work per step when the model is cut into components): GroupNorm
+    -> conv -> self-attention over all tokens, at the 2048 px level
+    (128 x 128 x 640, 16384 tokens; not part of the headline step)."""
+    from dpp_synth import CONFIGS, component_chain_inputs
+    from displaced_patch_parallelism_net_amd.step import ComponentChain
+    cfg = CONFIGS["sdxl_2048"]
+    inp = component_chain_inputs(cfg, 1, 1)
+
+    def dev(a):
+        if a.dtype == np.uint16:
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+        return torch.from_numpy(a).cuda()
+
+    p = inp["params"][0]
+    params = [(dev(p["gamma"]), dev(p["beta"]), dev(p["conv_w"]), dev(p["conv_b"]))]
+    x = dev(inp["xs"][0])
+    chain = ComponentChain(1, cfg.B, cfg.H, cfg.W, cfg.C, cfg.G, cfg.heads, torch.bfloat16, eps=cfg.gn_eps,
+                           head_dim=cfg.D)
+    chain.step(x, params, synchronous=True)
+    torch.cuda.synchronize()
+    ev = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        chain.step(x, params, synchronous=True)
+        e1.record()
+        ev.append((e0, e1))
+    torch.cuda.synchronize()
+    ms = float(np.median([a.elapsed_time(b_) for a, b_ in ev]))
+    N = cfg.H * cfg.W
+    work = 2.0 * cfg.B * N * cfg.C * 9 * cfg.C + 4.0 * cfg.B * cfg.heads * N * N * cfg.D
+    rate = work / (ms * 1e-3) / 1e12
+    return {"component_step_2048": {"median_ms": round(ms, 5), "TFLOP/s": round(rate, 2),
+                                    "frac_peak": round(rate / PEAK_BF16_TFLOPS, 4), "work": work}}
 
 
 def hbm_sweep(cfg, dpp, torch, reps=20):

@@ -77,3 +77,57 @@ class DisplacedLayer:
         L.dpp_self_attn_displaced(self.o, self.y2.view(self.B, self.R * self.W, self.C), kv, kv,
                                   self.heads, self.D, 0.0, self.attn_ws)
         return self.o
+
+
+class ComponentChain:
+    """Asynchronous denoising over K full-image components (AsyncDiff
+    abstract): the noise-prediction model is cut into components, one per
+    device; after the warm-up, component k at step t consumes the output that
+    component k-1 produced at step t-1, so on K devices all components run at
+    once.  One device's work per step is one component: GroupNorm -> 3x3 conv
+    -> self-attention over the whole image (one patch, identity projections,
+    Q = K = V = the conv output), through the same kernels as the displaced
+    layer.  This class runs the K components of a step one after the other on
+    the current stream; outputs are kept per component for the next step.
+    """
+
+    def __init__(self, K, B, H, W, C, G, heads, dtype, device="cuda", eps=1e-5, head_dim=64):
+        self.K, self.B, self.H, self.W, self.C, self.G = K, B, H, W, C, G
+        self.heads, self.D, self.eps = heads, head_dim, eps
+        act = dict(dtype=dtype, device=device)
+        self.y1 = [torch.empty(B, H, W, C, **act) for _ in range(K)]
+        self.y2 = [torch.empty(B, H, W, C, **act) for _ in range(K)]
+        self.out = [torch.empty(B, H, W, C, **act) for _ in range(K)]     # this step
+        self.prev = [torch.empty(B, H, W, C, **act) for _ in range(K)]    # previous step
+        self._stats = torch.empty(B, 1, G, 2, dtype=torch.float32, device=device)
+        gw = L.dpp_groupnorm_stale_workspace_bytes(B, H, W, C, G)
+        self.gn_ws = torch.empty(max(gw, 256), dtype=torch.uint8, device=device)
+        aw = L.dpp_self_attn_workspace_bytes(B, H * W, H * W, heads, head_dim,
+                                             L.DPP_BF16 if dtype == torch.bfloat16 else L.DPP_F32)
+        self.attn_ws = torch.empty(aw, dtype=torch.uint8, device=device) if aw else None
+        self._steps = 0
+
+    def component(self, k, x, gamma, beta, weight, bias):
+        """Component k on input x [B,H,W,C]; output in self.out[k]."""
+        L.dpp_groupnorm_stale(self.y1[k], self._stats, x, None, gamma, beta, self.H, self.G, 1, 0, self.eps,
+                              self.gn_ws)
+        L.dpp_conv3x3_halo(self.y2[k], self.y1[k], None, weight, bias, self.H, 0)
+        t = self.y2[k].view(self.B, self.H * self.W, self.C)
+        L.dpp_self_attn_displaced(self.out[k].view(self.B, self.H * self.W, self.C), t, t, t, self.heads, self.D,
+                                  0.0, self.attn_ws)
+        return self.out[k]
+
+    def step(self, x, params, synchronous=False):
+        """One denoising step.  params: K tuples (gamma, beta, weight, bias).
+        synchronous (the warm-up): component k takes component k-1's output
+        of this step; otherwise the one of the previous step.  Returns the
+        last component's output (valid until the next step).  The first
+        step must be synchronous: there is no previous output yet."""
+        if self._steps == 0 and not synchronous and self.K > 1:
+            raise ValueError("the first step of a component chain must be synchronous")
+        self._steps += 1
+        for k in range(self.K):
+            src = x if k == 0 else (self.out[k - 1] if synchronous else self.prev[k - 1])
+            self.component(k, src, *params[k])
+        self.out, self.prev = self.prev, self.out
+        return self.prev[self.K - 1]
