@@ -64,7 +64,7 @@ enum dpp_status {
                                where the kernel reads 16-byte vectors        */
   DPP_ERR_ALIAS = -5,       /* an output overlaps an input it may not alias  */
   DPP_ERR_WORKSPACE = -6,   /* workspace NULL or smaller than required       */
-  DPP_ERR_UNSUPPORTED = -7, /* valid shape this build has no kernel for      */
+  DPP_ERR_UNSUPPORTED = -7, /* valid shape the library has no kernel for    */
   DPP_ERR_LAUNCH = -8       /* the HIP runtime rejected a launch             */
 };
 
