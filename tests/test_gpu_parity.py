@@ -197,21 +197,27 @@ def test_conv_parity_ragged(cfg):
         _conv_case(cfg, p)
 
 
-def test_conv_ragged_cout():
-    # Cout not a multiple of the 128-channel tile, Cin != Cout
+@pytest.mark.parametrize("B,H,W,Cin,Cout,r0,R", [
+    (1, 10, 19, 64, 80, 3, 4),     # Cout not a multiple of the 128-channel tile, Cin != Cout
+    (2, 5, 1, 128, 16, 2, 1),      # one-pixel-wide image, one-row patch, the smallest Cout
+    (1, 4, 33, 192, 272, 0, 4),    # whole image without stale rows, 3 slices, 3 Cout tiles (last 16 wide)
+])
+def test_conv_ragged_cout(B, H, W, Cin, Cout, r0, R):
     dpp = _dpp()
     rng = np.random.default_rng(5)
-    B, H, W, Cin, Cout, r0, R = 1, 10, 19, 64, 80, 3, 4
-    say("conv ragged cout", Cin, Cout)
+    say("conv ragged cout", B, H, W, Cin, Cout, r0, R)
     xs = rng.standard_normal((B, H, W, Cin)).astype(np.float32)
     xp = rng.standard_normal((B, R, W, Cin)).astype(np.float32)
     wt = (0.05 * rng.standard_normal((Cout, 3, 3, Cin))).astype(np.float32)
     from dpp_synth import f32_to_bf16_bits
     xs_b, xp_b, w_b = (f32_to_bf16_bits(a) for a in (xs, xp, wt))
     y = torch.empty(B, R, W, Cout, dtype=torch.bfloat16, device="cuda")
-    dpp.dpp_conv3x3_halo(y, to_dev(xp_b, "bf16"), to_dev(xs_b, "bf16"), to_dev(w_b, "bf16"), None, H, r0)
+    whole = r0 == 0 and R == H
+    dpp.dpp_conv3x3_halo(y, to_dev(xp_b, "bf16"), None if whole else to_dev(xs_b, "bf16"), to_dev(w_b, "bf16"),
+                         None, H, r0)
     torch.cuda.synchronize()
-    want = oracle.conv3x3_halo(values("bf16", xp_b), values("bf16", xs_b), values("bf16", w_b), None, r0)
+    want = oracle.conv3x3_halo(values("bf16", xp_b), None if whole else values("bf16", xs_b), values("bf16", w_b),
+                               None, r0)
     parity(to_host(y), want, "bf16", "conv ragged cout")
 
 
