@@ -84,7 +84,36 @@ def _dtype(t):
 
 
 def _ptr(t):
-    return None if t is None else ctypes.c_void_p(t.data_ptr())
+    """Device pointer of a GPU tensor (None -> NULL).  A host tensor is
+    refused here: the kernels would dereference its address on the GPU."""
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("tensor must be on the GPU")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _same_dtype(*ts):
+    ts = [t for t in ts if t is not None]
+    if any(t.dtype != ts[0].dtype for t in ts):
+        raise TypeError("activation and weight tensors must share one dtype: " + ", ".join(str(t.dtype) for t in ts))
+
+
+def _f32(*ts):
+    import torch
+    for t in ts:
+        if t is not None and t.dtype != torch.float32:
+            raise TypeError(f"statistics, affine parameters and biases are float32, got {t.dtype}")
+
+
+def _shape(t, want, what):
+    if t is not None and tuple(t.shape) != tuple(want):
+        raise ValueError(f"{what}: shape {tuple(t.shape)}, expected {tuple(want)}")
+
+
+def _numel(t, n, what):
+    if t is not None and t.numel() != n:
+        raise ValueError(f"{what}: {t.numel()} elements, expected {n}")
 
 
 def _stream(stream):
@@ -105,8 +134,10 @@ def _contig(*ts):
 # ------------------------------------------------------------------ calls
 def dpp_splice_patch(full, patch, row0: int, stream=None):
     _contig(full, patch)
+    _same_dtype(full, patch)
     B, H, W, C = full.shape
     rows = patch.shape[1]
+    _shape(patch, (B, rows, W, C), "patch")
     _check("dpp_splice_patch", LIB.dpp_splice_patch(_ptr(full), _ptr(patch), B, H, W, C, row0, rows, _dtype(full),
                                                     _stream(stream)))
 
@@ -115,9 +146,22 @@ def dpp_groupnorm_stale_workspace_bytes(B, rows, W, C, G) -> int:
     return int(LIB.dpp_groupnorm_stale_workspace_bytes(B, rows, W, C, G))
 
 
+def _gn_args(y, stats_out, x, stale_stats, gamma, beta, P):
+    _contig(y, stats_out, x, stale_stats, gamma, beta)
+    _same_dtype(y, x)
+    _f32(stats_out, stale_stats, gamma, beta)
+    B, rows, W, C = x.shape
+    _shape(y, x.shape, "y")
+    _numel(gamma, C, "gamma")
+    _numel(beta, C, "beta")
+    for t, what in ((stats_out, "stats_out"), (stale_stats, "stale_stats")):
+        if t is not None and (t.dim() != 4 or t.shape[0] != B or t.shape[1] < P or t.shape[3] != 2):
+            raise ValueError(f"{what}: shape {tuple(t.shape)}, expected [B, P, G, 2] with B = {B}, P = {P}")
+
+
 def dpp_groupnorm_stale(y, stats_out, x, stale_stats, gamma, beta, H: int, G: int, P: int, p: int, eps: float,
                         workspace, stream=None):
-    _contig(y, stats_out, x, stale_stats, gamma, beta)
+    _gn_args(y, stats_out, x, stale_stats, gamma, beta, P)
     B, rows, W, C = x.shape
     _check("dpp_groupnorm_stale",
            LIB.dpp_groupnorm_stale(_ptr(y), _ptr(stats_out), _ptr(x), _ptr(stale_stats), _ptr(gamma), _ptr(beta), B, H,
@@ -128,7 +172,7 @@ def dpp_groupnorm_stale(y, stats_out, x, stale_stats, gamma, beta, H: int, G: in
 
 def dpp_groupnorm_silu_stale(y, stats_out, x, stale_stats, gamma, beta, H: int, G: int, P: int, p: int, eps: float,
                              workspace, stream=None):
-    _contig(y, stats_out, x, stale_stats, gamma, beta)
+    _gn_args(y, stats_out, x, stale_stats, gamma, beta, P)
     B, rows, W, C = x.shape
     _check("dpp_groupnorm_silu_stale",
            LIB.dpp_groupnorm_silu_stale(_ptr(y), _ptr(stats_out), _ptr(x), _ptr(stale_stats), _ptr(gamma), _ptr(beta),
@@ -142,6 +186,8 @@ def dpp_linear(y, x, w, bias=None, stream=None):
     [M,N] or [B,M,N] may be strided views (last dimension contiguous), e.g. y
     a row band of a larger K/V buffer; w [N,K] contiguous; bias [N] float32."""
     _contig(w, bias)
+    _same_dtype(y, x, w)
+    _f32(bias)
     x3 = x if x.dim() == 3 else x.unsqueeze(0)
     y3 = y if y.dim() == 3 else y.unsqueeze(0)
     B, M, K = x3.shape
@@ -150,14 +196,21 @@ def dpp_linear(y, x, w, bias=None, stream=None):
         raise ValueError(f"shape mismatch: x {tuple(x3.shape)}, w {tuple(w.shape)}, y {tuple(y3.shape)}")
     if x3.stride(2) != 1 or y3.stride(2) != 1:
         raise ValueError("last dimension of x and y must be contiguous")
+    _numel(bias, N, "bias")
     _check("dpp_linear", LIB.dpp_linear(_ptr(y3), _ptr(x3), _ptr(w), _ptr(bias), B, M, K, N, x3.stride(1),
                                         x3.stride(0), y3.stride(1), y3.stride(0), _dtype(x), _stream(stream)))
 
 
 def dpp_conv3x3_halo(y, x, stale_full, weight, bias, H: int, row0: int, stream=None):
     _contig(y, x, stale_full, weight, bias)
+    _same_dtype(y, x, stale_full, weight)
+    _f32(bias)
     B, rows, W, Cin = x.shape
     Cout = weight.shape[0]
+    _shape(weight, (Cout, 3, 3, Cin), "weight")
+    _shape(y, (B, rows, W, Cout), "y")
+    _shape(stale_full, (B, H, W, Cin), "stale_full")
+    _numel(bias, Cout, "bias")
     _check("dpp_conv3x3_halo",
            LIB.dpp_conv3x3_halo(_ptr(y), _ptr(x), _ptr(stale_full), _ptr(weight), _ptr(bias), B, H, W, Cin, Cout, row0,
                                 rows, _dtype(x), _stream(stream)))
@@ -174,8 +227,15 @@ def dpp_self_attn_displaced(o, q, k, v, heads: int, head_dim: int = 64, scale: f
     for t in (o, q, k, v):
         if t.stride(2) != 1 or t.stride(0) != t.shape[1] * t.stride(1):
             raise ValueError("attention tensors must be [B,N,ld] row-major with unit channel stride")
+    _same_dtype(o, q, k, v)
     B, n_q = q.shape[0], q.shape[1]
     n_kv = k.shape[1]
+    hd = heads * head_dim
+    if tuple(o.shape[:2]) != (B, n_q) or tuple(k.shape[:2]) != (B, n_kv) or tuple(v.shape[:2]) != (B, n_kv):
+        raise ValueError(f"shape mismatch: o {tuple(o.shape)}, q {tuple(q.shape)}, k {tuple(k.shape)}, "
+                         f"v {tuple(v.shape)}")
+    if min(o.shape[2], q.shape[2], k.shape[2], v.shape[2]) < hd or k.stride(1) != v.stride(1):
+        raise ValueError(f"rows must hold heads * head_dim = {hd} channels, k and v one row stride")
     _check("dpp_self_attn_displaced",
            LIB.dpp_self_attn_displaced(_ptr(o), _ptr(q), _ptr(k), _ptr(v), B, n_q, n_kv, heads, head_dim, q.stride(1),
                                        k.stride(1), o.stride(1), scale, _ptr(workspace),
@@ -189,7 +249,11 @@ def dpp_cfg_combine_workspace_bytes(n) -> int:
 
 def dpp_cfg_combine_relmae(eps, relmae, eps_c, eps_u, guidance: float, workspace=None, stream=None):
     _contig(eps, eps_c, eps_u)
+    _same_dtype(eps, eps_c, eps_u)
+    _f32(relmae)
     n = eps_c.numel()
+    _numel(eps, n, "eps")
+    _numel(eps_u, n, "eps_u")
     _check("dpp_cfg_combine_relmae",
            LIB.dpp_cfg_combine_relmae(_ptr(eps), _ptr(relmae), _ptr(eps_c), _ptr(eps_u), n, guidance, _ptr(workspace),
                                       0 if workspace is None else workspace.numel() * workspace.element_size(),

@@ -231,3 +231,39 @@ def test_linear_validation():
     assert lin(y=Cp + 64) == ALIAS                 # inside the weights
     # f32: no divisibility or alignment requirement beyond the shapes
     assert lin(K=60, ldx=60, N=62, ldy=62, bsx=6000, bsy=6200, dtype=F32, w=None) == NULL
+
+
+# ----------------------------------------------------------------- binding checks (no GPU needed)
+def test_binding_refuses_host_tensors_and_mismatches():
+    import torch
+    bf = torch.bfloat16
+    full, patch = torch.zeros(1, 8, 4, 16, dtype=bf), torch.zeros(1, 2, 4, 16, dtype=bf)
+    with pytest.raises(ValueError, match="GPU"):
+        dpp.dpp_splice_patch(full, patch, 0)
+    with pytest.raises(ValueError, match="patch"):
+        dpp.dpp_splice_patch(full, torch.zeros(1, 2, 4, 8, dtype=bf), 0)
+    with pytest.raises(TypeError):
+        dpp.dpp_splice_patch(full, patch.float(), 0)
+    x, w = torch.zeros(1, 2, 4, 64, dtype=bf), torch.zeros(64, 3, 3, 64, dtype=bf)
+    with pytest.raises(ValueError, match="weight"):
+        dpp.dpp_conv3x3_halo(torch.zeros(1, 2, 4, 64, dtype=bf), x, None, torch.zeros(64, 2, 3, 64, dtype=bf), None, 2, 0)
+    with pytest.raises(ValueError, match="y"):
+        dpp.dpp_conv3x3_halo(torch.zeros(1, 2, 4, 32, dtype=bf), x, None, w, None, 2, 0)
+    with pytest.raises(TypeError):
+        dpp.dpp_conv3x3_halo(torch.zeros(1, 2, 4, 64, dtype=bf), x, None, w, torch.zeros(64, dtype=bf), 2, 0)
+    g = torch.ones(64)
+    with pytest.raises(TypeError):
+        dpp.dpp_groupnorm_stale(x.clone(), None, x, None, g.to(bf), g, 2, 8, 1, 0, 1e-5, None)
+    with pytest.raises(ValueError, match="stats_out"):
+        dpp.dpp_groupnorm_stale(x.clone(), torch.zeros(1, 1, 8, 3), x, None, g, g, 2, 8, 1, 0, 1e-5, None)
+    q, kv = torch.zeros(1, 8, 64, dtype=bf), torch.zeros(1, 16, 128, dtype=bf)
+    with pytest.raises(ValueError, match="row stride"):
+        dpp.dpp_self_attn_displaced(q.clone(), q, kv[:, :, :64], torch.zeros(1, 16, 64, dtype=bf), 1)
+    with pytest.raises(ValueError, match="shape"):
+        dpp.dpp_self_attn_displaced(torch.zeros(1, 4, 64, dtype=bf), q, kv, kv, 1)
+    with pytest.raises(ValueError, match="eps"):
+        dpp.dpp_cfg_combine_relmae(torch.zeros(10, dtype=bf), None, torch.zeros(12, dtype=bf),
+                                   torch.zeros(12, dtype=bf), 7.5)
+    with pytest.raises(ValueError, match="bias"):
+        dpp.dpp_linear(torch.zeros(4, 8, dtype=bf), torch.zeros(4, 16, dtype=bf), torch.zeros(8, 16, dtype=bf),
+                       torch.zeros(4))
