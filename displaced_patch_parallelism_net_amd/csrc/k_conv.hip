@@ -13,9 +13,9 @@
 // the tiles cover the rows exactly where possible: 240 columns -> 3 tiles of
 // 80, one workgroup per CU).  For each 64-channel slice of Cin the halo band
 // (4 rows x 16*TG+2 columns, halo rows from the stale image) is staged once in
-// LDS and reused by all nine taps; the weights of one tap are staged per
-// step; both double-buffered in LDS, weights fetched two steps ahead into
-// registers.  Eight waves (two per SIMD) each compute 32 channels x 16*TG
+// LDS and reused by all nine taps; one barrier step covers the three taps of
+// one kernel row, whose weights are double-buffered in LDS and fetched two
+// steps ahead into registers.  Eight waves (two per SIMD) each compute 32 channels x 16*TG
 // pixels of one tile row with v_mfma_f32_16x16x32_bf16; the accumulator's
 // lane layout gives each lane four consecutive output channels of one pixel,
 // stored as one 8-byte write.
