@@ -337,11 +337,13 @@ def time_kernels(cfg, layer, x_patches, gamma, beta, w, b, eps, rel, eps_c, eps_
     }
     res = {}
     for k, lst in ev.items():
-        ms = float(np.mean([a.elapsed_time(b_) for a, b_ in lst]))
+        t = np.array([a.elapsed_time(b_) for a, b_ in lst])
+        ms = float(np.mean(t))
         amount, unit, peak = work[k]
         rate = amount / (ms * 1e-3) / (1e12 if unit == "TFLOP/s" else 1e9)
-        res[k] = {"avg_ms": round(ms, 5), unit: round(rate, 2), "frac_peak": round(rate / peak, 4),
-                  "work": amount}
+        res[k] = {"avg_ms": round(ms, 5), "median_ms": round(float(np.median(t)), 5),
+                  "p10_ms": round(float(np.percentile(t, 10)), 5), "p90_ms": round(float(np.percentile(t, 90)), 5),
+                  "calls": int(t.size), unit: round(rate, 2), "frac_peak": round(rate / peak, 4), "work": amount}
     return res
 
 
