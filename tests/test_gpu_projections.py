@@ -40,6 +40,9 @@ def _rand(rng, shape, dtype, scale=1.0):
 # (name, B, M, K, N, ld_x, ld_y, bias, dtype): ragged M/N/K tails, strided rows
 LINEAR_CASES = [
     ("tokens_1024", 1, 1024, 640, 640, 640, 640, True, "bf16"),
+    ("tokens_7200", 1, 7200, 640, 640, 640, 640, True, "bf16"),      # the 3840 px patch, as timed
+    ("kv_7200_k1280", 1, 7200, 1280, 1280, 1280, 1280, True, "bf16"),  # K = 1280: the 20-slice unrolled path
+    ("k320", 1, 517, 320, 192, 320, 192, True, "bf16"),                # K = 320: the 5-slice unrolled path
     ("kv_1280", 1, 1000, 640, 1280, 640, 1280, True, "bf16"),
     ("ragged_strided", 2, 301, 200, 84, 208, 96, True, "bf16"),
     ("no_bias", 1, 130, 64, 128, 64, 128, False, "bf16"),
