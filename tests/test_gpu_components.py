@@ -7,11 +7,15 @@ Two checks per step and component:
   the same component on the buffer it should have read (this step's output
   of the component before it during the warm-up, the previous step's after);
 * numerics against the oracle's chain on the same seeded inputs: every stage
-  of the fp32 chain, and in bf16 the first component of every step, whose
-  input bits are the seeded ones.  (A later bf16 component reads a bf16
-  tensor that the device and the oracle round independently; a one-ulp
-  difference there is amplified by its GroupNorm's 1/sigma, so the
-  single-operation bar does not apply to it.)
+  of the fp32 chain; in bf16 the GroupNorm (input: the seeded bits) and the
+  conv of the first component of every step.  A bf16 stage fed by a stored
+  bf16 tensor that the device and the oracle round independently is not
+  held to the single-operation bar where it is ill-conditioned: a later
+  component's GroupNorm scales one-ulp input differences by 1/sigma, and the
+  self-attention (Q = K = V) moves by up to 12% of its output RMS when 10%
+  of its input elements flip by one ulp (the oracle against itself).  The
+  attention's numerics are checked where its inputs are the seeded bits
+  (tests/test_gpu_parity.py).
 Each test prints the case it runs before touching the GPU."""
 import numpy as np
 import pytest
@@ -78,7 +82,8 @@ def test_component_chain_parity(cfg, K, T, warmup):
             tag = f"chain {cfg.name} t{t} k{k}"
             parity(to_host(chain.y1[k]), w["y1_exact"], cfg.dtype, tag + " GN")
             parity(to_host(chain.y2[k]), w["y2_exact"], cfg.dtype, tag + " conv")
-            parity(to_host(chain.prev[k]), w["o_exact"], cfg.dtype, tag + " attention")
+            if not bf:
+                parity(to_host(chain.prev[k]), w["o_exact"], cfg.dtype, tag + " attention")
 
 
 def test_component_chain_first_step_must_be_synchronous():
