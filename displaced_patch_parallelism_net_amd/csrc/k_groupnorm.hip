@@ -5,32 +5,26 @@
 // raw sums (sum x, sum x^2) from the previous step plus the own patch's fresh
 // sums (DistriFusion reading notes, Introduction, fourth paragraph).
 //
-// Two launches, both deterministic (no atomics):
+// Three launches, all deterministic (no atomics):
 //   1. partial: workgroup (chunk, b) sums its pixels per channel in float32
 //      registers (each thread owns one 16-byte channel vector and walks
-//      pixels, eight loads in flight), folds channels into groups through
-//      LDS in a fixed order and writes one (s1, s2) per group to the
-//      workspace;
-//   2. apply: every workgroup first adds the chunk partials of its batch
-//      entry in float64, in one fixed order (gn_totals), and the other
-//      patches' stale sums, giving mean/rstd per group -- the same values in
-//      every workgroup; workgroup 0 of each b writes the fresh sums to
-//      stats_out[b,p].  Then y = x * a_c + b_c with a_c = rstd_g gamma_c,
-//      b_c = beta_c - mean_g a_c (then SiLU when asked: the GroupNorm + SiLU
-//      pair opening an SDXL residual block); one 16-byte load and one
-//      streaming store per vector.
-// The partial chunks per b are capped (kGnChunksPerB) so that the per-
-// workgroup totals stay a few KB of L2 reads.  A statistics-only call
-// (y == NULL) runs the partial pass and a one-workgroup finalize with the
-// same totals code.  The second read of x normally hits the 256 MB
-// last-level cache.
+//      pixels, eight loads in flight), folds channels into groups through LDS in a fixed order and
+//      writes one (s1, s2) per group to the workspace;
+//   2. finalize: one workgroup per b adds the chunk partials in float64 (fixed
+//      order), adds the other patches' stale sums, writes the fresh sums to
+//      stats_out[b,p] and mean/rstd to the workspace;
+//   3. apply: y = x * a_c + b_c with a_c = rstd_g gamma_c, b_c = beta_c -
+//      mean_g a_c (then SiLU when asked: the GroupNorm + SiLU pair opening
+//      an SDXL residual block); one 16-byte load and one streaming store per
+//      vector.
+// The second read of x (step 3) normally hits the 256 MB last-level cache.
 #include "dpp_common.h"
 
 namespace dpp {
 
 constexpr int kGnMaxThreads = 256;
+constexpr int kGnFinThreads = 1024;  // finalize: threads per batch entry
 constexpr int kGnStatChunks = 256;    // total partial workgroups (over B)
-constexpr int kGnChunksPerB = 64;     // at most this many partial chunks per batch entry
 constexpr int kGnApplyChunks = 1024;  // total apply workgroups (over B)
 constexpr int kGnInFlight = 8;        // 16-byte loads in flight per thread
 
@@ -54,7 +48,6 @@ static GnGeom gn_geom(int64_t B, int64_t rows, int64_t W, int64_t C, bool bf16) 
   g.npix = rows * W;
   const int64_t maxc = ceil_div(g.npix, g.KP);
   int64_t want = ceil_div(kGnStatChunks, B);
-  if (want > kGnChunksPerB) want = kGnChunksPerB;
   g.nstat = want < maxc ? want : maxc;
   if (g.nstat < 1) g.nstat = 1;
   g.stat_ppc = ceil_div(g.npix, g.nstat);
@@ -137,30 +130,36 @@ __global__ __launch_bounds__(kGnMaxThreads) void gn_partial_kernel(const T* __re
   }
 }
 
-// Group totals of batch entry b over the nchunk partials, in one fixed order
-// for every caller: thread t of the kGnMaxThreads-thread block owns group
-// t % G and chunks part, part + nparts, ... (part = t / G, nparts =
-// kGnMaxThreads / G), summed in float64 with up to kGnTotLoads loads issued
-// together; thread g < G then adds the nparts part sums in order and returns
-// (s1, s2) -- meaningful for t < G only.  Every thread must call it (it
-// synchronises the block).
-constexpr int kGnTotLoads = 8;
+// Finalize: thread t of batch entry b owns group t % G and every
+// (1024/G)-th chunk from t / G; its chunk loads are all issued before they
+// are summed (up to kGnFinLoads each, else a loop), and the other patches'
+// stale sums are loaded into LDS by the same threads meanwhile.
+constexpr int kGnFinLoads = 8;
+constexpr int kGnFinStale = 2048;  // stale (q, g) pairs staged in LDS: P * G <= this
 
-__device__ double2 gn_totals(const float* __restrict__ partial, int64_t nchunk, int G, int b, double* r1,
-                             double* r2) {
+__global__ __launch_bounds__(kGnFinThreads) void gn_finalize_kernel(
+    const float* __restrict__ partial, int64_t nchunk, const float* __restrict__ stale, float* __restrict__ stats_out,
+    float* __restrict__ coef, int G, int P, int p, double n, float eps) {
+  __shared__ double r1[kGnFinThreads], r2[kGnFinThreads];
+  __shared__ float2 sst[kGnFinStale];
+  const int b = blockIdx.x;
   const int t = threadIdx.x;
-  const int nparts = kGnMaxThreads / G;  // G <= 256 (host check)
+  const int nparts = kGnFinThreads / G;  // G <= 256 (host check)
   const int g = t % G, part = t / G;
+  const bool stage_stale = stale != nullptr && coef != nullptr && P * G <= kGnFinStale;
+  if (stage_stale)
+    for (int i = t; i < P * G; i += kGnFinThreads)
+      sst[i] = *reinterpret_cast<const float2*>(stale + (static_cast<int64_t>(b) * P * G + i) * 2);
   double a = 0.0, c = 0.0;
   if (part < nparts) {
     const float* base = partial + (static_cast<int64_t>(b) * nchunk * G + g) * 2;
     int64_t ch = part;
-    for (; ch + (kGnTotLoads - 1) * nparts < nchunk; ch += kGnTotLoads * nparts) {
-      float2 v[kGnTotLoads];
+    for (; ch + (kGnFinLoads - 1) * nparts < nchunk; ch += kGnFinLoads * nparts) {
+      float2 v[kGnFinLoads];
 #pragma unroll
-      for (int j = 0; j < kGnTotLoads; ++j) v[j] = *reinterpret_cast<const float2*>(base + (ch + j * nparts) * G * 2);
+      for (int j = 0; j < kGnFinLoads; ++j) v[j] = *reinterpret_cast<const float2*>(base + (ch + j * nparts) * G * 2);
 #pragma unroll
-      for (int j = 0; j < kGnTotLoads; ++j) { a += v[j].x; c += v[j].y; }
+      for (int j = 0; j < kGnFinLoads; ++j) { a += v[j].x; c += v[j].y; }
     }
     for (; ch < nchunk; ch += nparts) {
       const float2 v = *reinterpret_cast<const float2*>(base + ch * G * 2);
@@ -171,41 +170,29 @@ __device__ double2 gn_totals(const float* __restrict__ partial, int64_t nchunk, 
   r1[t] = a;
   r2[t] = c;
   __syncthreads();
-  double2 s = make_double2(0.0, 0.0);
-  if (t < G)
-    for (int q = 0; q < nparts; ++q) { s.x += r1[q * G + t]; s.y += r2[q * G + t]; }
-  return s;
-}
-
-// mean and rstd of group g from the fresh totals and the other patches'
-// stale sums (reading: biased variance, clamped at 0).
-__device__ float2 gn_mean_rstd(double2 fresh, const float* __restrict__ stale, int b, int g, int G, int P, int p,
-                               double n, float eps) {
-  double T1 = fresh.x, T2 = fresh.y;
-  if (stale != nullptr)
-    for (int q = 0; q < P; ++q)
-      if (q != p) {
-        const float2 st = *reinterpret_cast<const float2*>(stale + ((static_cast<int64_t>(b) * P + q) * G + g) * 2);
-        T1 += st.x;
-        T2 += st.y;
-      }
-  const double mean = T1 / n;
-  double var = T2 / n - mean * mean;
-  if (var < 0.0) var = 0.0;
-  return make_float2(static_cast<float>(mean), static_cast<float>(1.0 / sqrt(var + static_cast<double>(eps))));
-}
-
-// Statistics-only calls: one workgroup per b writes the fresh sums.
-__global__ __launch_bounds__(kGnMaxThreads) void gn_finalize_kernel(const float* __restrict__ partial, int64_t nchunk,
-                                                                    float* __restrict__ stats_out, int G, int P,
-                                                                    int p) {
-  __shared__ double r1[kGnMaxThreads], r2[kGnMaxThreads];
-  const int b = blockIdx.x;
-  const double2 s = gn_totals(partial, nchunk, G, b, r1, r2);
-  if (threadIdx.x < G) {
-    float* so = stats_out + ((static_cast<int64_t>(b) * P + p) * G + threadIdx.x) * 2;
-    so[0] = static_cast<float>(s.x);
-    so[1] = static_cast<float>(s.y);
+  if (t < G) {
+    double s1 = 0.0, s2 = 0.0;
+    for (int q = 0; q < nparts; ++q) { s1 += r1[q * G + t]; s2 += r2[q * G + t]; }
+    float* so = stats_out + ((static_cast<int64_t>(b) * P + p) * G + t) * 2;
+    so[0] = static_cast<float>(s1);
+    so[1] = static_cast<float>(s2);
+    if (coef != nullptr) {
+      double T1 = s1, T2 = s2;
+      if (stale != nullptr)
+        for (int q = 0; q < P; ++q)
+          if (q != p) {
+            const float2 st = stage_stale ? sst[q * G + t]
+                                          : *reinterpret_cast<const float2*>(stale + ((static_cast<int64_t>(b) * P + q) * G + t) * 2);
+            T1 += st.x;
+            T2 += st.y;
+          }
+      const double mean = T1 / n;
+      double var = T2 / n - mean * mean;
+      if (var < 0.0) var = 0.0;
+      const double rstd = 1.0 / sqrt(var + static_cast<double>(eps));
+      coef[(static_cast<int64_t>(b) * G + t) * 2] = static_cast<float>(mean);
+      coef[(static_cast<int64_t>(b) * G + t) * 2 + 1] = static_cast<float>(rstd);
+    }
   }
 }
 
@@ -215,40 +202,15 @@ __device__ __forceinline__ float silu_f(float z) {
   return z * __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-1.4426950408889634f * z));
 }
 
-struct GnApplyArgs {
-  const float* partial;
-  int64_t nchunk;
-  const float* stale;
-  float* stats_out;
-  const float* gamma;
-  const float* beta;
-  int G, P, p;
-  double n;
-  float eps;
-};
-
 template <typename T, bool SILU>
 __global__ __launch_bounds__(kGnMaxThreads) void gn_apply_kernel(const T* __restrict__ x, T* __restrict__ y,
-                                                                 GnApplyArgs s, int64_t npix, int C, int V, int KP,
-                                                                 int64_t ppc) {
+                                                                 const float* __restrict__ coef,
+                                                                 const float* __restrict__ gamma,
+                                                                 const float* __restrict__ beta, int64_t npix, int C,
+                                                                 int G, int V, int KP, int64_t ppc) {
   constexpr int VEC = Elem<T>::kVec;
-  __shared__ double r1[kGnMaxThreads], r2[kGnMaxThreads];
-  __shared__ float2 mr[kGnMaxThreads];  // (mean, rstd) per group
   const int b = blockIdx.y;
   const int t = threadIdx.x;
-  const int G = s.G;
-  {
-    const double2 tot = gn_totals(s.partial, s.nchunk, G, b, r1, r2);
-    if (t < G) {
-      mr[t] = gn_mean_rstd(tot, s.stale, b, t, G, s.P, s.p, s.n, s.eps);
-      if (blockIdx.x == 0) {
-        float* so = s.stats_out + ((static_cast<int64_t>(b) * s.P + s.p) * G + t) * 2;
-        so[0] = static_cast<float>(tot.x);
-        so[1] = static_cast<float>(tot.y);
-      }
-    }
-    __syncthreads();
-  }
   const int v = t % V, k = t / V;
   if (k >= KP) return;
   const int cg = C / G;
@@ -256,9 +218,10 @@ __global__ __launch_bounds__(kGnMaxThreads) void gn_apply_kernel(const T* __rest
 #pragma unroll
   for (int j = 0; j < VEC; ++j) {
     const int c = v * VEC + j;
-    const float2 m = mr[c / cg];
-    a[j] = m.y * s.gamma[c];
-    sh[j] = fmaf(-m.x, a[j], s.beta[c]);
+    const int g = c / cg;
+    const float mean = coef[(b * G + g) * 2], rstd = coef[(b * G + g) * 2 + 1];
+    a[j] = rstd * gamma[c];
+    sh[j] = fmaf(-mean, a[j], beta[c]);
   }
   const int64_t p0 = static_cast<int64_t>(blockIdx.x) * ppc;
   const int64_t p1 = (p0 + ppc < npix) ? p0 + ppc : npix;
@@ -300,37 +263,25 @@ static hipError_t gn_run(T* y, float* stats_out, const T* x, const float* stale,
                          int64_t p, int64_t rows, float eps, void* ws, bool silu, hipStream_t s) {
   const GnGeom g = gn_geom(B, rows, W, C, sizeof(T) == 2);
   float* partial = static_cast<float*>(ws);
+  float* coef = partial + B * g.nstat * G * 2;
   hipLaunchKernelGGL(gn_partial_kernel<T>, dim3(static_cast<unsigned>(g.nstat), static_cast<unsigned>(B)),
                      dim3(g.threads), 0, s, x, partial, g.npix, static_cast<int>(C), static_cast<int>(G), g.V, g.KP,
                      g.stat_ppc, g.nstat);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  if (y == nullptr) {
-    hipLaunchKernelGGL(gn_finalize_kernel, dim3(static_cast<unsigned>(B)), dim3(kGnMaxThreads), 0, s, partial,
-                       g.nstat, stats_out, static_cast<int>(G), static_cast<int>(P), static_cast<int>(p));
-    return hipGetLastError();
-  }
-  GnApplyArgs a;
-  a.partial = partial;
-  a.nchunk = g.nstat;
-  a.stale = stale;
-  a.stats_out = stats_out;
-  a.gamma = gamma;
-  a.beta = beta;
-  a.G = static_cast<int>(G);
-  a.P = static_cast<int>(P);
-  a.p = static_cast<int>(p);
-  a.n = static_cast<double>(H) * static_cast<double>(W) * static_cast<double>(C / G);
-  a.eps = eps;
-  // the apply block runs the totals with kGnMaxThreads threads (all of them
-  // take part in its barrier), whatever the vector geometry needs
+  const double n = static_cast<double>(H) * static_cast<double>(W) * static_cast<double>(C / G);
+  hipLaunchKernelGGL(gn_finalize_kernel, dim3(static_cast<unsigned>(B)), dim3(kGnFinThreads), 0, s, partial, g.nstat,
+                     stale, stats_out, y ? coef : nullptr, static_cast<int>(G), static_cast<int>(P),
+                     static_cast<int>(p), n, eps);
+  err = hipGetLastError();
+  if (err != hipSuccess || y == nullptr) return err;
   const dim3 agrid(static_cast<unsigned>(g.napply), static_cast<unsigned>(B));
   if (silu)
-    hipLaunchKernelGGL((gn_apply_kernel<T, true>), agrid, dim3(kGnMaxThreads), 0, s, x, y, a, g.npix,
-                       static_cast<int>(C), g.V, g.KP, g.apply_ppc);
+    hipLaunchKernelGGL((gn_apply_kernel<T, true>), agrid, dim3(g.threads), 0, s, x, y, coef, gamma, beta, g.npix,
+                       static_cast<int>(C), static_cast<int>(G), g.V, g.KP, g.apply_ppc);
   else
-    hipLaunchKernelGGL((gn_apply_kernel<T, false>), agrid, dim3(kGnMaxThreads), 0, s, x, y, a, g.npix,
-                       static_cast<int>(C), g.V, g.KP, g.apply_ppc);
+    hipLaunchKernelGGL((gn_apply_kernel<T, false>), agrid, dim3(g.threads), 0, s, x, y, coef, gamma, beta, g.npix,
+                       static_cast<int>(C), static_cast<int>(G), g.V, g.KP, g.apply_ppc);
   return hipGetLastError();
 }
 
