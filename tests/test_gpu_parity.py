@@ -295,6 +295,16 @@ def _attn_case(cfg, p, sample_rows=None, use_ws=True, what=""):
 ATTN_FULL = [("tiny_f32", 0), ("tiny_f32", 1), ("sdxl_1024", 2), ("cfg_pair_1024", 0)]
 
 
+@pytest.mark.parametrize("seed", [1, 2, 3])
+def test_attention_parity_other_seeds(seed):
+    # the same 1024 px workload with other seeded draws: parity does not hang
+    # on one draw
+    from dpp_synth import CONFIGS as _C
+    cfg = _C["sdxl_1024"].replace(seed=seed)
+    say("attention", cfg.name, "seed", seed, "patch", seed % cfg.P)
+    _attn_case(cfg, seed % cfg.P, what=f"seed {seed}")
+
+
 @pytest.mark.parametrize("name,p", ATTN_FULL, ids=[f"{n}-p{p}" for n, p in ATTN_FULL])
 def test_attention_parity_full(name, p):
     say("attention", name, "patch", p)
