@@ -157,6 +157,7 @@ int dpp_self_attn_displaced(void* o, const void* q, const void* k, const void* v
   if (((n_q + 255) / 256) * B * heads * 16 > 0x7fffffffLL) return DPP_ERR_UNSUPPORTED;
   if (dtype == DPP_BF16) {
     if (head_dim != 64) return DPP_ERR_UNSUPPORTED;
+    if (ld_q > (1LL << 24) || ld_kv > (1LL << 24) || ld_o > (1LL << 24)) return DPP_ERR_UNSUPPORTED;
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || ld_q % 8 || ld_kv % 8 || ld_o % 8)
       return DPP_ERR_ALIGN;
   } else if (head_dim != 16 && head_dim != 32 && head_dim != 64 && head_dim != 128) {

@@ -176,7 +176,9 @@ int dpp_conv3x3_halo(void* y, const void* x, const void* stale_full,
  *   bf16 requires head_dim == 64, 16-byte aligned pointers and ld % 8 == 0.
  *   f32 requires head_dim in {16, 32, 64, 128}.
  *   Limits (else DPP_ERR_UNSUPPORTED): B*heads <= 65535, n_q and n_kv <=
- *   2^30, ceil(n_q/256)*B*heads*16 < 2^31.
+ *   2^30, ceil(n_q/256)*B*heads*16 < 2^31; bf16 row strides ld_q, ld_kv,
+ *   ld_o <= 2^24 elements (64 key rows of K/V are addressed with 32-bit byte
+ *   offsets).
  *   workspace: optional.  With workspace_bytes >=
  *   dpp_self_attn_workspace_bytes(...) the key range may be split across
  *   workgroups and merged in a second pass (more parallelism for short query

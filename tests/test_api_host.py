@@ -157,6 +157,13 @@ def test_attention_validation():
     assert attn(ws=A, wsb=1024) == ALIAS
 
 
+def test_attention_huge_row_stride_unsupported():
+    big = (1 << 24) + 8
+    assert attn(ldkv=big) == UNSUP
+    assert attn(ldq=big) == UNSUP
+    assert attn(ldo=big) == UNSUP
+
+
 def test_attention_workspace_query():
     # short query ranges are split over the keys; the split needs workspace
     assert dpp.dpp_self_attn_workspace_bytes(1, 1024, 4096, 10, 64, BF16) > 0
