@@ -208,7 +208,10 @@ int dpp_self_attn_displaced(void* o, const void* q, const void* k,
  *   batches must not overlap (bs_y >= (M-1)*ld_y + N when B > 1).
  *   Requires ld_x >= K, ld_y >= N.  bf16 requires K % 8 == 0, N % 4 == 0,
  *   x and w 16-byte aligned, ld_x and bs_x multiples of 8, y 8-byte aligned,
- *   ld_y and bs_y multiples of 4.  Float32 accumulation, one rounding.
+ *   ld_y and bs_y multiples of 4, and 32-bit byte offsets within w and within
+ *   one batch entry of x: (N + 128) * K * 2 < 2^31 and ((M + 160) * ld_x +
+ *   K) * 2 < 2^31 - 16 (else DPP_ERR_UNSUPPORTED).  Limits for both dtypes:
+ *   B <= 65535, M, K, N <= 2^30.  Float32 accumulation, one rounding.
  */
 int dpp_linear(void* y, const void* x, const void* w, const float* bias,
                int64_t B, int64_t M, int64_t K, int64_t N, int64_t ld_x,

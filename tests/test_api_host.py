@@ -24,6 +24,13 @@ Ep = 0x50000000
 WSP = 0x60000000
 
 
+def _no_launch(rc):
+    # the helpers pass fake device addresses: every call must stop at a
+    # validation check, never at (or past) a kernel launch
+    assert rc not in (OK, -8), f"validation let a call with fake pointers through (status {rc})"
+    return rc
+
+
 def header_symbols():
     text = open(os.path.join(ROOT, "include", "dpp.h")).read()
     return sorted(set(re.findall(r"\b(dpp_[a-z0-9_]+)\s*\(", text)))
@@ -54,7 +61,7 @@ def test_version_and_strerror():
 
 # ----------------------------------------------------------------- splice
 def splice(full=A, patch=Bp, B=1, H=8, W=4, C=16, row0=0, rows=2, dtype=BF16):
-    return L.dpp_splice_patch(full, patch, B, H, W, C, row0, rows, dtype, None)
+    return _no_launch(L.dpp_splice_patch(full, patch, B, H, W, C, row0, rows, dtype, None))
 
 
 def test_splice_validation():
@@ -72,7 +79,7 @@ def test_splice_validation():
 # ----------------------------------------------------------------- GroupNorm
 def gn(y=A, so=Bp, x=Cp, st=Dp, gamma=Ep, beta=Ep + 4096, B=1, H=8, W=4, C=64, G=8, P=2, p=0, rows=4, eps=1e-5,
        ws=WSP, wsb=1 << 20, dtype=BF16):
-    return L.dpp_groupnorm_stale(y, so, x, st, gamma, beta, B, H, W, C, G, P, p, rows, eps, ws, wsb, dtype, None)
+    return _no_launch(L.dpp_groupnorm_stale(y, so, x, st, gamma, beta, B, H, W, C, G, P, p, rows, eps, ws, wsb, dtype, None))
 
 
 def test_groupnorm_validation():
@@ -100,7 +107,7 @@ def test_groupnorm_stats_only_mode_needs_no_affine():
     # y == NULL: gamma/beta/stale may be NULL; validation passes all the way
     # to the workspace check
     assert gn(y=None, gamma=None, beta=None, st=None, ws=None) == WS
-    assert gn(y=None, st=None, P=1) != NULL
+    assert gn(y=None, st=None, P=1, wsb=8) == WS   # gets past every pointer check; never reaches a launch
 
 
 def test_groupnorm_workspace_query():
@@ -111,7 +118,7 @@ def test_groupnorm_workspace_query():
 
 # ----------------------------------------------------------------- conv
 def conv(y=A, x=Bp, st=Cp, w=Dp, bias=Ep, B=1, H=8, W=16, Cin=64, Cout=64, row0=2, rows=2, dtype=BF16):
-    return L.dpp_conv3x3_halo(y, x, st, w, bias, B, H, W, Cin, Cout, row0, rows, dtype, None)
+    return _no_launch(L.dpp_conv3x3_halo(y, x, st, w, bias, B, H, W, Cin, Cout, row0, rows, dtype, None))
 
 
 def test_conv_validation():
@@ -139,7 +146,7 @@ def test_conv_whole_image_needs_no_stale():
 # ----------------------------------------------------------------- attention
 def attn(o=A, q=Bp, k=Cp, v=Dp, B=1, nq=100, nkv=300, heads=2, D=64, ldq=128, ldkv=128, ldo=128, scale=0.0, ws=None,
          wsb=0, dtype=BF16):
-    return L.dpp_self_attn_displaced(o, q, k, v, B, nq, nkv, heads, D, ldq, ldkv, ldo, scale, ws, wsb, dtype, None)
+    return _no_launch(L.dpp_self_attn_displaced(o, q, k, v, B, nq, nkv, heads, D, ldq, ldkv, ldo, scale, ws, wsb, dtype, None))
 
 
 def test_attention_validation():
@@ -174,7 +181,7 @@ def test_attention_workspace_query():
 
 # ----------------------------------------------------------------- CFG
 def cfg(eps=A, rel=Bp, c=Cp, u=Dp, n=1000, w=7.5, ws=WSP, wsb=1 << 16, dtype=BF16):
-    return L.dpp_cfg_combine_relmae(eps, rel, c, u, n, w, ws, wsb, dtype, None)
+    return _no_launch(L.dpp_cfg_combine_relmae(eps, rel, c, u, n, w, ws, wsb, dtype, None))
 
 
 def test_cfg_validation():
@@ -215,7 +222,17 @@ def test_groupnorm_silu_validation_matches_groupnorm():
 
 # ----------------------------------------------------------------- projections
 def lin(y=A, x=Bp, w=Cp, bias=Dp, B=1, M=100, K=64, N=64, ldx=64, bsx=6400, ldy=64, bsy=6400, dtype=BF16):
-    return L.dpp_linear(y, x, w, bias, B, M, K, N, ldx, bsx, ldy, bsy, dtype, None)
+    return _no_launch(L.dpp_linear(y, x, w, bias, B, M, K, N, ldx, bsx, ldy, bsy, dtype, None))
+
+
+def test_linear_32bit_offset_limits():
+    # w of 2^31 bytes and an x batch entry of 2^31 bytes need 64-bit offsets
+    assert lin(N=32768, K=32768, ldx=32768, M=10, bsx=327680, ldy=32768, bsy=327680) == UNSUP
+    assert lin(M=1 << 20, K=1024, ldx=1024, bsx=1 << 30, ldy=64, bsy=64 << 20) == UNSUP
+    # a w just inside the limit passes the size checks: with y placed inside w
+    # the aliasing check, which comes after them, is the one that answers (no
+    # host test may reach a launch: these pointers are not device memory)
+    assert lin(N=8060, K=1 << 17, ldx=1 << 17, M=4, bsx=1 << 19, ldy=8064, bsy=1 << 15, y=Cp + 64) == ALIAS
 
 
 def test_linear_validation():
