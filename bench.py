@@ -218,7 +218,7 @@ def main():
             r0 = p * layer.R
             dpp.dpp_groupnorm_stale(layer.y1, layer.stats_next, x_patches[p], layer.stats_prev, gamma, beta, cfg.H,
                                     cfg.G, cfg.P, p, cfg.gn_eps, layer.gn_ws)
-            dpp.dpp_conv3x3_halo(layer.y2, layer.y1, layer.a1, w, b, cfg.H, r0)
+            dpp.dpp_conv3x3_halo(layer.y2, layer.y1, layer.a1, w, b, cfg.H, r0, workspace=layer.conv_ws)
             dpp.dpp_splice_patch(layer.kv[p], layer.y2, r0)
             kv = layer.kv[p].view(cfg.B, cfg.N, cfg.C)
             if record:
@@ -319,7 +319,8 @@ def time_kernels(cfg, layer, x_patches, gamma, beta, w, b, eps, rel, eps_c, eps_
             timed("groupnorm", lambda: dpp.dpp_groupnorm_stale(layer.y1, layer.stats_next, x_patches[p],
                                                                layer.stats_prev, gamma, beta, cfg.H, cfg.G, cfg.P, p,
                                                                cfg.gn_eps, layer.gn_ws))
-            timed("conv", lambda: dpp.dpp_conv3x3_halo(layer.y2, layer.y1, layer.a1, w, b, cfg.H, r0))
+            timed("conv", lambda: dpp.dpp_conv3x3_halo(layer.y2, layer.y1, layer.a1, w, b, cfg.H, r0,
+                                                       workspace=layer.conv_ws))
             timed("splice", lambda: dpp.dpp_splice_patch(layer.kv[p], layer.y2, r0))
             timed("attention", lambda: dpp.dpp_self_attn_displaced(layer.o, layer.y2.view(cfg.B, cfg.Nq, cfg.C), kv,
                                                                    kv, cfg.heads, cfg.D, 0.0, layer.attn_ws))

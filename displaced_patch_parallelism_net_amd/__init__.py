@@ -13,6 +13,7 @@ from ._lib import (  # noqa: F401
     dpp_cfg_combine_relmae,
     dpp_cfg_combine_workspace_bytes,
     dpp_conv3x3_halo,
+    dpp_conv3x3_halo_workspace_bytes,
     dpp_groupnorm_silu_stale,
     dpp_groupnorm_stale,
     dpp_groupnorm_stale_workspace_bytes,

@@ -34,6 +34,9 @@ SIGNATURES = {
     "dpp_groupnorm_silu_stale": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _i64, _i64, _i64,
                                       _f, _vp, _sz, _i, _vp]),
     "dpp_conv3x3_halo": (_i, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _i64, _i64, _i, _vp]),
+    "dpp_conv3x3_halo_workspace_bytes": (_sz, [_i64, _i64, _i64, _i64, _i64]),
+    "dpp_conv3x3_halo_ws": (_i, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _i64, _i64, _vp, _sz, _i,
+                                 _vp]),
     "dpp_self_attn_workspace_bytes": (_sz, [_i64, _i64, _i64, _i64, _i64, _i]),
     "dpp_self_attn_displaced": (_i, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _i64, _i64, _i64, _f, _vp, _sz,
                                      _i, _vp]),
@@ -201,7 +204,13 @@ def dpp_linear(y, x, w, bias=None, stream=None):
                                         x3.stride(0), y3.stride(1), y3.stride(0), _dtype(x), _stream(stream)))
 
 
-def dpp_conv3x3_halo(y, x, stale_full, weight, bias, H: int, row0: int, stream=None):
+def dpp_conv3x3_halo_workspace_bytes(B, rows, W, Cin, Cout) -> int:
+    return int(LIB.dpp_conv3x3_halo_workspace_bytes(B, rows, W, Cin, Cout))
+
+
+def dpp_conv3x3_halo(y, x, stale_full, weight, bias, H: int, row0: int, workspace=None, stream=None):
+    """With a workspace (dpp_conv3x3_halo_workspace_bytes) small patches may
+    split the input channels across workgroups (dpp_conv3x3_halo_ws)."""
     _contig(y, x, stale_full, weight, bias)
     _same_dtype(y, x, stale_full, weight)
     _f32(bias)
@@ -211,9 +220,15 @@ def dpp_conv3x3_halo(y, x, stale_full, weight, bias, H: int, row0: int, stream=N
     _shape(y, (B, rows, W, Cout), "y")
     _shape(stale_full, (B, H, W, Cin), "stale_full")
     _numel(bias, Cout, "bias")
-    _check("dpp_conv3x3_halo",
-           LIB.dpp_conv3x3_halo(_ptr(y), _ptr(x), _ptr(stale_full), _ptr(weight), _ptr(bias), B, H, W, Cin, Cout, row0,
-                                rows, _dtype(x), _stream(stream)))
+    if workspace is None:
+        _check("dpp_conv3x3_halo",
+               LIB.dpp_conv3x3_halo(_ptr(y), _ptr(x), _ptr(stale_full), _ptr(weight), _ptr(bias), B, H, W, Cin, Cout,
+                                    row0, rows, _dtype(x), _stream(stream)))
+    else:
+        _check("dpp_conv3x3_halo_ws",
+               LIB.dpp_conv3x3_halo_ws(_ptr(y), _ptr(x), _ptr(stale_full), _ptr(weight), _ptr(bias), B, H, W, Cin,
+                                       Cout, row0, rows, _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                       _dtype(x), _stream(stream)))
 
 
 def dpp_self_attn_workspace_bytes(B, n_q, n_kv, heads, head_dim, dtype) -> int:

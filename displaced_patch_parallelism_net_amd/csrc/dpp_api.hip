@@ -112,9 +112,21 @@ int dpp_groupnorm_silu_stale(void* y, float* stats_out, const void* x, const flo
 }
 
 // ------------------------------------------------------------------ a3
+size_t dpp_conv3x3_halo_workspace_bytes(int64_t B, int64_t rows, int64_t W, int64_t Cin, int64_t Cout) {
+  if (B <= 0 || rows <= 0 || W <= 0 || Cin <= 0 || Cout <= 0 || Cin % 64 != 0 || Cout % 16 != 0) return 0;
+  return dpp::conv_workspace_bytes(B, rows, W, Cin, Cout);
+}
+
 int dpp_conv3x3_halo(void* y, const void* x, const void* stale_full, const void* weight, const float* bias, int64_t B,
                      int64_t H, int64_t W, int64_t Cin, int64_t Cout, int64_t row0, int64_t rows, int dtype,
                      void* stream) {
+  return dpp_conv3x3_halo_ws(y, x, stale_full, weight, bias, B, H, W, Cin, Cout, row0, rows, nullptr, 0, dtype,
+                             stream);
+}
+
+int dpp_conv3x3_halo_ws(void* y, const void* x, const void* stale_full, const void* weight, const float* bias,
+                        int64_t B, int64_t H, int64_t W, int64_t Cin, int64_t Cout, int64_t row0, int64_t rows,
+                        void* workspace, size_t workspace_bytes, int dtype, void* stream) {
   if (bad_dtype(dtype)) return DPP_ERR_DTYPE;
   if (!y || !x || !weight) return DPP_ERR_NULL;
   if (B <= 0 || H <= 0 || W <= 0 || Cin <= 0 || Cout <= 0 || rows <= 0 || row0 < 0 || row0 + rows > H)
@@ -134,8 +146,17 @@ int dpp_conv3x3_halo(void* y, const void* x, const void* stale_full, const void*
   if (overlap(y, ybytes, x, B * rows * W * Cin * es) || overlap(y, ybytes, weight, Cout * 9 * Cin * es) ||
       (stale_full && overlap(y, ybytes, stale_full, B * H * W * Cin * es)) || (bias && overlap(y, ybytes, bias, Cout * 4)))
     return DPP_ERR_ALIAS;
-  return launch_status(dpp::launch_conv3x3(y, x, stale_full, weight, bias, B, H, W, Cin, Cout, row0, rows,
-                                           dtype == DPP_BF16, static_cast<hipStream_t>(stream)));
+  if (workspace && workspace_bytes > 0) {
+    const int64_t wb = static_cast<int64_t>(workspace_bytes);
+    if (!aligned16(workspace)) return DPP_ERR_ALIGN;
+    if (overlap(workspace, wb, y, ybytes) || overlap(workspace, wb, x, B * rows * W * Cin * es) ||
+        overlap(workspace, wb, weight, Cout * 9 * Cin * es) ||
+        (stale_full && overlap(workspace, wb, stale_full, B * H * W * Cin * es)) ||
+        (bias && overlap(workspace, wb, bias, Cout * 4)))
+      return DPP_ERR_ALIAS;
+  }
+  return launch_status(dpp::launch_conv3x3(y, x, stale_full, weight, bias, B, H, W, Cin, Cout, row0, rows, workspace,
+                                           workspace_bytes, dtype == DPP_BF16, static_cast<hipStream_t>(stream)));
 }
 
 // ------------------------------------------------------------------ a4

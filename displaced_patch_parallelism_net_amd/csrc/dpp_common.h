@@ -116,9 +116,11 @@ hipError_t launch_groupnorm(void* y, float* stats_out, const void* x, const floa
                             int64_t C, int64_t G, int64_t P, int64_t p, int64_t rows, float eps,
                             void* ws, bool bf16, bool silu, hipStream_t s);
 
+size_t conv_workspace_bytes(int64_t B, int64_t rows, int64_t W, int64_t Cin, int64_t Cout);
 hipError_t launch_conv3x3(void* y, const void* x, const void* stale_full, const void* weight,
                           const float* bias, int64_t B, int64_t H, int64_t W, int64_t Cin,
-                          int64_t Cout, int64_t row0, int64_t rows, bool bf16, hipStream_t s);
+                          int64_t Cout, int64_t row0, int64_t rows, void* ws, size_t ws_bytes, bool bf16,
+                          hipStream_t s);
 
 size_t attn_workspace_bytes(int64_t B, int64_t n_q, int64_t n_kv, int64_t heads, int64_t D, bool bf16);
 hipError_t launch_attention(void* o, const void* q, const void* k, const void* v, int64_t B,

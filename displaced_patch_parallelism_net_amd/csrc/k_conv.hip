@@ -93,8 +93,11 @@ struct ConvArgs {
   const uint16_t* w;
   const float* bias;
   uint16_t* y;
+  float* part;  // split-K: float32 partial outputs [nsplit][B][rows][W][Cout], else NULL
   int H, W, Cin, Cout, row0, rows;
   int tiles_c;  // column tiles per row pair
+  int nsplit;   // input-channel splits (blockIdx.z = b * nsplit + split)
+  int spl;      // 64-channel slices per split
 };
 
 // LDS row of 8 x 16-byte slots, slot index XOR-swizzled by the row index so
@@ -118,12 +121,14 @@ __global__ __launch_bounds__(kConvThreads, 1) void conv3x3_bf16_mfma_kernel(Conv
   const int tid = threadIdx.x;
   const int wave = tid / kWave, lane = tid % kWave;
   const int wr = wave / kConvWN, wn = wave % kConvWN;
-  const int b = blockIdx.z;
+  const int b = blockIdx.z / a.nsplit, split = blockIdx.z % a.nsplit;
   const int m0 = blockIdx.y * kConvBM;
   const int tile_r = blockIdx.x / a.tiles_c, tile_c = blockIdx.x % a.tiles_c;
   const int pr0 = tile_r * kConvTR, pc0 = tile_c * TC;  // patch-relative origin of the pixel tile
   const int H = a.H, W = a.W, Cin = a.Cin;
-  const int nslices = Cin / kConvKC;
+  // this workgroup's input-channel slices: [s0, s0 + nslices)
+  const int s0 = split * a.spl;
+  const int nslices = min(a.spl, Cin / kConvKC - s0);
   const int nsteps = nslices * 3;
 
   // Band staging map, fixed for the kernel: vector u of half hf (rows 2hf,
@@ -169,7 +174,7 @@ __global__ __launch_bounds__(kConvThreads, 1) void conv3x3_bf16_mfma_kernel(Conv
   uint4 w_regA[3][W_ITERS], w_regB[3][W_ITERS];  // weights of the next two steps
   // Loads never touch their results until the staging store.
   auto load_half = [&](uint4 (&reg)[HB_ITERS], int hf, int slice) {
-    const int c0 = min(slice, nslices - 1) * kConvKC;
+    const int c0 = (s0 + min(slice, nslices - 1)) * kConvKC;
 #pragma unroll
     for (int u = 0; u < HB_ITERS; ++u) reg[u] = *reinterpret_cast<const uint4*>(band_src[hf][u] + c0);
   };
@@ -185,10 +190,10 @@ __global__ __launch_bounds__(kConvThreads, 1) void conv3x3_bf16_mfma_kernel(Conv
   };
   auto load_w = [&](uint4 (&reg)[3][W_ITERS], int step) {
     const int st = min(step, nsteps - 1);
-    const int sl = st / 3, dy = st - sl * 3;
+    const int sl = st / 3, dy = st - sl * 3;  // local slice, kernel row
 #pragma unroll
     for (int dx = 0; dx < 3; ++dx) {
-      const int soff = ((dy * 3 + dx) * Cin + sl * kConvKC) * 2;
+      const int soff = ((dy * 3 + dx) * Cin + (s0 + sl) * kConvKC) * 2;
 #pragma unroll
       for (int u = 0; u < W_ITERS; ++u)
         reg[dx][u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rw, w_off[u] + soff, 0, 0));
@@ -292,6 +297,21 @@ __global__ __launch_bounds__(kConvThreads, 1) void conv3x3_bf16_mfma_kernel(Conv
   // -------- epilogue: lane holds channels m0 + wn*CW + i*16 + 4*(lane/16) + 0..3 of one pixel
   const int r = pr0 + wr;
   if (r >= a.rows) return;
+  if (a.part != nullptr) {  // split-K: float32 partials, bias added by the reduction
+    const int64_t nb = gridDim.z / a.nsplit;
+#pragma unroll
+    for (int j = 0; j < TG; ++j) {
+      const int col = pc0 + j * 16 + pl;
+      if (col >= W) continue;
+      float* pp = a.part + (((static_cast<int64_t>(split) * nb + b) * a.rows + r) * W + col) * a.Cout;
+#pragma unroll
+      for (int i = 0; i < kConvCG; ++i) {
+        const int m = m0 + wn * kConvCW + i * 16 + 4 * kg;
+        if (m < a.Cout) *reinterpret_cast<f32x4*>(pp + m) = acc[i][j];
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int j = 0; j < TG; ++j) {
     const int col = pc0 + j * 16 + pl;
@@ -311,6 +331,25 @@ __global__ __launch_bounds__(kConvThreads, 1) void conv3x3_bf16_mfma_kernel(Conv
   }
 }
 
+// Split-K reduction: y = bf16(bias + sum over splits of the float32 partials),
+// the splits added in order; thread per 4 output channels of one pixel.
+__global__ __launch_bounds__(256) void conv_splitk_reduce_kernel(const float* __restrict__ part,
+                                                                 uint16_t* __restrict__ y,
+                                                                 const float* __restrict__ bias, int nsplit,
+                                                                 int64_t npix, int Cout) {
+  const int64_t idx = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  const int cq = Cout / 4;
+  if (idx >= npix * cq) return;
+  const int64_t pix = idx / cq;
+  const int m = static_cast<int>(idx % cq) * 4;
+  f32x4 acc = bias ? f32x4{bias[m], bias[m + 1], bias[m + 2], bias[m + 3]} : f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int sp = 0; sp < nsplit; ++sp) acc += *reinterpret_cast<const f32x4*>(part + (sp * npix + pix) * Cout + m);
+  uint2 out;
+  out.x = pack_bf16x2(acc[0], acc[1]);
+  out.y = pack_bf16x2(acc[2], acc[3]);
+  *reinterpret_cast<uint2*>(y + pix * Cout + m) = out;
+}
+
 // Column-tile choice: the TG (1..5 groups of 16 columns) whose tiles waste the
 // fewest columns; ties go to the larger tile.
 static int conv_pick_tg(int64_t W) {
@@ -327,9 +366,51 @@ static int conv_pick_tg(int64_t W) {
   return best;
 }
 
+struct ConvSplit {
+  int nsplit, spl;
+};
+
+// Input-channel split for grids that would leave CUs idle.  Cost of a launch
+// in slice-rounds: ceil(workgroups x splits / 256) rounds of spl 64-channel
+// slices each, a slice-round being about 3.2 us on MI355X.  A split adds its
+// float32 partials, written and read back by the reduction (counted at
+// 5 TB/s, 16 MB per slice-round), and one slice-round for the reduction's
+// launch.  Gains under 10% go to fewer splits.  The model picks the measured
+// fastest split count at every shape of a forced-split sweep (B = 1-2,
+// 8-240 rows, 64-240 px wide, 320 and 640 channels): 3840 px 8-patch band,
+// 225 workgroups -> no split; 16-patch band, 120 -> 2 (60 -> 47 us); 1024 px
+// 8-patch band, 20 -> 10 (54 -> 29 us); full images never split.
+static ConvSplit conv_split(int64_t B, int64_t rows, int64_t W, int64_t Cin, int64_t Cout) {
+  constexpr double kSliceRoundBytes = 16e6;
+  const int tg = conv_pick_tg(W);
+  const int64_t wgs = ceil_div(rows, kConvTR) * ceil_div(W, 16 * tg) * ceil_div(Cout, kConvBM) * B;
+  const int64_t nsl = Cin / kConvKC;
+  const double out_bytes = static_cast<double>(B) * rows * W * Cout * sizeof(float);
+  ConvSplit best{1, static_cast<int>(nsl)};
+  double best_cost = static_cast<double>(ceil_div(wgs, 256) * nsl);
+  const double bar = 0.9 * best_cost;
+  for (int64_t ns = 2; ns <= nsl; ++ns) {
+    const int64_t spl = ceil_div(nsl, ns), nse = ceil_div(nsl, spl);
+    if (B * nse > 65535) break;
+    const double cost = static_cast<double>(ceil_div(wgs * nse, 256) * spl) + 1.0 +
+                        2.0 * nse * out_bytes / kSliceRoundBytes;
+    if (cost < bar && cost < best_cost) {
+      best_cost = cost;
+      best = ConvSplit{static_cast<int>(nse), static_cast<int>(spl)};
+    }
+  }
+  return best;
+}
+
+size_t conv_workspace_bytes(int64_t B, int64_t rows, int64_t W, int64_t Cin, int64_t Cout) {
+  const ConvSplit sp = conv_split(B, rows, W, Cin, Cout);
+  if (sp.nsplit <= 1) return 0;
+  return static_cast<size_t>(sp.nsplit) * B * rows * W * Cout * sizeof(float);
+}
+
 hipError_t launch_conv3x3(void* y, const void* x, const void* stale_full, const void* weight, const float* bias,
                           int64_t B, int64_t H, int64_t W, int64_t Cin, int64_t Cout, int64_t row0, int64_t rows,
-                          bool bf16, hipStream_t s) {
+                          void* ws, size_t ws_bytes, bool bf16, hipStream_t s) {
   if (!bf16) {
     const int64_t total = B * rows * W * Cout;
     int64_t blocks = ceil_div(total, 256);
@@ -354,13 +435,28 @@ hipError_t launch_conv3x3(void* y, const void* x, const void* stale_full, const 
   const int tg = conv_pick_tg(W);
   a.tiles_c = static_cast<int>(ceil_div(W, 16 * tg));
   const int64_t tiles = ceil_div(rows, kConvTR) * a.tiles_c;
-  dim3 grid(static_cast<unsigned>(tiles), static_cast<unsigned>(ceil_div(Cout, kConvBM)), static_cast<unsigned>(B));
+  ConvSplit sp = conv_split(B, rows, W, Cin, Cout);
+  if (sp.nsplit > 1 && (ws == nullptr || ws_bytes < conv_workspace_bytes(B, rows, W, Cin, Cout)))
+    sp = ConvSplit{1, static_cast<int>(Cin / kConvKC)};
+  a.nsplit = sp.nsplit;
+  a.spl = sp.spl;
+  a.part = sp.nsplit > 1 ? static_cast<float*>(ws) : nullptr;
+  dim3 grid(static_cast<unsigned>(tiles), static_cast<unsigned>(ceil_div(Cout, kConvBM)),
+            static_cast<unsigned>(B * sp.nsplit));
   switch (tg) {
     case 1: hipLaunchKernelGGL(conv3x3_bf16_mfma_kernel<1>, grid, dim3(kConvThreads), 0, s, a); break;
     case 2: hipLaunchKernelGGL(conv3x3_bf16_mfma_kernel<2>, grid, dim3(kConvThreads), 0, s, a); break;
     case 3: hipLaunchKernelGGL(conv3x3_bf16_mfma_kernel<3>, grid, dim3(kConvThreads), 0, s, a); break;
     case 4: hipLaunchKernelGGL(conv3x3_bf16_mfma_kernel<4>, grid, dim3(kConvThreads), 0, s, a); break;
     default: hipLaunchKernelGGL(conv3x3_bf16_mfma_kernel<5>, grid, dim3(kConvThreads), 0, s, a); break;
+  }
+  if (sp.nsplit > 1) {
+    const hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    const int64_t npix = B * rows * W;
+    hipLaunchKernelGGL(conv_splitk_reduce_kernel, dim3(static_cast<unsigned>(ceil_div(npix * (Cout / 4), 256))),
+                       dim3(256), 0, s, static_cast<const float*>(ws), static_cast<uint16_t*>(y), bias, sp.nsplit,
+                       npix, static_cast<int>(Cout));
   }
   return hipGetLastError();
 }

@@ -46,6 +46,9 @@ class DisplacedLayer:
         aw = L.dpp_self_attn_workspace_bytes(B, self.R * W, H * W, heads, head_dim,
                                              L.DPP_BF16 if dtype == torch.bfloat16 else L.DPP_F32)
         self.attn_ws = torch.empty(aw, dtype=torch.uint8, device=device) if aw else None
+        cw = max(L.dpp_conv3x3_halo_workspace_bytes(B, self.R, W, C, C),
+                 L.dpp_conv3x3_halo_workspace_bytes(B, H, W, C, C)) if dtype == torch.bfloat16 else 0
+        self.conv_ws = torch.empty(cw, dtype=torch.uint8, device=device) if cw else None   # split-K partials
         self._stats_full = torch.zeros(B, 1, G, 2, **f32)
 
     def band(self, x, p):
@@ -59,7 +62,7 @@ class DisplacedLayer:
                                   self.H, self.G, self.P, q, self.eps, self.gn_ws)
         L.dpp_groupnorm_stale(self.a1, self._stats_full, x_stale, None, gamma, beta,
                               self.H, self.G, 1, 0, self.eps, self.gn_ws)
-        L.dpp_conv3x3_halo(self.a2, self.a1, None, weight, bias, self.H, 0)
+        L.dpp_conv3x3_halo(self.a2, self.a1, None, weight, bias, self.H, 0, workspace=self.conv_ws)
         for p in range(self.P):
             if self.kv[p] is None:
                 self.kv[p] = torch.empty_like(self.a2)
@@ -71,7 +74,7 @@ class DisplacedLayer:
         r0 = p * self.R
         L.dpp_groupnorm_stale(self.y1, self.stats_next, x_patch, self.stats_prev, gamma, beta,
                               self.H, self.G, self.P, p, self.eps, self.gn_ws)
-        L.dpp_conv3x3_halo(self.y2, self.y1, self.a1, weight, bias, self.H, r0)
+        L.dpp_conv3x3_halo(self.y2, self.y1, self.a1, weight, bias, self.H, r0, workspace=self.conv_ws)
         L.dpp_splice_patch(self.kv[p], self.y2, r0)
         kv = self.kv[p].view(self.B, self.H * self.W, self.C)
         L.dpp_self_attn_displaced(self.o, self.y2.view(self.B, self.R * self.W, self.C), kv, kv,
@@ -105,13 +108,15 @@ class ComponentChain:
         aw = L.dpp_self_attn_workspace_bytes(B, H * W, H * W, heads, head_dim,
                                              L.DPP_BF16 if dtype == torch.bfloat16 else L.DPP_F32)
         self.attn_ws = torch.empty(aw, dtype=torch.uint8, device=device) if aw else None
+        cw = L.dpp_conv3x3_halo_workspace_bytes(B, H, W, C, C) if dtype == torch.bfloat16 else 0
+        self.conv_ws = torch.empty(cw, dtype=torch.uint8, device=device) if cw else None
         self._steps = 0
 
     def component(self, k, x, gamma, beta, weight, bias):
         """Component k on input x [B,H,W,C]; output in self.out[k]."""
         L.dpp_groupnorm_stale(self.y1[k], self._stats, x, None, gamma, beta, self.H, self.G, 1, 0, self.eps,
                               self.gn_ws)
-        L.dpp_conv3x3_halo(self.y2[k], self.y1[k], None, weight, bias, self.H, 0)
+        L.dpp_conv3x3_halo(self.y2[k], self.y1[k], None, weight, bias, self.H, 0, workspace=self.conv_ws)
         t = self.y2[k].view(self.B, self.H * self.W, self.C)
         L.dpp_self_attn_displaced(self.out[k].view(self.B, self.H * self.W, self.C), t, t, t, self.heads, self.D,
                                   0.0, self.attn_ws)

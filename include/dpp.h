@@ -164,6 +164,27 @@ int dpp_conv3x3_halo(void* y, const void* x, const void* stale_full,
                      int64_t row0, int64_t rows, int dtype, void* stream);
 
 /*
+ * dpp_conv3x3_halo with an optional float32 workspace.  When the bf16 patch
+ * is too small to fill the GPU with output tiles (e.g. the 1024 px level: 40
+ * tiles), the input channels are split across workgroups that write float32
+ * partial outputs to the workspace, and a second kernel adds them (in a
+ * fixed order) with the bias; results match the oracle to the same bar, not
+ * bit for bit the unsplit call.  workspace_bytes >=
+ * dpp_conv3x3_halo_workspace_bytes(B, rows, W, Cin, Cout) enables the split
+ * (0 = the shape needs none); NULL / smaller runs unsplit.  The workspace
+ * must be 16-byte aligned (else DPP_ERR_ALIGN) and must not overlap any
+ * operand (else DPP_ERR_ALIAS); calls sharing one must be ordered.
+ * Everything else exactly as dpp_conv3x3_halo.
+ */
+size_t dpp_conv3x3_halo_workspace_bytes(int64_t B, int64_t rows, int64_t W,
+                                        int64_t Cin, int64_t Cout);
+int dpp_conv3x3_halo_ws(void* y, const void* x, const void* stale_full,
+                        const void* weight, const float* bias, int64_t B,
+                        int64_t H, int64_t W, int64_t Cin, int64_t Cout,
+                        int64_t row0, int64_t rows, void* workspace,
+                        size_t workspace_bytes, int dtype, void* stream);
+
+/*
  * a4 -- displaced self-attention (DistriSelfAttentionPP; DistriFusion
  * architecture article, attention section).  The patch's queries attend over
  * all tokens of the spliced full-image K/V buffer (fresh own rows, previous

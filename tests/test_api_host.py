@@ -38,7 +38,7 @@ def header_symbols():
 
 def test_header_symbols_exported_and_bound():
     syms = header_symbols()
-    assert len(syms) == 13, syms
+    assert len(syms) == 15, syms
     for s in syms:
         assert hasattr(L, s), s
         assert s in _lib.SIGNATURES, s
@@ -136,6 +136,24 @@ def test_conv_validation():
     assert conv(y=Dp) == ALIAS
     # f32 has no divisibility or alignment requirement
     assert conv(Cin=3, Cout=5, dtype=F32, x=None) == NULL
+
+
+def test_conv_workspace_query_and_alias():
+    # the 3840 px 8-patch band fills the GPU unsplit; the 16-patch band
+    # splits in two, the 1024 px band in five; full images never split (the
+    # float32 partials would cost more than the idle CUs)
+    assert dpp.dpp_conv3x3_halo_workspace_bytes(1, 30, 240, 640, 640) == 0
+    assert dpp.dpp_conv3x3_halo_workspace_bytes(1, 15, 240, 640, 640) == 2 * 15 * 240 * 640 * 4
+    assert dpp.dpp_conv3x3_halo_workspace_bytes(1, 16, 64, 640, 640) == 5 * 16 * 64 * 640 * 4
+    for hw in (64, 128, 240):
+        assert dpp.dpp_conv3x3_halo_workspace_bytes(1, hw, hw, 640, 640) == 0
+    assert dpp.dpp_conv3x3_halo_workspace_bytes(1, 128, 128, 320, 320) == 0
+    assert dpp.dpp_conv3x3_halo_workspace_bytes(1, 16, 64, 630, 640) == 0   # Cin % 64 != 0
+    ws_rc = _no_launch(L.dpp_conv3x3_halo_ws(A, Bp, Cp, Dp, Ep, 1, 8, 16, 64, 64, 2, 2, A + 64, 1 << 20, BF16, None))
+    assert ws_rc == ALIAS                                                    # workspace over y
+    assert _no_launch(L.dpp_conv3x3_halo_ws(A, Bp, Cp, Dp, Ep, 1, 8, 16, 64, 64, 2, 2, WSP + 4, 1 << 20, BF16,
+                                            None)) == ALIGN
+    assert _no_launch(L.dpp_conv3x3_halo_ws(A, Bp, Cp, Dp, Ep, 1, 8, 16, 64, 64, 2, 2, None, 0, 7, None)) == DTYPE
 
 
 def test_conv_whole_image_needs_no_stale():

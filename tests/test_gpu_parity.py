@@ -221,6 +221,57 @@ def test_conv_ragged_cout(B, H, W, Cin, Cout, r0, R):
     parity(to_host(y), want, "bf16", "conv ragged cout")
 
 
+@pytest.mark.parametrize("name,p", [("sdxl_1024", 1), ("sdxl_2048", 3), ("cfg_pair_1024", 2)])
+def test_conv_split_k_parity(name, p):
+    # small patches split the input channels across workgroups (float32
+    # partials in the workspace, summed with the bias by a second kernel)
+    dpp = _dpp()
+    cfg = CONFIGS[name]
+    wsb = dpp.dpp_conv3x3_halo_workspace_bytes(cfg.B, cfg.rows, cfg.W, cfg.C, cfg.C)
+    assert wsb > 0, "these patch shapes are expected to split"
+    inp = layer_inputs(cfg)
+    r0 = cfg.row0(p)
+    x_np = rows_of(inp["x_fresh"], r0, cfg.rows)
+    x, st, w = to_dev(x_np, cfg.dtype), to_dev(inp["x_stale"], cfg.dtype), to_dev(inp["conv_w"], cfg.dtype)
+    b = torch.from_numpy(inp["conv_b"]).cuda()
+    ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+    y = torch.empty(cfg.B, cfg.rows, cfg.W, cfg.C, dtype=tdt(cfg.dtype), device="cuda")
+    y1 = torch.empty_like(y)
+    say("conv split-K", name, "patch", p, "workspace", wsb)
+    dpp.dpp_conv3x3_halo(y, x, st, w, b, cfg.H, r0, workspace=ws)
+    dpp.dpp_conv3x3_halo(y1, x, st, w, b, cfg.H, r0)
+    torch.cuda.synchronize()
+    want = oracle.conv3x3_halo(values(cfg, x_np), values(cfg, inp["x_stale"]), values(cfg, inp["conv_w"]),
+                               inp["conv_b"], r0)
+    parity(to_host(y), want, cfg.dtype, f"conv split-K {name} p{p}")
+    parity(to_host(y1), want, cfg.dtype, f"conv unsplit {name} p{p}")
+
+
+@pytest.mark.parametrize("B,H,W,Cin,Cout,r0,R", [
+    (2, 9, 5, 192, 80, 3, 3),      # 3 slices split unevenly, ragged Cout, tiny width
+    (1, 6, 20, 320, 144, 0, 6),    # whole image, 5 slices
+])
+def test_conv_split_k_ragged(B, H, W, Cin, Cout, r0, R):
+    dpp = _dpp()
+    rng = np.random.default_rng(9)
+    wsb = dpp.dpp_conv3x3_halo_workspace_bytes(B, R, W, Cin, Cout)
+    assert wsb > 0
+    say("conv split-K ragged", B, H, W, Cin, Cout, r0, R, "workspace", wsb)
+    from dpp_synth import f32_to_bf16_bits
+    xs = f32_to_bf16_bits(rng.standard_normal((B, H, W, Cin)).astype(np.float32))
+    xp = f32_to_bf16_bits(rng.standard_normal((B, R, W, Cin)).astype(np.float32))
+    wt = f32_to_bf16_bits((0.05 * rng.standard_normal((Cout, 3, 3, Cin))).astype(np.float32))
+    bias = (0.1 * rng.standard_normal(Cout)).astype(np.float32)
+    whole = r0 == 0 and R == H
+    y = torch.empty(B, R, W, Cout, dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+    dpp.dpp_conv3x3_halo(y, to_dev(xp, "bf16"), None if whole else to_dev(xs, "bf16"), to_dev(wt, "bf16"),
+                         torch.from_numpy(bias).cuda(), H, r0, workspace=ws)
+    torch.cuda.synchronize()
+    want = oracle.conv3x3_halo(values("bf16", xp), None if whole else values("bf16", xs), values("bf16", wt), bias, r0)
+    parity(to_host(y), want, "bf16", "conv split-K ragged")
+
+
 def test_conv_only_halo_rows_read_on_gpu():
     dpp = _dpp()
     cfg = Config("halo", B=1, H=12, W=33, C=64, P=4, G=8, heads=1, D=64)
