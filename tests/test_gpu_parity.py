@@ -247,11 +247,12 @@ def test_conv_split_k_parity(name, p):
     parity(to_host(y1), want, cfg.dtype, f"conv unsplit {name} p{p}")
 
 
-@pytest.mark.parametrize("B,H,W,Cin,Cout,r0,R", [
-    (2, 9, 5, 192, 80, 3, 3),      # 3 slices split unevenly, ragged Cout, tiny width
-    (1, 6, 20, 320, 144, 0, 6),    # whole image, 5 slices
+@pytest.mark.parametrize("B,H,W,Cin,Cout,r0,R,with_bias", [
+    (2, 9, 5, 192, 80, 3, 3, True),      # 3 slices split unevenly, ragged Cout, tiny width
+    (1, 6, 20, 320, 144, 0, 6, True),    # whole image, 5 slices
+    (1, 6, 20, 320, 144, 0, 6, False),   # no bias: the reduction starts from zero
 ])
-def test_conv_split_k_ragged(B, H, W, Cin, Cout, r0, R):
+def test_conv_split_k_ragged(B, H, W, Cin, Cout, r0, R, with_bias):
     dpp = _dpp()
     rng = np.random.default_rng(9)
     wsb = dpp.dpp_conv3x3_halo_workspace_bytes(B, R, W, Cin, Cout)
@@ -261,12 +262,12 @@ def test_conv_split_k_ragged(B, H, W, Cin, Cout, r0, R):
     xs = f32_to_bf16_bits(rng.standard_normal((B, H, W, Cin)).astype(np.float32))
     xp = f32_to_bf16_bits(rng.standard_normal((B, R, W, Cin)).astype(np.float32))
     wt = f32_to_bf16_bits((0.05 * rng.standard_normal((Cout, 3, 3, Cin))).astype(np.float32))
-    bias = (0.1 * rng.standard_normal(Cout)).astype(np.float32)
+    bias = (0.1 * rng.standard_normal(Cout)).astype(np.float32) if with_bias else None
     whole = r0 == 0 and R == H
     y = torch.empty(B, R, W, Cout, dtype=torch.bfloat16, device="cuda")
     ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
     dpp.dpp_conv3x3_halo(y, to_dev(xp, "bf16"), None if whole else to_dev(xs, "bf16"), to_dev(wt, "bf16"),
-                         torch.from_numpy(bias).cuda(), H, r0, workspace=ws)
+                         None if bias is None else torch.from_numpy(bias).cuda(), H, r0, workspace=ws)
     torch.cuda.synchronize()
     want = oracle.conv3x3_halo(values("bf16", xp), None if whole else values("bf16", xs), values("bf16", wt), bias, r0)
     parity(to_host(y), want, "bf16", "conv split-K ragged")
