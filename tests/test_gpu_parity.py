@@ -419,6 +419,43 @@ def test_attention_many_key_splits():
         parity(to_host(o), want, "bf16", f"attn {nsplit} splits {B},{nq},{nkv}")
 
 
+@pytest.mark.parametrize("split", [False, True])
+def test_attention_growing_scores_rescale_often(split):
+    # Scores that grow along the key range (keys drift along a direction the
+    # queries share) raise each query's running maximum by more than the
+    # kernel's lazy-rescale margin every few key tiles, so the exact path
+    # (true tile max, rescale of O and the row sum, recomputed weights) runs
+    # many times per workgroup; the last quarter of the keys falls back to
+    # small scores, whose weights underflow.  Unsplit: one key range of 65
+    # tiles; split: the key ranges start at different maxima and the merge
+    # combines them.
+    dpp = _dpp()
+    rng = np.random.default_rng(11)
+    from dpp_synth import f32_to_bf16_bits
+    B, nq, nkv, heads = 1, 300, 4133, 2
+    hd = heads * 64
+    say("attention growing scores", "split" if split else "unsplit")
+    u = rng.standard_normal((heads, 64))
+    u /= np.linalg.norm(u, axis=1, keepdims=True)
+    amp = rng.uniform(2.0, 6.0, size=(B, nq, heads, 1))
+    q = (amp * u[None, None] + 0.3 * rng.standard_normal((B, nq, heads, 64))).reshape(B, nq, hd)
+    ramp = 150.0 * np.arange(nkv) / nkv
+    ramp[3 * nkv // 4:] = 0.0
+    k = (rng.standard_normal((B, nkv, heads, 64)) + ramp[None, :, None, None] * u[None, None]).reshape(B, nkv, hd)
+    v = rng.standard_normal((B, nkv, hd))
+    qb, kb, vb = (f32_to_bf16_bits(a.astype(np.float32)) for a in (q, k, v))
+    ws = None
+    if split:
+        wsb = dpp.dpp_self_attn_workspace_bytes(B, nq, nkv, heads, 64, 0)
+        assert wsb > 0
+        ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+    o = torch.empty(B, nq, hd, dtype=torch.bfloat16, device="cuda")
+    dpp.dpp_self_attn_displaced(o, to_dev(qb, "bf16"), to_dev(kb, "bf16"), to_dev(vb, "bf16"), heads, 64, 0.0, ws)
+    torch.cuda.synchronize()
+    want = oracle.self_attn_displaced(values("bf16", qb), values("bf16", kb), values("bf16", vb), heads)
+    parity(to_host(o), want, "bf16", f"attn growing scores {'split' if split else 'unsplit'}")
+
+
 def test_attention_closed_form_zero_query():
     # Q = 0: uniform weights, output = mean of V over all keys
     dpp = _dpp()
