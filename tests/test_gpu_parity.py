@@ -108,6 +108,45 @@ def test_groupnorm_stale_parity(name, cfg):
         assert np.all(others == 7.0), "stats_out slots of other patches were written"
 
 
+def test_groupnorm_offset_means():
+    # Group means far from zero (-6 .. 6, spreads 0.5 .. 2): the variance comes
+    # from raw sums whose E[x^2] - mean^2 cancels up to 99%.  The float32
+    # partial sums are formed in the same reading on both sides (float32
+    # stale sums, float64 totals), so the outputs still meet the bar.
+    dpp = _dpp()
+    cfg = Config("gn_off", B=2, H=64, W=64, C=640, P=4, G=32, heads=10, D=64)
+    rng = np.random.default_rng(21)
+    from dpp_synth import f32_to_bf16_bits
+    say("groupnorm offset means")
+    cpg = cfg.C // cfg.G
+    mean_c = np.repeat(rng.uniform(-6.0, 6.0, cfg.G), cpg)
+    sd_c = np.repeat(rng.uniform(0.5, 2.0, cfg.G), cpg)
+    xf = mean_c + sd_c * rng.standard_normal((cfg.B, cfg.H, cfg.W, cfg.C))
+    xs = xf + 0.05 * rng.standard_normal(xf.shape)
+    xf_b, xs_b = f32_to_bf16_bits(xf.astype(np.float32)), f32_to_bf16_bits(xs.astype(np.float32))
+    stale = _stale_stats(values("bf16", xs_b).astype(np.float64), cfg).astype(np.float32)
+    gamma = (1.0 + 0.02 * rng.standard_normal(cfg.C)).astype(np.float32)
+    beta = (0.02 * rng.standard_normal(cfg.C)).astype(np.float32)
+    ws = torch.empty(dpp.dpp_groupnorm_stale_workspace_bytes(cfg.B, cfg.rows, cfg.W, cfg.C, cfg.G), dtype=torch.uint8,
+                     device="cuda")
+    for p in (1, 3):
+        x_np = xf_b[:, cfg.row0(p):cfg.row0(p) + cfg.rows]
+        x = to_dev(x_np, "bf16")
+        y = torch.empty_like(x)
+        so = torch.zeros(cfg.B, cfg.P, cfg.G, 2, device="cuda")
+        dpp.dpp_groupnorm_stale(y, so, x, torch.from_numpy(stale).cuda(), torch.from_numpy(gamma).cuda(),
+                                torch.from_numpy(beta).cuda(), cfg.H, cfg.G, cfg.P, p, cfg.gn_eps, ws)
+        torch.cuda.synchronize()
+        want_y, want_s = oracle.groupnorm_stale(values("bf16", x_np), stale, gamma, beta, cfg.H, cfg.G, p, cfg.gn_eps)
+        parity(to_host(y), want_y, "bf16", f"gn offset means p{p}")
+        got_s = so.cpu().numpy()[:, p]
+        n = cfg.rows * cfg.W * cpg
+        e1 = (np.abs(got_s[..., 0] - want_s[..., 0]) / (np.abs(want_s[..., 0]) + n)).max()
+        e2 = (np.abs(got_s[..., 1] - want_s[..., 1]) / np.abs(want_s[..., 1])).max()
+        print(f"gn offset stats p{p}: sum err {e1:.3e} of (|sum| + n), sumsq rel err {e2:.3e}", flush=True)
+        assert e1 <= 1e-5 and e2 <= 1e-5
+
+
 def test_groupnorm_stats_only_and_stale_equals_fresh():
     # Synchronous first step: sums of every patch (stats-only calls), then
     # normalising each patch with them equals GroupNorm of the whole image.
