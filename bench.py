@@ -253,6 +253,7 @@ def main():
         if cfg.dtype == "bf16":
             kernels.update(time_projections(cfg, layer, x_patches, gamma, beta, dpp, torch))
             kernels.update(time_component(dpp, torch))
+            kernels.update(time_conv_bands(dpp, torch))
 
     out = {
         "metric": "displaced-attn + halo-conv TFLOP/s (% bf16 MFMA peak); ms per patch-layer step",
@@ -441,6 +442,43 @@ def time_component(dpp, torch, reps=10):
     rate = work / (ms * 1e-3) / 1e12
     return {"component_step_2048": {"median_ms": round(ms, 5), "TFLOP/s": round(rate, 2),
                                     "frac_peak": round(rate / PEAK_BF16_TFLOPS, 4), "work": work}}
+
+
+def time_conv_bands(dpp, torch, reps=20):
+    """The 640 -> 640 conv of smaller patch bands (not part of the headline
+    step), without and with the split-K workspace: the 1024 px level (64 x 64)
+    in 4 and 8 patches, the 2048 px level (128 x 128) in 8 patches and the
+    3840 px level (240 x 240) in 16 patches.  Back-to-back calls timed as one
+    sequence with HIP events; the split count is the library's choice."""
+    C = 640
+    gen = torch.Generator(device="cuda").manual_seed(0)
+    out = {}
+    for name, H, P in (("1024_p4", 64, 4), ("1024_p8", 64, 8), ("2048_p8", 128, 8), ("3840_p16", 240, 16)):
+        R, W = H // P, H
+        x = torch.randn(1, R, W, C, device="cuda", generator=gen).to(torch.bfloat16)
+        st = torch.randn(1, H, W, C, device="cuda", generator=gen).to(torch.bfloat16)
+        w = (0.02 * torch.randn(C, 3, 3, C, device="cuda", generator=gen)).to(torch.bfloat16)
+        b = torch.zeros(C, device="cuda")
+        y = torch.empty_like(x)
+        wsb = dpp.dpp_conv3x3_halo_workspace_bytes(1, R, W, C, C)
+        ws = torch.empty(wsb, dtype=torch.uint8, device="cuda") if wsb else None
+        row = {"rows": R, "W": W, "nsplit": wsb // (R * W * C * 4) if wsb else 1}
+        flop = 2.0 * R * W * C * 9 * C
+        for mode, wsx in (("unsplit", None), ("split", ws)):
+            call = lambda: dpp.dpp_conv3x3_halo(y, x, st, w, b, H, R, workspace=wsx)
+            call()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(reps):
+                call()
+            e1.record()
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) * 1e3 / reps
+            row[f"{mode}_us"] = round(us, 2)
+            row[f"{mode}_TFLOP/s"] = round(flop / (us * 1e-6) / 1e12, 1)
+        out[f"conv_band_{name}"] = row
+    return out
 
 
 def hbm_sweep(cfg, dpp, torch, reps=20):
