@@ -353,7 +353,10 @@ def time_projections(cfg, layer, x_patches, gamma, beta, dpp, torch, reps=10):
     """The projection calls of the attention module and GroupNorm + SiLU at
     the workload's patch size (not part of the headline step): q = x Wq^T +
     bq, the fresh K/V projection written into the patch's rows of a [B,N,2C]
-    K/V buffer, out = o Wo^T + bo.  Seeded weights (projection_inputs)."""
+    K/V buffer, out = o Wo^T + bo.  Seeded weights (projection_inputs).
+    For scale, the same two products through PyTorch's own GEMM
+    (torch.nn.functional.linear, hipBLASLt; bf16 bias, fresh contiguous
+    output): a library reference, not part of this path."""
     from dpp_synth import projection_inputs
     pi = projection_inputs(cfg)
     dev = "cuda"
@@ -371,7 +374,10 @@ def time_projections(cfg, layer, x_patches, gamma, beta, dpp, torch, reps=10):
     q = torch.empty(cfg.B, M, C, dtype=torch.bfloat16, device=dev)
     out = torch.empty_like(q)
     o = layer.o.view(cfg.B, M, C)
-    ev = {k: [] for k in ("linear_q", "linear_kv_into_buffer", "linear_out", "groupnorm_silu")}
+    ev = {k: [] for k in ("linear_q", "linear_kv_into_buffer", "linear_out", "groupnorm_silu",
+                          "library_reference_linear_q", "library_reference_linear_kv")}
+    bq16, bkv16 = bq.to(torch.bfloat16), bkv.to(torch.bfloat16)
+    xq2 = xq.reshape(cfg.B * M, C)   # 2-D: a plain GEMM, no batched product
 
     def timed(name, fn):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -389,6 +395,8 @@ def time_projections(cfg, layer, x_patches, gamma, beta, dpp, torch, reps=10):
             timed("linear_q", lambda: dpp.dpp_linear(q, xq, wq, bq))
             timed("linear_kv_into_buffer", lambda: dpp.dpp_linear(kv2[:, t0:t0 + M, :], xq, wkv, bkv))
             timed("linear_out", lambda: dpp.dpp_linear(out, o, wo, bo))
+            timed("library_reference_linear_q", lambda: torch.nn.functional.linear(xq2, wq, bq16))
+            timed("library_reference_linear_kv", lambda: torch.nn.functional.linear(xq2, wkv, bkv16))
     torch.cuda.synchronize()
     act = cfg.B * M * C * 2
     work = {
@@ -396,6 +404,8 @@ def time_projections(cfg, layer, x_patches, gamma, beta, dpp, torch, reps=10):
         "linear_kv_into_buffer": (2.0 * cfg.B * M * C * 2 * C, "TFLOP/s", PEAK_BF16_TFLOPS),
         "linear_out": (2.0 * cfg.B * M * C * C, "TFLOP/s", PEAK_BF16_TFLOPS),
         "groupnorm_silu": (2.0 * act + 2 * 4 * cfg.B * cfg.G * (cfg.P + 1), "GB/s", PEAK_HBM_GBS),
+        "library_reference_linear_q": (2.0 * cfg.B * M * C * C, "TFLOP/s", PEAK_BF16_TFLOPS),
+        "library_reference_linear_kv": (2.0 * cfg.B * M * C * 2 * C, "TFLOP/s", PEAK_BF16_TFLOPS),
     }
     res = {}
     for k, lst in ev.items():

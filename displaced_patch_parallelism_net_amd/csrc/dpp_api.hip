@@ -213,8 +213,10 @@ int dpp_linear(void* y, const void* x, const void* w, const float* bias, int64_t
   if (dtype == DPP_BF16) {
     if (K % 8 != 0 || N % 4 != 0) return DPP_ERR_UNSUPPORTED;
     // the kernel addresses w and one batch entry of x with 32-bit byte offsets
-    // (rows padded to its 128 x 160 tile; 0x7ffffff0 marks rows past M)
-    if ((N + 128) * K * 2 > 0x7fffffffLL || ((M + 160) * ld_x + K) * 2 > 0x7fffffefLL) return DPP_ERR_UNSUPPORTED;
+    // (rows padded to its tile of up to 256 channels x 160 tokens, plus the
+    // last K slice; 0x7ffffff0 marks rows past M)
+    if ((N + 256) * K * 2 + 128 > 0x7fffffffLL || ((M + 160) * ld_x + K) * 2 > 0x7fffffefLL)
+      return DPP_ERR_UNSUPPORTED;
     if (!aligned16(x) || !aligned16(w) || (reinterpret_cast<uintptr_t>(y) & 7u) || ld_x % 8 || bs_x % 8 ||
         ld_y % 4 || bs_y % 4)
       return DPP_ERR_ALIGN;

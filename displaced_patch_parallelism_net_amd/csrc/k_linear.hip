@@ -8,9 +8,11 @@
 //
 // bf16 path: MFMA v_mfma_f32_16x16x32_bf16 with A = weight rows (output
 // channels, K-contiguous) and B = token rows (K-contiguous).  A workgroup owns
-// 128 channels x 160 tokens (7200 tokens x 640 channels: 225 workgroups, one
-// round on 256 CUs); eight waves, each 32 channels x 80 tokens (2 x 5
-// accumulator tiles).  K is walked in 64-wide slices staged in LDS (XOR-
+// 64*CG channels x 160 tokens, eight waves of 16*CG channels x 80 tokens (CG x
+// 5 accumulator tiles).  CG = 2 (128 channels) for 7200 tokens x 640 channels:
+// 225 workgroups, one round on 256 CUs; CG = 4 (256 channels) for the fused
+// K/V projection (1280 channels): again 225 workgroups instead of two rounds
+// of 225, and each token row is loaded once.  K is walked in 64-wide slices staged in LDS (XOR-
 // swizzled rows, double-buffered); for K = 320, 640, 1280 the slice loop is
 // unrolled and the global loads run four slices ahead (their latency is long
 // against one slice's MFMAs at these sizes); one barrier per slice.  Each lane's
@@ -37,13 +39,10 @@ __global__ __launch_bounds__(256) void linear_f32_kernel(float* __restrict__ y, 
   }
 }
 
-constexpr int kLinBN = 128;   // output channels per workgroup
 constexpr int kLinBM = 160;   // tokens per workgroup
 constexpr int kLinKC = 64;    // K slice (8 x 16-byte vectors per row)
 constexpr int kLinThreads = 512;
-constexpr int kLinCG = 2;     // 16-channel MFMA groups per wave
 constexpr int kLinTG = 5;     // 16-token MFMA groups per wave
-constexpr int kLinItersA = kLinBN * 8 / kLinThreads;                      // weight vectors per thread
 constexpr int kLinItersB = (kLinBM * 8 + kLinThreads - 1) / kLinThreads;  // token vectors per thread
 
 struct LinArgs {
@@ -58,7 +57,7 @@ struct LinArgs {
 __device__ __forceinline__ int lin_swz(int row, int slot) { return row * 8 + (slot ^ (row & 7)); }
 
 constexpr int kLinBufWord3 = 0x00020000;  // raw 32-bit buffer access, no swizzle
-constexpr int kLinAhead = 4;              // K slices in flight (fully unrolled instantiations)
+constexpr int kLinAhead = 4;              // K slices in flight (fully unrolled instantiations, CG = 2)
 
 // NSL > 0: the K loop has exactly NSL slices and is fully unrolled, with the
 // global loads kLinAhead slices ahead in a ring of registers (every count is
@@ -67,9 +66,14 @@ constexpr int kLinAhead = 4;              // K slices in flight (fully unrolled 
 // resources that end at the last element of w and of x's batch entry: rows
 // past N or M read as zero, so no load is predicated; the K tail (k >= K in
 // the last slice) is zeroed by a select.
-template <int NSL>
+template <int NSL, int CG>
 __global__ __launch_bounds__(kLinThreads) void linear_bf16_mfma_kernel(LinArgs a) {
-  constexpr int AHEAD = NSL > 0 ? (NSL < kLinAhead ? NSL : kLinAhead) : 1;
+  constexpr int kLinBN = 64 * CG;                        // output channels per workgroup
+  constexpr int kLinCG = CG;                             // 16-channel MFMA groups per wave
+  constexpr int kLinItersA = kLinBN * 8 / kLinThreads;   // weight vectors per thread
+  // the wider tile holds twice the weight vectors per slice: one slice less in flight
+  constexpr int kAhead = CG == 2 ? kLinAhead : kLinAhead - 1;
+  constexpr int AHEAD = NSL > 0 ? (NSL < kAhead ? NSL : kAhead) : 1;
   __shared__ uint4 As[2][kLinBN * 8];
   __shared__ uint4 Bs[2][kLinBM * 8];
   const int tid = threadIdx.x;
@@ -135,7 +139,7 @@ __global__ __launch_bounds__(kLinThreads) void linear_bf16_mfma_kernel(LinArgs a
 
   const int kg = lane >> 4, pl = lane & 15;
   // fragment rows r = base + 16 i + pl share (r & 7) = (pl & 7)
-  const int a_row0 = wn * 32 + pl, b_row0 = wm * (16 * kLinTG) + pl;
+  const int a_row0 = wn * 16 * kLinCG + pl, b_row0 = wm * (16 * kLinTG) + pl;
   auto compute = [&](int buf) {
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
@@ -185,7 +189,7 @@ __global__ __launch_bounds__(kLinThreads) void linear_bf16_mfma_kernel(LinArgs a
     }
   }
 
-  // epilogue: lane holds channels n0 + wn*32 + 16 i + 4 kg + 0..3 of token m0 + wm*80 + 16 j + pl
+  // epilogue: lane holds channels n0 + wn*16*CG + 16 i + 4 kg + 0..3 of token m0 + wm*80 + 16 j + pl
 #pragma unroll
   for (int j = 0; j < kLinTG; ++j) {
     const int64_t m = m0 + wm * (16 * kLinTG) + 16 * j + pl;
@@ -193,7 +197,7 @@ __global__ __launch_bounds__(kLinThreads) void linear_bf16_mfma_kernel(LinArgs a
     uint16_t* yp = a.y + b * a.bs_y + m * a.ld_y;
 #pragma unroll
     for (int i = 0; i < kLinCG; ++i) {
-      const int64_t n = n0 + wn * 32 + 16 * i + 4 * kg;
+      const int64_t n = n0 + wn * 16 * kLinCG + 16 * i + 4 * kg;
       if (n >= a.N) continue;
       float v0 = acc[i][j][0], v1 = acc[i][j][1], v2 = acc[i][j][2], v3 = acc[i][j][3];
       if (a.bias) { v0 += a.bias[n]; v1 += a.bias[n + 1]; v2 += a.bias[n + 2]; v3 += a.bias[n + 3]; }
@@ -227,13 +231,27 @@ hipError_t launch_linear(void* y, const void* x, const void* w, const float* bia
   a.bs_x = bs_x;
   a.ld_y = ld_y;
   a.bs_y = bs_y;
-  dim3 grid(static_cast<unsigned>(ceil_div(M, kLinBM)), static_cast<unsigned>(ceil_div(N, kLinBN)),
+  // channel tile: the one with the fewer rounds of workgroups times tile
+  // width (one workgroup per CU); ties go to the wider tile (fewer loads of
+  // the token rows, one prologue instead of several)
+  const int64_t tm = ceil_div(M, kLinBM) * B;
+  const int64_t cost2 = ceil_div(tm * ceil_div(N, 128), 256) * 128;
+  const int64_t cost4 = ceil_div(tm * ceil_div(N, 256), 256) * 256;
+  const bool wide = cost4 <= cost2;
+  dim3 grid(static_cast<unsigned>(ceil_div(M, kLinBM)), static_cast<unsigned>(ceil_div(N, wide ? 256 : 128)),
             static_cast<unsigned>(B));
-  switch (ceil_div(K, kLinKC)) {
-    case 5: hipLaunchKernelGGL(linear_bf16_mfma_kernel<5>, grid, dim3(kLinThreads), 0, s, a); break;
-    case 10: hipLaunchKernelGGL(linear_bf16_mfma_kernel<10>, grid, dim3(kLinThreads), 0, s, a); break;
-    case 20: hipLaunchKernelGGL(linear_bf16_mfma_kernel<20>, grid, dim3(kLinThreads), 0, s, a); break;
-    default: hipLaunchKernelGGL(linear_bf16_mfma_kernel<0>, grid, dim3(kLinThreads), 0, s, a); break;
+  const dim3 blk(kLinThreads);
+  switch (ceil_div(K, kLinKC) * 2 + (wide ? 1 : 0)) {
+    case 10: hipLaunchKernelGGL((linear_bf16_mfma_kernel<5, 2>), grid, blk, 0, s, a); break;
+    case 11: hipLaunchKernelGGL((linear_bf16_mfma_kernel<5, 4>), grid, blk, 0, s, a); break;
+    case 20: hipLaunchKernelGGL((linear_bf16_mfma_kernel<10, 2>), grid, blk, 0, s, a); break;
+    case 21: hipLaunchKernelGGL((linear_bf16_mfma_kernel<10, 4>), grid, blk, 0, s, a); break;
+    case 40: hipLaunchKernelGGL((linear_bf16_mfma_kernel<20, 2>), grid, blk, 0, s, a); break;
+    case 41: hipLaunchKernelGGL((linear_bf16_mfma_kernel<20, 4>), grid, blk, 0, s, a); break;
+    default:
+      if (wide) hipLaunchKernelGGL((linear_bf16_mfma_kernel<0, 4>), grid, blk, 0, s, a);
+      else hipLaunchKernelGGL((linear_bf16_mfma_kernel<0, 2>), grid, blk, 0, s, a);
+      break;
   }
   return hipGetLastError();
 }

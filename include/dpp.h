@@ -230,7 +230,7 @@ int dpp_self_attn_displaced(void* o, const void* q, const void* k,
  *   Requires ld_x >= K, ld_y >= N.  bf16 requires K % 8 == 0, N % 4 == 0,
  *   x and w 16-byte aligned, ld_x and bs_x multiples of 8, y 8-byte aligned,
  *   ld_y and bs_y multiples of 4, and 32-bit byte offsets within w and within
- *   one batch entry of x: (N + 128) * K * 2 < 2^31 and ((M + 160) * ld_x +
+ *   one batch entry of x: (N + 256) * K * 2 + 128 < 2^31 and ((M + 160) * ld_x +
  *   K) * 2 < 2^31 - 16 (else DPP_ERR_UNSUPPORTED).  Limits for both dtypes:
  *   B <= 65535, M, K, N <= 2^30.  Float32 accumulation, one rounding.
  */

@@ -250,7 +250,8 @@ def test_linear_32bit_offset_limits():
     # a w just inside the limit passes the size checks: with y placed inside w
     # the aliasing check, which comes after them, is the one that answers (no
     # host test may reach a launch: these pointers are not device memory)
-    assert lin(N=8060, K=1 << 17, ldx=1 << 17, M=4, bsx=1 << 19, ldy=8064, bsy=1 << 15, y=Cp + 64) == ALIAS
+    assert lin(N=7932, K=1 << 17, ldx=1 << 17, M=4, bsx=1 << 19, ldy=8064, bsy=1 << 15, y=Cp + 64) == ALIAS
+    assert lin(N=7936, K=1 << 17, ldx=1 << 17, M=4, bsx=1 << 19, ldy=8064, bsy=1 << 15, y=Cp + 64) == UNSUP
 
 
 def test_linear_validation():

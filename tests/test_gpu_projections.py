@@ -44,6 +44,8 @@ LINEAR_CASES = [
     ("kv_7200_k1280", 1, 7200, 1280, 1280, 1280, 1280, True, "bf16"),  # K = 1280: the 20-slice unrolled path
     ("k320", 1, 517, 320, 192, 320, 192, True, "bf16"),                # K = 320: the 5-slice unrolled path
     ("kv_1280", 1, 1000, 640, 1280, 640, 1280, True, "bf16"),
+    ("kv_7200", 1, 7200, 640, 1280, 640, 1280, True, "bf16"),          # the fused K/V projection, 256-channel tiles
+    ("wide_ragged", 2, 3001, 328, 1152, 336, 1160, True, "bf16"),      # 256-channel tiles, half-empty last tile, generic K
     ("ragged_strided", 2, 301, 200, 84, 208, 96, True, "bf16"),
     ("no_bias", 1, 130, 64, 128, 64, 128, False, "bf16"),
     ("f32", 2, 37, 24, 20, 30, 22, True, "f32"),
