@@ -74,8 +74,11 @@ __global__ __launch_bounds__(kLinThreads) void linear_bf16_mfma_kernel(LinArgs a
   // the wider tile holds twice the weight vectors per slice: one slice less in flight
   constexpr int kAhead = CG == 2 ? kLinAhead : kLinAhead - 1;
   constexpr int AHEAD = NSL > 0 ? (NSL < kAhead ? NSL : kAhead) : 1;
-  __shared__ uint4 As[2][kLinBN * 8];
-  __shared__ uint4 Bs[2][kLinBM * 8];
+  // LDS: the two weight and two token slice buffers; after the K loop the
+  // same memory holds the output tile for the coalesced store
+  __shared__ uint4 smem[2 * kLinBN * 8 + 2 * kLinBM * 8];
+  uint4* const As = smem;                     // [2][kLinBN * 8]
+  uint4* const Bs = smem + 2 * kLinBN * 8;    // [2][kLinBM * 8]
   const int tid = threadIdx.x;
   const int wave = tid / kWave, lane = tid % kWave;
   const int wn = wave % 4, wm = wave / 4;
@@ -122,12 +125,12 @@ __global__ __launch_bounds__(kLinThreads) void linear_bf16_mfma_kernel(LinArgs a
 #pragma unroll
     for (int u = 0; u < kLinItersA; ++u) {
       const int id = tid + u * kLinThreads;
-      As[buf][lin_swz(id >> 3, id & 7)] = masked(a_reg[r][u], m);
+      As[buf * kLinBN * 8 + lin_swz(id >> 3, id & 7)] = masked(a_reg[r][u], m);
     }
 #pragma unroll
     for (int u = 0; u < kLinItersB; ++u) {
       const int id = tid + u * kLinThreads;
-      if (id < kLinBM * 8) Bs[buf][lin_swz(id >> 3, id & 7)] = masked(b_reg[r][u], m);
+      if (id < kLinBM * 8) Bs[buf * kLinBM * 8 + lin_swz(id >> 3, id & 7)] = masked(b_reg[r][u], m);
     }
   };
 
@@ -146,9 +149,9 @@ __global__ __launch_bounds__(kLinThreads) void linear_bf16_mfma_kernel(LinArgs a
       const int slot = (ks * 4 + kg) ^ (pl & 7);
       bf16x8 af[kLinCG], bfr[kLinTG];
 #pragma unroll
-      for (int i = 0; i < kLinCG; ++i) af[i] = __builtin_bit_cast(bf16x8, As[buf][(a_row0 + 16 * i) * 8 + slot]);
+      for (int i = 0; i < kLinCG; ++i) af[i] = __builtin_bit_cast(bf16x8, As[buf * kLinBN * 8 + (a_row0 + 16 * i) * 8 + slot]);
 #pragma unroll
-      for (int j = 0; j < kLinTG; ++j) bfr[j] = __builtin_bit_cast(bf16x8, Bs[buf][(b_row0 + 16 * j) * 8 + slot]);
+      for (int j = 0; j < kLinTG; ++j) bfr[j] = __builtin_bit_cast(bf16x8, Bs[buf * kLinBM * 8 + (b_row0 + 16 * j) * 8 + slot]);
 #pragma unroll
       for (int i = 0; i < kLinCG; ++i)
 #pragma unroll
@@ -189,23 +192,42 @@ __global__ __launch_bounds__(kLinThreads) void linear_bf16_mfma_kernel(LinArgs a
     }
   }
 
-  // epilogue: lane holds channels n0 + wn*16*CG + 16 i + 4 kg + 0..3 of token m0 + wm*80 + 16 j + pl
+  // epilogue: lane holds channels wn*16*CG + 16 i + 4 kg + 0..3 (of the tile)
+  // of token wm*80 + 16 j + pl.  Bias added and rounded here, then the tile
+  // goes through LDS ([token][channel], rows padded by 32 bytes against bank
+  // conflicts) so that every wave store writes whole rows: 64 lanes x 8 bytes
+  // = 2 (CG = 2) or 1 (CG = 4) full tile rows, instead of 32-byte pieces of
+  // 16 rows.  The K loop ended with a barrier: the slice buffers are free.
+  constexpr int kRowU2 = kLinBN / 4 + 4;  // uint2 per padded LDS row
+  uint2* const tile = reinterpret_cast<uint2*>(smem);
 #pragma unroll
-  for (int j = 0; j < kLinTG; ++j) {
-    const int64_t m = m0 + wm * (16 * kLinTG) + 16 * j + pl;
-    if (m >= a.M) continue;
-    uint16_t* yp = a.y + b * a.bs_y + m * a.ld_y;
+  for (int i = 0; i < kLinCG; ++i) {
+    const int c = wn * 16 * kLinCG + 16 * i + 4 * kg;
+    const int64_t n = n0 + c;
+    float bv[4] = {0.f, 0.f, 0.f, 0.f};
+    if (a.bias && n < a.N) {
 #pragma unroll
-    for (int i = 0; i < kLinCG; ++i) {
-      const int64_t n = n0 + wn * 16 * kLinCG + 16 * i + 4 * kg;
-      if (n >= a.N) continue;
-      float v0 = acc[i][j][0], v1 = acc[i][j][1], v2 = acc[i][j][2], v3 = acc[i][j][3];
-      if (a.bias) { v0 += a.bias[n]; v1 += a.bias[n + 1]; v2 += a.bias[n + 2]; v3 += a.bias[n + 3]; }
-      uint2 out;
-      out.x = pack_bf16x2(v0, v1);
-      out.y = pack_bf16x2(v2, v3);
-      *reinterpret_cast<uint2*>(yp + n) = out;
+      for (int e = 0; e < 4; ++e) bv[e] = a.bias[n + e];
     }
+#pragma unroll
+    for (int j = 0; j < kLinTG; ++j) {
+      const int r = wm * (16 * kLinTG) + 16 * j + pl;
+      uint2 out;
+      out.x = pack_bf16x2(acc[i][j][0] + bv[0], acc[i][j][1] + bv[1]);
+      out.y = pack_bf16x2(acc[i][j][2] + bv[2], acc[i][j][3] + bv[3]);
+      tile[r * kRowU2 + c / 4] = out;
+    }
+  }
+  __syncthreads();
+  constexpr int kChunks = kLinBM * (kLinBN / 4);  // 8-byte chunks of the tile
+  static_assert(kChunks % kLinThreads == 0, "whole chunks per thread");
+#pragma unroll
+  for (int u = 0; u < kChunks / kLinThreads; ++u) {
+    const int id = tid + u * kLinThreads;
+    const int r = id / (kLinBN / 4), q = id % (kLinBN / 4);
+    const int64_t m = m0 + r, n = n0 + 4 * q;
+    if (m < a.M && n < a.N)
+      *reinterpret_cast<uint2*>(a.y + b * a.bs_y + m * a.ld_y + n) = tile[r * kRowU2 + q];
   }
 }
 
