@@ -296,38 +296,59 @@ __global__ __launch_bounds__(kConvThreads, 1) void conv3x3_bf16_mfma_kernel(Conv
 
   // -------- epilogue: lane holds channels m0 + wn*CW + i*16 + 4*(lane/16) + 0..3 of one pixel
   const int r = pr0 + wr;
-  if (r >= a.rows) return;
   if (a.part != nullptr) {  // split-K: float32 partials, bias added by the reduction
-    const int64_t nb = gridDim.z / a.nsplit;
+    if (r < a.rows) {
+      const int64_t nb = gridDim.z / a.nsplit;
 #pragma unroll
-    for (int j = 0; j < TG; ++j) {
-      const int col = pc0 + j * 16 + pl;
-      if (col >= W) continue;
-      float* pp = a.part + (((static_cast<int64_t>(split) * nb + b) * a.rows + r) * W + col) * a.Cout;
+      for (int j = 0; j < TG; ++j) {
+        const int col = pc0 + j * 16 + pl;
+        if (col >= W) continue;
+        float* pp = a.part + (((static_cast<int64_t>(split) * nb + b) * a.rows + r) * W + col) * a.Cout;
 #pragma unroll
-      for (int i = 0; i < kConvCG; ++i) {
-        const int m = m0 + wn * kConvCW + i * 16 + 4 * kg;
-        if (m < a.Cout) *reinterpret_cast<f32x4*>(pp + m) = acc[i][j];
+        for (int i = 0; i < kConvCG; ++i) {
+          const int m = m0 + wn * kConvCW + i * 16 + 4 * kg;
+          if (m < a.Cout) *reinterpret_cast<f32x4*>(pp + m) = acc[i][j];
+        }
       }
     }
-    return;
+    return;  // uniform over the workgroup: no barrier follows
   }
+  // bf16 output: bias added and rounded in registers, the tile (2 rows x TC
+  // pixels x 128 channels) staged in LDS ([pixel][channel], pixels padded by
+  // 32 bytes against bank conflicts), then stored so that each wave store
+  // writes the 256 contiguous bytes of two whole pixels instead of 32-byte
+  // pieces of 16 pixels.  The slice loop ended with a barrier, so the weight
+  // buffers are free.
+  constexpr int kPixU2 = kConvBM / 4 + 4;  // uint2 per padded LDS pixel
+  uint2* const tile = reinterpret_cast<uint2*>(&wts[0][0][0]);
 #pragma unroll
-  for (int j = 0; j < TG; ++j) {
-    const int col = pc0 + j * 16 + pl;
-    if (col >= W) continue;
-    uint16_t* yp = a.y + ((static_cast<int64_t>(b) * a.rows + r) * W + col) * a.Cout;
+  for (int i = 0; i < kConvCG; ++i) {
+    const int c = wn * kConvCW + i * 16 + 4 * kg;
+    const int m = m0 + c;
+    float bv[4] = {0.f, 0.f, 0.f, 0.f};
+    if (a.bias && m < a.Cout) {
 #pragma unroll
-    for (int i = 0; i < kConvCG; ++i) {
-      const int m = m0 + wn * kConvCW + i * 16 + 4 * kg;
-      if (m >= a.Cout) continue;
-      float v0 = acc[i][j][0], v1 = acc[i][j][1], v2 = acc[i][j][2], v3 = acc[i][j][3];
-      if (a.bias) { v0 += a.bias[m]; v1 += a.bias[m + 1]; v2 += a.bias[m + 2]; v3 += a.bias[m + 3]; }
-      uint2 out;
-      out.x = pack_bf16x2(v0, v1);
-      out.y = pack_bf16x2(v2, v3);
-      *reinterpret_cast<uint2*>(yp + m) = out;
+      for (int e = 0; e < 4; ++e) bv[e] = a.bias[m + e];
     }
+#pragma unroll
+    for (int j = 0; j < TG; ++j) {
+      uint2 out;
+      out.x = pack_bf16x2(acc[i][j][0] + bv[0], acc[i][j][1] + bv[1]);
+      out.y = pack_bf16x2(acc[i][j][2] + bv[2], acc[i][j][3] + bv[3]);
+      tile[(wr * TC + j * 16 + pl) * kPixU2 + c / 4] = out;
+    }
+  }
+  __syncthreads();
+  constexpr int kChunks = kConvTR * TC * (kConvBM / 4);  // 8-byte chunks of the tile
+  static_assert(kChunks % kConvThreads == 0, "whole chunks per thread");
+#pragma unroll
+  for (int u = 0; u < kChunks / kConvThreads; ++u) {
+    const int id = tid + u * kConvThreads;
+    const int pix = id / (kConvBM / 4), q = id % (kConvBM / 4);
+    const int row = pr0 + pix / TC, col = pc0 + pix % TC, m = m0 + 4 * q;
+    if (row < a.rows && col < W && m < a.Cout)
+      *reinterpret_cast<uint2*>(a.y + ((static_cast<int64_t>(b) * a.rows + row) * W + col) * a.Cout + m) =
+          tile[pix * kPixU2 + q];
   }
 }
 
