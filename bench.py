@@ -158,10 +158,17 @@ def cpu_baseline(cfg, budget_s):
         if dt < budget_s / 8:
             nq *= 2
             npx *= 2
+    cpu_model = None
+    try:
+        with open("/proc/cpuinfo") as fh:
+            cpu_model = next((ln.split(":", 1)[1].strip() for ln in fh if ln.startswith("model name")), None)
+    except OSError:  # pragma: no cover
+        pass
     return {
         "value": done_flops / t_total / 1e12,
         "unit": "TFLOP/s",
         "cores": int(threads),
+        "cpu_model": cpu_model,
         "kind": "oracle",
         "sample": (f"float64 numpy oracle: displaced attention of {sum(s[0] for s in samples)} query rows x "
                    f"{cfg.N} keys x {cfg.heads} heads and the halo conv of {sum(s[1] for s in samples)} output "
@@ -212,10 +219,14 @@ def main():
     torch.cuda.synchronize()
 
     attn_events = []
+    patch_events = []
 
     def step(record=False):
         for p in range(cfg.P):
             r0 = p * layer.R
+            if record:
+                p0 = torch.cuda.Event(enable_timing=True)
+                p0.record()
             dpp.dpp_groupnorm_stale(layer.y1, layer.stats_next, x_patches[p], layer.stats_prev, gamma, beta, cfg.H,
                                     cfg.G, cfg.P, p, cfg.gn_eps, layer.gn_ws)
             dpp.dpp_conv3x3_halo(layer.y2, layer.y1, layer.a1, w, b, cfg.H, r0, workspace=layer.conv_ws)
@@ -229,6 +240,7 @@ def main():
             if record:
                 e1.record()
                 attn_events.append((e0, e1))
+                patch_events.append((p0, e1))
         dpp.dpp_cfg_combine_relmae(eps, rel, eps_c, eps_u, cfg.guidance, cfg_ws)
 
     for _ in range(args.warmup):
@@ -241,6 +253,9 @@ def main():
     wall = time.perf_counter() - t0
     ms_step = wall * 1e3 / args.steps
     attn_ms = float(np.mean([a.elapsed_time(b_) for a, b_ in attn_events]))
+    # one patch's GN -> conv -> splice -> attention, by events on the launch
+    # stream, over every patch and timed step
+    patch_ms = np.array([a.elapsed_time(b_) for a, b_ in patch_events])
 
     f_conv, f_attn = flops(cfg)
     step_flops = cfg.P * (f_conv + f_attn)
@@ -279,6 +294,11 @@ def main():
         },
         "pct_bf16_mfma_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
         "ms_per_patch_layer_step": round(ms_step / cfg.P, 4),
+        "patch_layer_step_ms": {"median": round(float(np.median(patch_ms)), 4),
+                                "p10": round(float(np.percentile(patch_ms, 10)), 4),
+                                "p90": round(float(np.percentile(patch_ms, 90)), 4),
+                                "sum_over_patches": round(float(np.median(patch_ms)) * cfg.P, 4),
+                                "samples": int(patch_ms.size)},
         "roofline": {
             "kernel": "dpp_self_attn_displaced",
             "bound": "mfma",

@@ -36,3 +36,5 @@ def test_bench_prints_one_json_line_with_the_contract_fields():
     assert d["value"] > 0 and d["ms_per_step"] > 0
     assert 0 < d["roofline"]["frac"] < 1
     assert d["config"]["workload"].startswith("sdxl_3840")
+    pl = d["patch_layer_step_ms"]   # one patch's GN -> conv -> splice -> attention, by events
+    assert pl["samples"] == 8 and 0 < pl["p10"] <= pl["median"] <= pl["p90"] < d["ms_per_step"]
