@@ -314,12 +314,13 @@ __global__ __launch_bounds__(kConvThreads, 1) void conv3x3_bf16_mfma_kernel(Conv
     return;  // uniform over the workgroup: no barrier follows
   }
   // bf16 output: bias added and rounded in registers, the tile (2 rows x TC
-  // pixels x 128 channels) staged in LDS ([pixel][channel], pixels padded by
-  // 32 bytes against bank conflicts), then stored so that each wave store
+  // pixels x 128 channels) staged in LDS ([pixel][channel]; pixels padded by
+  // 16 bytes, a stride of 4 banks mod 64, so the 16 pixels of a tile write
+  // fall on distinct banks), then stored so that each wave store
   // writes the 256 contiguous bytes of two whole pixels instead of 32-byte
   // pieces of 16 pixels.  The slice loop ended with a barrier, so the weight
   // buffers are free.
-  constexpr int kPixU2 = kConvBM / 4 + 4;  // uint2 per padded LDS pixel
+  constexpr int kPixU2 = kConvBM / 4 + 2;  // uint2 per padded LDS pixel
   uint2* const tile = reinterpret_cast<uint2*>(&wts[0][0][0]);
 #pragma unroll
   for (int i = 0; i < kConvCG; ++i) {

@@ -194,11 +194,12 @@ __global__ __launch_bounds__(kLinThreads) void linear_bf16_mfma_kernel(LinArgs a
 
   // epilogue: lane holds channels wn*16*CG + 16 i + 4 kg + 0..3 (of the tile)
   // of token wm*80 + 16 j + pl.  Bias added and rounded here, then the tile
-  // goes through LDS ([token][channel], rows padded by 32 bytes against bank
-  // conflicts) so that every wave store writes whole rows: 64 lanes x 8 bytes
+  // goes through LDS ([token][channel]; rows padded by 16 bytes, a stride of
+  // 4 banks mod 64, so the 16 tokens of a tile write fall on distinct banks)
+  // so that every wave store writes whole rows: 64 lanes x 8 bytes
   // = 2 (CG = 2) or 1 (CG = 4) full tile rows, instead of 32-byte pieces of
   // 16 rows.  The K loop ended with a barrier: the slice buffers are free.
-  constexpr int kRowU2 = kLinBN / 4 + 4;  // uint2 per padded LDS row
+  constexpr int kRowU2 = kLinBN / 4 + 2;  // uint2 per padded LDS row
   uint2* const tile = reinterpret_cast<uint2*>(smem);
 #pragma unroll
   for (int i = 0; i < kLinCG; ++i) {
