@@ -128,8 +128,8 @@ __device__ __forceinline__ uint4 buffer_load16(__amdgpu_buffer_rsrc_t r, int vof
 constexpr int kAttBufs = 4;
 
 __global__ __launch_bounds__(kAttThreads, 2) void attn_bf16_kernel(AttnArgs a) {
-  __shared__ uint16_t Ks[kAttBufs][kAttKT * kAttRow];
-  __shared__ uint16_t Vt[kAttBufs][kAttD * kAttRow];
+  __shared__ __align__(16) uint16_t Ks[kAttBufs][kAttKT * kAttRow];
+  __shared__ __align__(16) uint16_t Vt[kAttBufs][kAttD * kAttRow];
 
   const int tid = threadIdx.x;
   const int wave = tid / kWave, lane = tid % kWave;
@@ -392,12 +392,12 @@ __global__ __launch_bounds__(kAttThreads, 2) void attn_bf16_kernel(AttnArgs a) {
   }
 
   // ---- epilogue: lane holds query l32, d = db*32 + 8*(r/4) + 4*g + r%4
+  if (a.o_part == nullptr) {
 #pragma unroll
-  for (int qb2 = 0; qb2 < 2; ++qb2) {
-    const int qi = q0 + qb2 * 32 + l32;
-    const float l_tot = l_run[qb2] + __shfl_xor(l_run[qb2], 32, kWave);
-    if (qi >= a.n_q) continue;
-    if (a.o_part == nullptr) {
+    for (int qb2 = 0; qb2 < 2; ++qb2) {
+      const int qi = q0 + qb2 * 32 + l32;
+      const float l_tot = l_run[qb2] + __shfl_xor(l_run[qb2], 32, kWave);
+      if (qi >= a.n_q) continue;
       const float inv = 1.f / l_tot;
       uint16_t* op = a.o + (static_cast<int64_t>(b) * a.n_q + qi) * a.ld_o + h * kAttD;
 #pragma unroll
@@ -410,22 +410,41 @@ __global__ __launch_bounds__(kAttThreads, 2) void attn_bf16_kernel(AttnArgs a) {
           u.y = pack_bf16x2(O[qb2][db][r4 * 4 + 2] * inv, O[qb2][db][r4 * 4 + 3] * inv);
           *reinterpret_cast<uint2*>(op + d) = u;
         }
-    } else {
-      const int64_t row = (static_cast<int64_t>(split) * a.n_bh + bh) * a.n_q + qi;
-      float* op = a.o_part + row * kAttD;
-#pragma unroll
-      for (int db = 0; db < 2; ++db)
-#pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-          const int d = db * 32 + 8 * r4 + 4 * g;
-          *reinterpret_cast<float4*>(op + d) =
-              make_float4(O[qb2][db][r4 * 4 + 0], O[qb2][db][r4 * 4 + 1], O[qb2][db][r4 * 4 + 2], O[qb2][db][r4 * 4 + 3]);
-        }
-      if (g == 0) {
-        a.ml_part[row * 2] = m_run[qb2];
-        a.ml_part[row * 2 + 1] = l_tot;
-      }
     }
+    return;
+  }
+  // Split partials: each wave's 64 x 64 float32 block goes through LDS (the
+  // tile buffers, free once every wave has finished the drain; rows padded
+  // to 68 floats, a stride of 4 banks mod 64) so that each store writes four
+  // whole 256-byte rows, which are consecutive in o_part, instead of 16-byte
+  // pieces of 32 rows.
+  constexpr int kStageRow = kAttD + 4;
+  __syncthreads();
+  float* const stage = reinterpret_cast<float*>(wave < 2 ? &Ks[0][0] : &Vt[0][0]) + (wave & 1) * kAttQW * kStageRow;
+#pragma unroll
+  for (int qb2 = 0; qb2 < 2; ++qb2) {
+    const int qi = q0 + qb2 * 32 + l32;
+    const float l_tot = l_run[qb2] + __shfl_xor(l_run[qb2], 32, kWave);
+#pragma unroll
+    for (int db = 0; db < 2; ++db)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4)
+        *reinterpret_cast<float4*>(stage + (qb2 * 32 + l32) * kStageRow + db * 32 + 8 * r4 + 4 * g) =
+            make_float4(O[qb2][db][r4 * 4 + 0], O[qb2][db][r4 * 4 + 1], O[qb2][db][r4 * 4 + 2], O[qb2][db][r4 * 4 + 3]);
+    if (g == 0 && qi < a.n_q) {
+      const int64_t row = (static_cast<int64_t>(split) * a.n_bh + bh) * a.n_q + qi;
+      a.ml_part[row * 2] = m_run[qb2];
+      a.ml_part[row * 2 + 1] = l_tot;
+    }
+  }
+  __syncthreads();
+  const int64_t row0 = (static_cast<int64_t>(split) * a.n_bh + bh) * a.n_q + q0;
+#pragma unroll
+  for (int it = 0; it < kAttQW / 4; ++it) {
+    const int r = it * 4 + (lane >> 4), c = lane & 15;
+    if (q0 + r < a.n_q)
+      *reinterpret_cast<float4*>(a.o_part + (row0 + r) * kAttD + 4 * c) =
+          *reinterpret_cast<const float4*>(stage + r * kStageRow + 4 * c);
   }
 }
 
