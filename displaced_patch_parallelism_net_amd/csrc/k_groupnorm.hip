@@ -10,9 +10,9 @@
 //      registers (each thread owns one 16-byte channel vector and walks
 //      pixels, eight loads in flight), folds channels into groups through LDS in a fixed order and
 //      writes one (s1, s2) per group to the workspace;
-//   2. finalize: one workgroup per b adds the chunk partials in float64 (fixed
-//      order), adds the other patches' stale sums, writes the fresh sums to
-//      stats_out[b,p] and mean/rstd to the workspace;
+//   2. finalize: one wave per (group, b) adds the chunk partials in float64
+//      (fixed order), adds the other patches' stale sums, writes the fresh
+//      sums to stats_out[b,p] and mean/rstd to the workspace;
 //   3. apply: y = x * a_c + b_c with a_c = rstd_g gamma_c, b_c = beta_c -
 //      mean_g a_c (then SiLU when asked: the GroupNorm + SiLU pair opening
 //      an SDXL residual block); one 16-byte load and one streaming store per
@@ -23,7 +23,6 @@
 namespace dpp {
 
 constexpr int kGnMaxThreads = 256;
-constexpr int kGnFinThreads = 1024;  // finalize: threads per batch entry
 constexpr int kGnStatChunks = 256;    // total partial workgroups (over B)
 constexpr int kGnApplyChunks = 1024;  // total apply workgroups (over B)
 constexpr int kGnInFlight = 8;        // 16-byte loads in flight per thread
@@ -130,70 +129,61 @@ __global__ __launch_bounds__(kGnMaxThreads) void gn_partial_kernel(const T* __re
   }
 }
 
-// Finalize: thread t of batch entry b owns group t % G and every
-// (1024/G)-th chunk from t / G; its chunk loads are all issued before they
-// are summed (up to kGnFinLoads each, else a loop), and the other patches'
-// stale sums are loaded into LDS by the same threads meanwhile.
+// Finalize: one wave per (group g, batch entry b).  Lane l sums chunks l,
+// l + 64, ... of the group's partials in float64 (kGnFinLoads loads issued
+// before they are summed, then a remainder loop) and, issued with the first
+// of them, the stale sums of patches l, l + 64, ... other than p; two fixed
+// xor butterflies add the lanes (every lane ends with the same totals); lane
+// 0 writes the fresh sums and (mean, rstd).  Deterministic, no atomics.
 constexpr int kGnFinLoads = 8;
-constexpr int kGnFinStale = 2048;  // stale (q, g) pairs staged in LDS: P * G <= this
 
-__global__ __launch_bounds__(kGnFinThreads) void gn_finalize_kernel(
+__global__ __launch_bounds__(kWave) void gn_finalize_kernel(
     const float* __restrict__ partial, int64_t nchunk, const float* __restrict__ stale, float* __restrict__ stats_out,
     float* __restrict__ coef, int G, int P, int p, double n, float eps) {
-  __shared__ double r1[kGnFinThreads], r2[kGnFinThreads];
-  __shared__ float2 sst[kGnFinStale];
-  const int b = blockIdx.x;
-  const int t = threadIdx.x;
-  const int nparts = kGnFinThreads / G;  // G <= 256 (host check)
-  const int g = t % G, part = t / G;
-  const bool stage_stale = stale != nullptr && coef != nullptr && P * G <= kGnFinStale;
-  if (stage_stale)
-    for (int i = t; i < P * G; i += kGnFinThreads)
-      sst[i] = *reinterpret_cast<const float2*>(stale + (static_cast<int64_t>(b) * P * G + i) * 2);
+  const int g = blockIdx.x, b = blockIdx.y;
+  const int l = threadIdx.x;
+  const float* base = partial + (static_cast<int64_t>(b) * nchunk * G + g) * 2;
+  double sa = 0.0, sc = 0.0;  // stale sums of the other patches
+  if (stale != nullptr && coef != nullptr)
+    for (int q = l; q < P; q += kWave)
+      if (q != p) {
+        const float2 st = *reinterpret_cast<const float2*>(stale + ((static_cast<int64_t>(b) * P + q) * G + g) * 2);
+        sa += st.x;
+        sc += st.y;
+      }
   double a = 0.0, c = 0.0;
-  if (part < nparts) {
-    const float* base = partial + (static_cast<int64_t>(b) * nchunk * G + g) * 2;
-    int64_t ch = part;
-    for (; ch + (kGnFinLoads - 1) * nparts < nchunk; ch += kGnFinLoads * nparts) {
-      float2 v[kGnFinLoads];
+  int64_t ch = l;
+  for (; ch + (kGnFinLoads - 1) * kWave < nchunk; ch += kGnFinLoads * kWave) {
+    float2 v[kGnFinLoads];
 #pragma unroll
-      for (int j = 0; j < kGnFinLoads; ++j) v[j] = *reinterpret_cast<const float2*>(base + (ch + j * nparts) * G * 2);
+    for (int j = 0; j < kGnFinLoads; ++j) v[j] = *reinterpret_cast<const float2*>(base + (ch + j * kWave) * G * 2);
 #pragma unroll
-      for (int j = 0; j < kGnFinLoads; ++j) { a += v[j].x; c += v[j].y; }
-    }
-    for (; ch < nchunk; ch += nparts) {
-      const float2 v = *reinterpret_cast<const float2*>(base + ch * G * 2);
-      a += v.x;
-      c += v.y;
-    }
+    for (int j = 0; j < kGnFinLoads; ++j) { a += v[j].x; c += v[j].y; }
   }
-  r1[t] = a;
-  r2[t] = c;
-  __syncthreads();
-  if (t < G) {
-    double s1 = 0.0, s2 = 0.0;
-    for (int q = 0; q < nparts; ++q) { s1 += r1[q * G + t]; s2 += r2[q * G + t]; }
-    float* so = stats_out + ((static_cast<int64_t>(b) * P + p) * G + t) * 2;
-    so[0] = static_cast<float>(s1);
-    so[1] = static_cast<float>(s2);
-    if (coef != nullptr) {
-      double T1 = s1, T2 = s2;
-      if (stale != nullptr)
-        for (int q = 0; q < P; ++q)
-          if (q != p) {
-            const float2 st = stage_stale ? sst[q * G + t]
-                                          : *reinterpret_cast<const float2*>(stale + ((static_cast<int64_t>(b) * P + q) * G + t) * 2);
-            T1 += st.x;
-            T2 += st.y;
-          }
-      const double mean = T1 / n;
-      double var = T2 / n - mean * mean;
-      if (var < 0.0) var = 0.0;
-      const double rstd = 1.0 / sqrt(var + static_cast<double>(eps));
-      coef[(static_cast<int64_t>(b) * G + t) * 2] = static_cast<float>(mean);
-      coef[(static_cast<int64_t>(b) * G + t) * 2 + 1] = static_cast<float>(rstd);
-    }
+  for (; ch < nchunk; ch += kWave) {
+    const float2 v = *reinterpret_cast<const float2*>(base + ch * G * 2);
+    a += v.x;
+    c += v.y;
   }
+#pragma unroll
+  for (int off = kWave / 2; off > 0; off >>= 1) {
+    a += __shfl_xor(a, off, kWave);
+    c += __shfl_xor(c, off, kWave);
+    sa += __shfl_xor(sa, off, kWave);
+    sc += __shfl_xor(sc, off, kWave);
+  }
+  if (l != 0) return;
+  float* so = stats_out + ((static_cast<int64_t>(b) * P + p) * G + g) * 2;
+  so[0] = static_cast<float>(a);
+  so[1] = static_cast<float>(c);
+  if (coef == nullptr) return;
+  const double T1 = a + sa, T2 = c + sc;
+  const double mean = T1 / n;
+  double var = T2 / n - mean * mean;
+  if (var < 0.0) var = 0.0;
+  const double rstd = 1.0 / sqrt(var + static_cast<double>(eps));
+  coef[(static_cast<int64_t>(b) * G + g) * 2] = static_cast<float>(mean);
+  coef[(static_cast<int64_t>(b) * G + g) * 2 + 1] = static_cast<float>(rstd);
 }
 
 // SiLU z sigmoid(z) = z / (1 + 2^(-z log2 e)): large negative z gives
@@ -270,7 +260,8 @@ static hipError_t gn_run(T* y, float* stats_out, const T* x, const float* stale,
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   const double n = static_cast<double>(H) * static_cast<double>(W) * static_cast<double>(C / G);
-  hipLaunchKernelGGL(gn_finalize_kernel, dim3(static_cast<unsigned>(B)), dim3(kGnFinThreads), 0, s, partial, g.nstat,
+  hipLaunchKernelGGL(gn_finalize_kernel, dim3(static_cast<unsigned>(G), static_cast<unsigned>(B)), dim3(kWave), 0, s,
+                     partial, g.nstat,
                      stale, stats_out, y ? coef : nullptr, static_cast<int>(G), static_cast<int>(P),
                      static_cast<int>(p), n, eps);
   err = hipGetLastError();
