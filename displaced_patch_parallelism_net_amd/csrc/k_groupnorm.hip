@@ -115,17 +115,33 @@ __global__ __launch_bounds__(kGnMaxThreads) void gn_partial_kernel(const T* __re
     }
   }
   __syncthreads();
-  const int cg = C / G;
-  for (int g = t; g < G; g += blockDim.x) {
-    float a = 0.f, c = 0.f;
-    for (int kk = 0; kk < KP; ++kk)
-      for (int ch = g * cg; ch < (g + 1) * cg; ++ch) {
+  // Fold channels into groups: eight consecutive lanes per group, lane j
+  // summing the group's (pixel column, channel) values j, j + 8, ..., then a
+  // fixed xor butterfly over the eight lanes.  Only whole eight-lane sets
+  // take part (blockDim need not be a multiple of 8).
+  constexpr int kFold = 8;
+  const int cg = C / G, nv = KP * cg;
+  const int sets = static_cast<int>(blockDim.x) / kFold;
+  const int j = t % kFold;
+  if (t < sets * kFold) {
+    for (int g = t / kFold; g < G; g += sets) {
+      float a = 0.f, c = 0.f;
+      for (int i = j; i < nv; i += kFold) {
+        const int kk = i / cg, ch = g * cg + i % cg;
         a += red1[kk * C + ch];
         c += red2[kk * C + ch];
       }
-    float* out = partial + ((static_cast<int64_t>(b) * nchunk + chunk) * G + g) * 2;
-    out[0] = a;
-    out[1] = c;
+#pragma unroll
+      for (int off = kFold / 2; off > 0; off >>= 1) {
+        a += __shfl_xor(a, off, kFold);
+        c += __shfl_xor(c, off, kFold);
+      }
+      if (j == 0) {
+        float* out = partial + ((static_cast<int64_t>(b) * nchunk + chunk) * G + g) * 2;
+        out[0] = a;
+        out[1] = c;
+      }
+    }
   }
 }
 
