@@ -76,6 +76,8 @@ GN_CASES = [(n, None) for n in ["tiny_f32", "sdxl_1024", "sdxl_2048", "sdxl_3840
     ("ragged_bf16", Config("rg", B=2, H=9, W=7, C=96, P=3, G=12, heads=1, D=96)),
     ("ragged_f32", Config("rgf", B=2, H=10, W=3, C=12, P=5, G=3, heads=1, D=12, dtype="f32")),
     ("one_patch", Config("g1", B=1, H=6, W=11, C=64, P=1, G=32, heads=1, D=64)),
+    ("group_per_channel", Config("gpc", B=2, H=5, W=7, C=64, P=5, G=64, heads=1, D=64)),   # 1 channel per group
+    ("one_group", Config("g1g", B=1, H=6, W=9, C=128, P=3, G=1, heads=2, D=64)),          # 128 channels, 1 group
 ]
 
 
