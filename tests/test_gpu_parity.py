@@ -497,6 +497,26 @@ def test_attention_growing_scores_rescale_often(split):
     parity(to_host(o), want, "bf16", f"attn growing scores {'split' if split else 'unsplit'}")
 
 
+def test_attention_single_key_returns_its_value():
+    # One key: every softmax weight is exactly 1, so o = v of that key; the
+    # bf16 result must equal v bit for bit (B = 3, 3 heads, 37 queries).
+    dpp = _dpp()
+    rng = np.random.default_rng(6)
+    from dpp_synth import f32_to_bf16_bits
+    B, nq, heads = 3, 37, 3
+    hd = heads * 64
+    say("attention single key")
+    q = f32_to_bf16_bits(rng.standard_normal((B, nq, hd)).astype(np.float32))
+    k = f32_to_bf16_bits(rng.standard_normal((B, 1, hd)).astype(np.float32))
+    v = f32_to_bf16_bits(rng.standard_normal((B, 1, hd)).astype(np.float32))
+    o = torch.empty(B, nq, hd, dtype=torch.bfloat16, device="cuda")
+    wsb = dpp.dpp_self_attn_workspace_bytes(B, nq, 1, heads, 64, 0)
+    ws = torch.empty(wsb, dtype=torch.uint8, device="cuda") if wsb else None
+    dpp.dpp_self_attn_displaced(o, to_dev(q, "bf16"), to_dev(k, "bf16"), to_dev(v, "bf16"), heads, 64, 0.0, ws)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(bits(o), np.broadcast_to(v, (B, nq, hd)))
+
+
 def test_attention_closed_form_zero_query():
     # Q = 0: uniform weights, output = mean of V over all keys
     dpp = _dpp()
@@ -534,6 +554,7 @@ CFG_CASES = [
     ("misaligned_bf16", "bf16", 4099, 1),
     ("f32", "f32", 777, 0),
     ("f32_large", "f32", 3_000_001, 0),
+    ("single_element", "bf16", 1, 0),
 ]
 
 

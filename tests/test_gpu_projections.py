@@ -48,6 +48,7 @@ LINEAR_CASES = [
     ("wide_ragged", 2, 3001, 328, 1152, 336, 1160, True, "bf16"),      # 256-channel tiles, half-empty last tile, generic K
     ("ragged_strided", 2, 301, 200, 84, 208, 96, True, "bf16"),
     ("no_bias", 1, 130, 64, 128, 64, 128, False, "bf16"),
+    ("minimal", 1, 1, 8, 4, 8, 4, True, "bf16"),                      # smallest bf16 shape: 1 token, K = 8, N = 4
     ("f32", 2, 37, 24, 20, 30, 22, True, "f32"),
 ]
 
