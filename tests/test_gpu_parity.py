@@ -652,6 +652,50 @@ def test_block_parity(name, patches):
     _block_case(CONFIGS[name], patches)
 
 
+def test_step_is_bitwise_deterministic():
+    # Every kernel reduces in a fixed order (no atomics): two runs of the
+    # 3840 px patch step, workspaces and launch configuration as the benchmark
+    # uses them (attention key splits; conv without split at this band),
+    # give identical bits in every output and statistic; so do two calls of
+    # the split-K conv.
+    from displaced_patch_parallelism_net_amd.step import DisplacedLayer
+    cfg = CONFIGS["sdxl_3840"]
+    inp = layer_inputs(cfg)
+    say("step determinism", cfg.name)
+    gamma, beta = torch.from_numpy(inp["gamma"]).cuda(), torch.from_numpy(inp["beta"]).cuda()
+    w, b = to_dev(inp["conv_w"], cfg.dtype), torch.from_numpy(inp["conv_b"]).cuda()
+    xs, xf = to_dev(inp["x_stale"], cfg.dtype), to_dev(inp["x_fresh"], cfg.dtype)
+    runs = []
+    for _ in range(2):
+        layer = DisplacedLayer(cfg.B, cfg.H, cfg.W, cfg.C, cfg.P, cfg.G, cfg.heads, tdt(cfg.dtype), eps=cfg.gn_eps,
+                               head_dim=cfg.D)
+        layer.synchronous_step(xs, gamma, beta, w, b)
+        p = cfg.P - 1
+        o = layer.patch_step(p, layer.band(xf, p), gamma, beta, w, b)
+        torch.cuda.synchronize()
+        runs.append([bits(layer.a2), bits(layer.y1), bits(layer.y2), bits(o), layer.stats_next.cpu().numpy().copy()])
+    for a_, b_ in zip(*runs):
+        np.testing.assert_array_equal(a_, b_)
+    # the split-K conv (1024 px band: float32 partials, ordered reduction)
+    dpp = _dpp()
+    c2 = CONFIGS["sdxl_1024"]
+    i2 = layer_inputs(c2)
+    r0 = c2.row0(1)
+    x = to_dev(rows_of(i2["x_fresh"], r0, c2.rows), c2.dtype)
+    st, w2 = to_dev(i2["x_stale"], c2.dtype), to_dev(i2["conv_w"], c2.dtype)
+    b2 = torch.from_numpy(i2["conv_b"]).cuda()
+    wsb = dpp.dpp_conv3x3_halo_workspace_bytes(c2.B, c2.rows, c2.W, c2.C, c2.C)
+    assert wsb > 0
+    ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+    outs = []
+    for _ in range(2):
+        y = torch.empty(c2.B, c2.rows, c2.W, c2.C, dtype=tdt(c2.dtype), device="cuda")
+        dpp.dpp_conv3x3_halo(y, x, st, w2, b2, c2.H, r0, workspace=ws)
+        torch.cuda.synchronize()
+        outs.append(bits(y))
+    np.testing.assert_array_equal(outs[0], outs[1])
+
+
 def test_block_parity_full_size_sampled():
     # The 3840 px step exactly as the benchmark runs it (DisplacedLayer with
     # its GroupNorm, conv and attention workspaces): previous-step state,
