@@ -696,6 +696,34 @@ def test_step_is_bitwise_deterministic():
     np.testing.assert_array_equal(outs[0], outs[1])
 
 
+def test_step_on_a_side_stream_matches_the_default_stream():
+    # The binding passes PyTorch's current stream to every call: the patch
+    # step issued on a side stream (created at the default priority) gives the
+    # same bits as on the default stream.
+    from displaced_patch_parallelism_net_amd.step import DisplacedLayer
+    cfg = CONFIGS["sdxl_1024"]
+    inp = layer_inputs(cfg)
+    say("step on a side stream", cfg.name)
+    gamma, beta = torch.from_numpy(inp["gamma"]).cuda(), torch.from_numpy(inp["beta"]).cuda()
+    w, b = to_dev(inp["conv_w"], cfg.dtype), torch.from_numpy(inp["conv_b"]).cuda()
+    xs, xf = to_dev(inp["x_stale"], cfg.dtype), to_dev(inp["x_fresh"], cfg.dtype)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    results = []
+    for stream in (None, side):
+        layer = DisplacedLayer(cfg.B, cfg.H, cfg.W, cfg.C, cfg.P, cfg.G, cfg.heads, tdt(cfg.dtype), eps=cfg.gn_eps,
+                               head_dim=cfg.D)
+        torch.cuda.synchronize()
+        ctx = torch.cuda.stream(stream) if stream is not None else torch.cuda.stream(torch.cuda.current_stream())
+        with ctx:
+            layer.synchronous_step(xs, gamma, beta, w, b)
+            o = layer.patch_step(2, layer.band(xf, 2), gamma, beta, w, b)
+        torch.cuda.synchronize()
+        results.append([bits(layer.y2), bits(o), layer.stats_next.cpu().numpy().copy()])
+    for a_, b_ in zip(*results):
+        np.testing.assert_array_equal(a_, b_)
+
+
 def test_block_parity_full_size_sampled():
     # The 3840 px step exactly as the benchmark runs it (DisplacedLayer with
     # its GroupNorm, conv and attention workspaces): previous-step state,
