@@ -176,6 +176,20 @@ def cpu_baseline(cfg, budget_s):
     }
 
 
+def release_device_memory():
+    """Free every cached device block while the HIP runtime (and a profiler
+    attached to it) is still fully up.  Left to the interpreter's exit, the
+    caching allocator returns its blocks from static destructors that can run
+    after a profiler tool has finalised and torn down its hooks: a host
+    SIGSEGV during exit, after the results were written."""
+    import gc
+    import torch
+    gc.collect()
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    torch.cuda.synchronize()
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -184,7 +198,13 @@ def main():
         sys.exit(2)
     if args.calib_copy:
         calib_copy()
-        return
+    else:
+        out = run(args)
+        print(json.dumps(out), flush=True)
+    release_device_memory()
+
+
+def run(args):
     import torch
     import displaced_patch_parallelism_net_amd as dpp
     from displaced_patch_parallelism_net_amd.step import DisplacedLayer
@@ -318,7 +338,7 @@ def main():
         out["hbm_sweep"] = hbm_sweep(cfg, dpp, torch)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(cfg, args.cpu_budget_s)
-    print(json.dumps(out), flush=True)
+    return out
 
 
 def time_kernels(cfg, layer, x_patches, gamma, beta, w, b, eps, rel, eps_c, eps_u, cfg_ws, dpp, torch, reps=10):

@@ -149,7 +149,9 @@ def dpp_groupnorm_stale_workspace_bytes(B, rows, W, C, G) -> int:
     return int(LIB.dpp_groupnorm_stale_workspace_bytes(B, rows, W, C, G))
 
 
-def _gn_args(y, stats_out, x, stale_stats, gamma, beta, P):
+def _gn_args(y, stats_out, x, stale_stats, gamma, beta, G, P):
+    """The library indexes both statistics arrays as [B,P,G,2] with the P and
+    G it is passed, so anything but exactly that shape is refused here."""
     _contig(y, stats_out, x, stale_stats, gamma, beta)
     _same_dtype(y, x)
     _f32(stats_out, stale_stats, gamma, beta)
@@ -158,13 +160,12 @@ def _gn_args(y, stats_out, x, stale_stats, gamma, beta, P):
     _numel(gamma, C, "gamma")
     _numel(beta, C, "beta")
     for t, what in ((stats_out, "stats_out"), (stale_stats, "stale_stats")):
-        if t is not None and (t.dim() != 4 or t.shape[0] != B or t.shape[1] < P or t.shape[3] != 2):
-            raise ValueError(f"{what}: shape {tuple(t.shape)}, expected [B, P, G, 2] with B = {B}, P = {P}")
+        _shape(t, (B, P, G, 2), what)
 
 
 def dpp_groupnorm_stale(y, stats_out, x, stale_stats, gamma, beta, H: int, G: int, P: int, p: int, eps: float,
                         workspace, stream=None):
-    _gn_args(y, stats_out, x, stale_stats, gamma, beta, P)
+    _gn_args(y, stats_out, x, stale_stats, gamma, beta, G, P)
     B, rows, W, C = x.shape
     _check("dpp_groupnorm_stale",
            LIB.dpp_groupnorm_stale(_ptr(y), _ptr(stats_out), _ptr(x), _ptr(stale_stats), _ptr(gamma), _ptr(beta), B, H,
@@ -175,7 +176,7 @@ def dpp_groupnorm_stale(y, stats_out, x, stale_stats, gamma, beta, H: int, G: in
 
 def dpp_groupnorm_silu_stale(y, stats_out, x, stale_stats, gamma, beta, H: int, G: int, P: int, p: int, eps: float,
                              workspace, stream=None):
-    _gn_args(y, stats_out, x, stale_stats, gamma, beta, P)
+    _gn_args(y, stats_out, x, stale_stats, gamma, beta, G, P)
     B, rows, W, C = x.shape
     _check("dpp_groupnorm_silu_stale",
            LIB.dpp_groupnorm_silu_stale(_ptr(y), _ptr(stats_out), _ptr(x), _ptr(stale_stats), _ptr(gamma), _ptr(beta),

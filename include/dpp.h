@@ -27,8 +27,11 @@
  *  - dtype selects the storage type of activations and conv weights:
  *    DPP_BF16 (bf16 bit patterns) or DPP_F32.  GroupNorm gamma/beta, conv
  *    bias, group statistics and the rel-MAE scalar are always float32.
- *    Arithmetic is float32 (statistics float64) with one rounding to the
- *    output type at the end.
+ *    Arithmetic is float32 (group statistics finalised in float64); every
+ *    bf16 output is stored with one round-to-nearest-even conversion of its
+ *    float32 result.  The one rounding inside a call is the attention's: its
+ *    softmax weights enter the bf16 weight x value product as bf16, while
+ *    the normaliser sums the same weights in float32 before that rounding.
  *  - stream is a hipStream_t passed as void* (NULL = the null stream).  Work
  *    is enqueued on it and the call returns at once; faults inside a kernel
  *    surface at the caller's next synchronisation.
@@ -245,8 +248,10 @@ int dpp_linear(void* y, const void* x, const void* w, const float* bias,
  * branches; section 2B: rel-MAE between their noise predictions).
  *   eps[i]  = eps_u[i] + guidance * (eps_c[i] - eps_u[i])
  *   *relmae = sum_i |eps_c[i] - eps_u[i]| / sum_i |eps_u[i]|
- *             (float64 accumulation, deterministic order; 0/0 -> NaN,
- *              x/0 -> +inf)
+ *             (deterministic order: each thread first adds its own
+ *              elements in float32 -- about 8 * ceil(n / 2^21) of them, 8
+ *              at n = 65536 -- then the workgroup and grid sums are
+ *              float64; 0/0 -> NaN, x/0 -> +inf)
  *   eps, eps_c, eps_u: n elements; eps may be exactly eps_c or eps_u, and
  *   must not partly overlap them.  relmae: one device float32, or NULL to
  *   skip the reduction.  Workspace: dpp_cfg_combine_workspace_bytes(n)

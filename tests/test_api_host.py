@@ -310,3 +310,29 @@ def test_binding_refuses_host_tensors_and_mismatches():
     with pytest.raises(ValueError, match="bias"):
         dpp.dpp_linear(torch.zeros(4, 8, dtype=bf), torch.zeros(4, 16, dtype=bf), torch.zeros(8, 16, dtype=bf),
                        torch.zeros(4))
+
+
+def test_binding_requires_exact_statistics_shape():
+    # The library indexes stats_out and stale_stats as [B,P,G,2] with the P
+    # and G it is passed: fewer groups would be written past their end, more
+    # patch slots (B > 1) in the wrong layout.  The binding refuses both.
+    import torch
+    bf = torch.bfloat16
+    x = torch.zeros(2, 2, 4, 64, dtype=bf)
+    g = torch.ones(64)
+    good = torch.zeros(2, 3, 8, 2)
+    for bad, what in ((torch.zeros(2, 3, 4, 2), "stats_out"),      # fewer groups than G
+                      (torch.zeros(2, 4, 8, 2), "stats_out"),      # more patch slots than P
+                      (torch.zeros(1, 3, 8, 2), "stats_out"),      # batch mismatch
+                      (torch.zeros(2, 3, 8, 3), "stats_out")):     # not (sum, sum of squares)
+        with pytest.raises(ValueError, match=what):
+            dpp.dpp_groupnorm_stale(x.clone(), bad, x, good, g, g, 6, 8, 3, 1, 1e-5, None)
+        with pytest.raises(ValueError, match=what):
+            dpp.dpp_groupnorm_silu_stale(x.clone(), bad, x, good, g, g, 6, 8, 3, 1, 1e-5, None)
+    for bad in (torch.zeros(2, 3, 16, 2), torch.zeros(2, 2, 8, 2)):
+        with pytest.raises(ValueError, match="stale_stats"):
+            dpp.dpp_groupnorm_stale(x.clone(), good, x, bad, g, g, 6, 8, 3, 1, 1e-5, None)
+    # the exact shape passes every binding check and stops at the host-tensor check
+    with pytest.raises(ValueError, match="GPU"):
+        dpp.dpp_groupnorm_stale(x.clone(), good, x, torch.zeros(2, 3, 8, 2), g, g, 6, 8, 3, 1, 1e-5, None)
+

@@ -8,7 +8,7 @@ import pytest
 
 import oracle
 from dpp_synth import CONFIGS, Config, attention_inputs, cfg_inputs, layer_inputs, rows_of, tokens, values
-from tests._helpers import REL_TOL, bits, parity, to_dev, to_host
+from tests._helpers import REL_TOL, bits, check_guards, guarded_copy, guarded_empty, parity, to_dev, to_host
 
 pytestmark = pytest.mark.gpu
 
@@ -50,10 +50,11 @@ def test_splice_bit_exact(name, cfg):
     inp = layer_inputs(cfg)
     for p in sorted({0, cfg.P - 1, cfg.P // 2}):
         say("splice", name, "patch", p)
-        full = to_dev(inp["x_stale"], cfg.dtype)
+        fbase, full = guarded_copy(to_dev(inp["x_stale"], cfg.dtype))
         patch = to_dev(rows_of(inp["x_fresh"], cfg.row0(p), cfg.rows), cfg.dtype)
         dpp.dpp_splice_patch(full, patch, cfg.row0(p))
         torch.cuda.synchronize()
+        check_guards(fbase, f"splice {name} p{p}")
         want = oracle.splice(inp["x_stale"], rows_of(inp["x_fresh"], cfg.row0(p), cfg.rows), cfg.row0(p))
         np.testing.assert_array_equal(bits(full), want.view(np.uint16 if cfg.dtype == "bf16" else np.uint32))
 
@@ -96,11 +97,14 @@ def test_groupnorm_stale_parity(name, cfg):
         say("groupnorm", name, "patch", p)
         x_np = rows_of(inp["x_fresh"], cfg.row0(p), cfg.rows)
         x = to_dev(x_np, cfg.dtype)
-        y = torch.empty_like(x)
-        so = torch.full((cfg.B, cfg.P, cfg.G, 2), 7.0, device="cuda")
+        ybase, y = guarded_empty(tuple(x.shape), x.dtype)
+        sbase, so = guarded_empty((cfg.B, cfg.P, cfg.G, 2), torch.float32)
+        so.fill_(7.0)
         dpp.dpp_groupnorm_stale(y, so, x, d_stale if cfg.P > 1 else None, gamma, beta, cfg.H, cfg.G, cfg.P, p,
                                 cfg.gn_eps, ws)
         torch.cuda.synchronize()
+        check_guards(ybase, f"gn {name} p{p} y")
+        check_guards(sbase, f"gn {name} p{p} stats_out")
         want_y, want_s = oracle.groupnorm_stale(values(cfg, x_np), stale if cfg.P > 1 else None, inp["gamma"],
                                                 inp["beta"], cfg.H, cfg.G, p, cfg.gn_eps)
         parity(to_host(y), want_y, cfg.dtype, f"gn {name} p{p}")
@@ -194,10 +198,11 @@ def _conv_case(cfg, p, sample=None):
     st = to_dev(inp["x_stale"], cfg.dtype)
     w = to_dev(inp["conv_w"], cfg.dtype)
     b = torch.from_numpy(inp["conv_b"]).cuda()
-    y = torch.empty(cfg.B, cfg.rows, cfg.W, cfg.C, dtype=tdt(cfg.dtype), device="cuda")
+    ybase, y = guarded_empty((cfg.B, cfg.rows, cfg.W, cfg.C), tdt(cfg.dtype))
     only_patch = cfg.P == 1
     dpp.dpp_conv3x3_halo(y, x, None if only_patch else st, w, b, cfg.H, r0)
     torch.cuda.synchronize()
+    check_guards(ybase, f"conv {cfg.name} p{p}")
     yh = to_host(y)
     xv, sv, wv = values(cfg, x_np), values(cfg, inp["x_stale"]), values(cfg, inp["conv_w"])
     if sample is None:
@@ -252,11 +257,12 @@ def test_conv_ragged_cout(B, H, W, Cin, Cout, r0, R):
     wt = (0.05 * rng.standard_normal((Cout, 3, 3, Cin))).astype(np.float32)
     from dpp_synth import f32_to_bf16_bits
     xs_b, xp_b, w_b = (f32_to_bf16_bits(a) for a in (xs, xp, wt))
-    y = torch.empty(B, R, W, Cout, dtype=torch.bfloat16, device="cuda")
+    ybase, y = guarded_empty((B, R, W, Cout), torch.bfloat16)
     whole = r0 == 0 and R == H
     dpp.dpp_conv3x3_halo(y, to_dev(xp_b, "bf16"), None if whole else to_dev(xs_b, "bf16"), to_dev(w_b, "bf16"),
                          None, H, r0)
     torch.cuda.synchronize()
+    check_guards(ybase, "conv ragged cout")
     want = oracle.conv3x3_halo(values("bf16", xp_b), None if whole else values("bf16", xs_b), values("bf16", w_b),
                                None, r0)
     parity(to_host(y), want, "bf16", "conv ragged cout")
@@ -276,12 +282,14 @@ def test_conv_split_k_parity(name, p):
     x, st, w = to_dev(x_np, cfg.dtype), to_dev(inp["x_stale"], cfg.dtype), to_dev(inp["conv_w"], cfg.dtype)
     b = torch.from_numpy(inp["conv_b"]).cuda()
     ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
-    y = torch.empty(cfg.B, cfg.rows, cfg.W, cfg.C, dtype=tdt(cfg.dtype), device="cuda")
-    y1 = torch.empty_like(y)
+    ybase, y = guarded_empty((cfg.B, cfg.rows, cfg.W, cfg.C), tdt(cfg.dtype))
+    y1base, y1 = guarded_empty((cfg.B, cfg.rows, cfg.W, cfg.C), tdt(cfg.dtype))
     say("conv split-K", name, "patch", p, "workspace", wsb)
     dpp.dpp_conv3x3_halo(y, x, st, w, b, cfg.H, r0, workspace=ws)
     dpp.dpp_conv3x3_halo(y1, x, st, w, b, cfg.H, r0)
     torch.cuda.synchronize()
+    check_guards(ybase, f"conv split-K {name} p{p}")
+    check_guards(y1base, f"conv unsplit {name} p{p}")
     want = oracle.conv3x3_halo(values(cfg, x_np), values(cfg, inp["x_stale"]), values(cfg, inp["conv_w"]),
                                inp["conv_b"], r0)
     parity(to_host(y), want, cfg.dtype, f"conv split-K {name} p{p}")
@@ -305,11 +313,12 @@ def test_conv_split_k_ragged(B, H, W, Cin, Cout, r0, R, with_bias):
     wt = f32_to_bf16_bits((0.05 * rng.standard_normal((Cout, 3, 3, Cin))).astype(np.float32))
     bias = (0.1 * rng.standard_normal(Cout)).astype(np.float32) if with_bias else None
     whole = r0 == 0 and R == H
-    y = torch.empty(B, R, W, Cout, dtype=torch.bfloat16, device="cuda")
+    ybase, y = guarded_empty((B, R, W, Cout), torch.bfloat16)
     ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
     dpp.dpp_conv3x3_halo(y, to_dev(xp, "bf16"), None if whole else to_dev(xs, "bf16"), to_dev(wt, "bf16"),
                          None if bias is None else torch.from_numpy(bias).cuda(), H, r0, workspace=ws)
     torch.cuda.synchronize()
+    check_guards(ybase, "conv split-K ragged")
     want = oracle.conv3x3_halo(values("bf16", xp), None if whole else values("bf16", xs), values("bf16", wt), bias, r0)
     parity(to_host(y), want, "bf16", "conv split-K ragged")
 
@@ -367,11 +376,12 @@ def _attn_case(cfg, p, sample_rows=None, use_ws=True, what=""):
     dpp.dpp_splice_patch(k_d, to_dev(kf, cfg.dtype), r0)
     dpp.dpp_splice_patch(v_d, to_dev(vf, cfg.dtype), r0)
     q_d = to_dev(q_np, cfg.dtype)
-    o = torch.empty(B, cfg.Nq, C, dtype=tdt(cfg.dtype), device="cuda")
+    obase, o = guarded_empty((B, cfg.Nq, C), tdt(cfg.dtype))
     wsb = dpp.dpp_self_attn_workspace_bytes(B, cfg.Nq, cfg.N, cfg.heads, cfg.D, 0 if cfg.dtype == "bf16" else 1)
     ws = torch.empty(wsb, dtype=torch.uint8, device="cuda") if (use_ws and wsb) else None
     dpp.dpp_self_attn_displaced(o, q_d, k_d.view(B, cfg.N, C), v_d.view(B, cfg.N, C), cfg.heads, cfg.D, 0.0, ws)
     torch.cuda.synchronize()
+    check_guards(obase, f"attn {cfg.name} p{p} {what}")
     kk = tokens(oracle.splice(values(cfg, img(inp["k_stale"])), values(cfg, kf), r0))
     vv = tokens(oracle.splice(values(cfg, img(inp["v_stale"])), values(cfg, vf), r0))
     qv = values(cfg, q_np)
@@ -453,9 +463,10 @@ def test_attention_many_key_splits():
         nsplit = wsb // (B * heads * nq * 66 * 4)
         assert nsplit > 8, (B, nq, nkv, heads, nsplit)
         ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
-        o = torch.empty(B, nq, hd, dtype=torch.bfloat16, device="cuda")
+        obase, o = guarded_empty((B, nq, hd), torch.bfloat16)
         dpp.dpp_self_attn_displaced(o, to_dev(q, "bf16"), to_dev(k, "bf16"), to_dev(v, "bf16"), heads, 64, 0.0, ws)
         torch.cuda.synchronize()
+        check_guards(obase, f"attn {nsplit} splits")
         want = oracle.self_attn_displaced(values("bf16", q), values("bf16", k), values("bf16", v), heads)
         parity(to_host(o), want, "bf16", f"attn {nsplit} splits {B},{nq},{nkv}")
 
@@ -490,9 +501,10 @@ def test_attention_growing_scores_rescale_often(split):
         wsb = dpp.dpp_self_attn_workspace_bytes(B, nq, nkv, heads, 64, 0)
         assert wsb > 0
         ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
-    o = torch.empty(B, nq, hd, dtype=torch.bfloat16, device="cuda")
+    obase, o = guarded_empty((B, nq, hd), torch.bfloat16)
     dpp.dpp_self_attn_displaced(o, to_dev(qb, "bf16"), to_dev(kb, "bf16"), to_dev(vb, "bf16"), heads, 64, 0.0, ws)
     torch.cuda.synchronize()
+    check_guards(obase, "attn growing scores")
     want = oracle.self_attn_displaced(values("bf16", qb), values("bf16", kb), values("bf16", vb), heads)
     parity(to_host(o), want, "bf16", f"attn growing scores {'split' if split else 'unsplit'}")
 
@@ -566,11 +578,16 @@ def test_cfg_combine_parity(name, dtype, n, offset):
     inp = cfg_inputs(cfg, n=n + offset)
     c_all, u_all = to_dev(inp["eps_c"], dtype), to_dev(inp["eps_u"], dtype)
     c, u = c_all[offset:], u_all[offset:]        # offset 1 element: unaligned views -> scalar path
-    eps = torch.empty(n + offset, dtype=tdt(dtype), device="cuda")[offset:]
+    ebase, eps_all = guarded_empty((n + offset,), tdt(dtype))
+    if offset:
+        eps_all[:offset].fill_(0.25)
+    eps = eps_all[offset:]
     rel = torch.full((1,), -1.0, device="cuda")
     ws = torch.empty(dpp.dpp_cfg_combine_workspace_bytes(n), dtype=torch.uint8, device="cuda")
     dpp.dpp_cfg_combine_relmae(eps, rel, c, u, 7.5, ws)
     torch.cuda.synchronize()
+    check_guards(ebase, f"cfg eps {name}")
+    assert torch.all(eps_all[:offset] == 0.25), "cfg wrote before its output view"
     want_eps, want_rel = oracle.cfg_combine_relmae(values(dtype, inp["eps_c"])[offset:],
                                                    values(dtype, inp["eps_u"])[offset:], 7.5)
     parity(to_host(eps), want_eps, dtype, f"cfg eps {name}")
