@@ -16,6 +16,7 @@ from ._lib import (  # noqa: F401
     dpp_conv3x3_halo_workspace_bytes,
     dpp_groupnorm_silu_stale,
     dpp_groupnorm_stale,
+    dpp_groupnorm_stale_noalloc,
     dpp_groupnorm_stale_workspace_bytes,
     dpp_hybrid_schedule,
     dpp_linear,

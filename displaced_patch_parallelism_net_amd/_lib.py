@@ -33,6 +33,8 @@ SIGNATURES = {
                                  _vp, _sz, _i, _vp]),
     "dpp_groupnorm_silu_stale": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _i64, _i64, _i64,
                                       _f, _vp, _sz, _i, _vp]),
+    "dpp_groupnorm_stale_noalloc": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _i64, _i64,
+                                         _i64, _f, _i, _vp]),
     "dpp_conv3x3_halo": (_i, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _i64, _i64, _i, _vp]),
     "dpp_conv3x3_halo_workspace_bytes": (_sz, [_i64, _i64, _i64, _i64, _i64]),
     "dpp_conv3x3_halo_ws": (_i, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _i64, _i64, _vp, _sz, _i,
@@ -183,6 +185,20 @@ def dpp_groupnorm_silu_stale(y, stats_out, x, stale_stats, gamma, beta, H: int, 
                                         B, H, W, C, G, P, p, rows, eps, _ptr(workspace),
                                         0 if workspace is None else workspace.numel() * workspace.element_size(),
                                         _dtype(x), _stream(stream)))
+
+
+GN_NOALLOC_MAX_BYTES = 1 << 20   # DPP_GN_NOALLOC_MAX_BYTES
+
+
+def dpp_groupnorm_stale_noalloc(y, stats_out, x, stale_stats, gamma, beta, H: int, G: int, P: int, p: int,
+                                eps: float, stream=None):
+    """dpp_groupnorm_stale with the library's static per-device scratch
+    instead of a caller workspace (no device allocation in the call)."""
+    _gn_args(y, stats_out, x, stale_stats, gamma, beta, G, P)
+    B, rows, W, C = x.shape
+    _check("dpp_groupnorm_stale_noalloc",
+           LIB.dpp_groupnorm_stale_noalloc(_ptr(y), _ptr(stats_out), _ptr(x), _ptr(stale_stats), _ptr(gamma),
+                                           _ptr(beta), B, H, W, C, G, P, p, rows, eps, _dtype(x), _stream(stream)))
 
 
 def dpp_linear(y, x, w, bias=None, stream=None):

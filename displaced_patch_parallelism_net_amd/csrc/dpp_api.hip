@@ -63,10 +63,10 @@ size_t dpp_groupnorm_stale_workspace_bytes(int64_t B, int64_t rows, int64_t W, i
 }  // extern "C"
 
 namespace {
-int groupnorm_call(void* y, float* stats_out, const void* x, const float* stale_stats, const float* gamma,
-                   const float* beta, int64_t B, int64_t H, int64_t W, int64_t C, int64_t G, int64_t P, int64_t p,
-                   int64_t rows, float eps, void* workspace, size_t workspace_bytes, int dtype, bool silu,
-                   void* stream) {
+// Every check of a GroupNorm call except those of its workspace.
+int groupnorm_validate(void* y, float* stats_out, const void* x, const float* stale_stats, const float* gamma,
+                       const float* beta, int64_t B, int64_t H, int64_t W, int64_t C, int64_t G, int64_t P, int64_t p,
+                       int64_t rows, float eps, int dtype) {
   if (bad_dtype(dtype)) return DPP_ERR_DTYPE;
   if (!x || !stats_out) return DPP_ERR_NULL;
   if (y && (!gamma || !beta)) return DPP_ERR_NULL;
@@ -84,6 +84,18 @@ int groupnorm_call(void* y, float* stats_out, const void* x, const float* stale_
   if (stale_stats && overlap(stats_out, st, stale_stats, st)) return DPP_ERR_ALIAS;
   if (y && (overlap(y, act, x, act) || overlap(y, act, stats_out, st))) return DPP_ERR_ALIAS;
   if (y && stale_stats && overlap(y, act, stale_stats, st)) return DPP_ERR_ALIAS;
+  return DPP_OK;
+}
+
+int groupnorm_call(void* y, float* stats_out, const void* x, const float* stale_stats, const float* gamma,
+                   const float* beta, int64_t B, int64_t H, int64_t W, int64_t C, int64_t G, int64_t P, int64_t p,
+                   int64_t rows, float eps, void* workspace, size_t workspace_bytes, int dtype, bool silu,
+                   void* stream) {
+  const int rc = groupnorm_validate(y, stats_out, x, stale_stats, gamma, beta, B, H, W, C, G, P, p, rows, eps, dtype);
+  if (rc != DPP_OK) return rc;
+  const int es = esize_of(dtype);
+  const int64_t act = B * rows * W * C * es;
+  const int64_t st = B * P * G * 2 * 4;
   const size_t need = dpp::gn_workspace_bytes(B, rows, W, C, G);
   if (!workspace || workspace_bytes < need) return DPP_ERR_WORKSPACE;
   if (overlap(workspace, static_cast<int64_t>(need), x, act) || overlap(workspace, static_cast<int64_t>(need), stats_out, st) ||
@@ -109,6 +121,20 @@ int dpp_groupnorm_silu_stale(void* y, float* stats_out, const void* x, const flo
                              void* stream) {
   return groupnorm_call(y, stats_out, x, stale_stats, gamma, beta, B, H, W, C, G, P, p, rows, eps, workspace,
                         workspace_bytes, dtype, true, stream);
+}
+
+int dpp_groupnorm_stale_noalloc(void* y, float* stats_out, const void* x, const float* stale_stats,
+                                const float* gamma, const float* beta, int64_t B, int64_t H, int64_t W, int64_t C,
+                                int64_t G, int64_t P, int64_t p, int64_t rows, float eps, int dtype, void* stream) {
+  const int rc = groupnorm_validate(y, stats_out, x, stale_stats, gamma, beta, B, H, W, C, G, P, p, rows, eps, dtype);
+  if (rc != DPP_OK) return rc;
+  // the shape's scratch must fit the library's static array
+  static_assert(DPP_GN_NOALLOC_MAX_BYTES == (1u << 20), "header limit and scratch size agree");
+  if (dpp::gn_workspace_bytes(B, rows, W, C, G) > dpp::gn_scratch_bytes()) return DPP_ERR_WORKSPACE;
+  void* scratch = nullptr;
+  if (dpp::gn_scratch_ptr(&scratch) != hipSuccess) return DPP_ERR_LAUNCH;
+  return launch_status(dpp::launch_groupnorm(y, stats_out, x, stale_stats, gamma, beta, B, H, W, C, G, P, p, rows, eps,
+                                             scratch, dtype == DPP_BF16, false, static_cast<hipStream_t>(stream)));
 }
 
 // ------------------------------------------------------------------ a3

@@ -111,6 +111,8 @@ hipError_t launch_splice(void* full, const void* patch, int64_t B, int64_t H, in
                          int64_t row0, int64_t rows, int esize, hipStream_t s);
 
 size_t gn_workspace_bytes(int64_t B, int64_t rows, int64_t W, int64_t C, int64_t G);
+size_t gn_scratch_bytes();
+hipError_t gn_scratch_ptr(void** out);
 hipError_t launch_groupnorm(void* y, float* stats_out, const void* x, const float* stale_stats,
                             const float* gamma, const float* beta, int64_t B, int64_t H, int64_t W,
                             int64_t C, int64_t G, int64_t P, int64_t p, int64_t rows, float eps,

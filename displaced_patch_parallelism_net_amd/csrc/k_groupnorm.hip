@@ -18,9 +18,43 @@
 //      an SDXL residual block); one 16-byte load and one streaming store per
 //      vector.
 // The second read of x (step 3) normally hits the 256 MB last-level cache.
+#include <mutex>
+
 #include "dpp_common.h"
 
+// Scratch of the allocation-free GroupNorm entry point (chunk partial sums
+// and per-group mean/rstd, exactly the workspace the other entry points take
+// from the caller).  Each GPU the library runs on holds its own copy until
+// the process ends.  Host code never uses this name as an address: the
+// device address comes from hipGetSymbolAddress, once per device.
+constexpr size_t kGnScratchBytes = size_t(1) << 20;   // DPP_GN_NOALLOC_MAX_BYTES
+static __device__ __align__(256) unsigned char scratch[kGnScratchBytes];
+
 namespace dpp {
+
+size_t gn_scratch_bytes() { return kGnScratchBytes; }
+
+// Device address of this device's scratch array, looked up on the first call
+// made with that device current and kept for later calls.
+hipError_t gn_scratch_ptr(void** out) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* ptr[kMaxDevices] = {};
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    ptr[dev] = p;
+  }
+  *out = ptr[dev];
+  return hipSuccess;
+}
 
 constexpr int kGnMaxThreads = 256;
 constexpr int kGnStatChunks = 256;    // total partial workgroups (over B)

@@ -141,6 +141,32 @@ int dpp_groupnorm_silu_stale(void* y, float* stats_out, const void* x,
                              int dtype, void* stream);
 
 /*
+ * dpp_groupnorm_stale without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  The scratch it needs (the partial sums
+ * and per-group mean/rstd that dpp_groupnorm_stale keeps in its workspace)
+ * lives in a static device array of DPP_GN_NOALLOC_MAX_BYTES inside the
+ * library; each GPU holds its own copy from the first call made with that
+ * device current until the process ends.  The call allocates and frees
+ * nothing.  Shapes whose scratch
+ * (dpp_groupnorm_stale_workspace_bytes) exceeds DPP_GN_NOALLOC_MAX_BYTES
+ * return DPP_ERR_WORKSPACE -- e.g. G = 32 fits every B <= 2048.  All calls on
+ * one GPU share that GPU's array: calls that may overlap on one GPU (several
+ * streams, several host threads without ordering) race and must be ordered
+ * by the caller.  Nothing in the array needs clearing: every element a call
+ * reads was written earlier in the same call.  DPP_ERR_LAUNCH also reports a
+ * failed lookup of the array's device address.  Arguments, statistics,
+ * requirements and results otherwise exactly as dpp_groupnorm_stale.
+ */
+#define DPP_GN_NOALLOC_MAX_BYTES (1u << 20)
+int dpp_groupnorm_stale_noalloc(void* y, float* stats_out, const void* x,
+                                const float* stale_stats, const float* gamma,
+                                const float* beta, int64_t B, int64_t H,
+                                int64_t W, int64_t C, int64_t G, int64_t P,
+                                int64_t p, int64_t rows, float eps, int dtype,
+                                void* stream);
+
+/*
  * a3 -- 3x3 convolution of the patch rows with halo rows from the stale image
  * (DistriConv2dPP; DistriFusion architecture article, conv section; only the
  * own region is computed: DistriFusion reading notes, Introduction, fourth

@@ -38,7 +38,7 @@ def header_symbols():
 
 def test_header_symbols_exported_and_bound():
     syms = header_symbols()
-    assert len(syms) == 15, syms
+    assert len(syms) == 16, syms
     for s in syms:
         assert hasattr(L, s), s
         assert s in _lib.SIGNATURES, s
@@ -336,3 +336,26 @@ def test_binding_requires_exact_statistics_shape():
     with pytest.raises(ValueError, match="GPU"):
         dpp.dpp_groupnorm_stale(x.clone(), good, x, torch.zeros(2, 3, 8, 2), g, g, 6, 8, 3, 1, 1e-5, None)
 
+
+def gn_noalloc(y=A, so=Bp, x=Cp, st=Dp, gamma=Ep, beta=Ep + 4096, B=1, H=8, W=4, C=64, G=8, P=2, p=0, rows=4,
+               eps=1e-5, dtype=BF16):
+    return _no_launch(L.dpp_groupnorm_stale_noalloc(y, so, x, st, gamma, beta, B, H, W, C, G, P, p, rows, eps, dtype,
+                                                    None))
+
+
+def test_groupnorm_noalloc_validation():
+    # the same argument checks as dpp_groupnorm_stale, before any HIP call
+    assert gn_noalloc(dtype=2) == DTYPE
+    assert gn_noalloc(x=None) == NULL
+    assert gn_noalloc(st=None) == NULL
+    assert gn_noalloc(C=60, G=8) == SHAPE
+    assert gn_noalloc(p=2) == SHAPE
+    assert gn_noalloc(C=20, G=4) == UNSUP
+    assert gn_noalloc(x=Cp + 2) == ALIGN
+    assert gn_noalloc(so=Dp) == ALIAS
+    assert gn_noalloc(y=Cp) == ALIAS
+    # shapes whose scratch exceeds the static array: refused, nothing launched
+    need = dpp.dpp_groupnorm_stale_workspace_bytes(4096, 4, 4, 64, 32)
+    assert need > _lib.GN_NOALLOC_MAX_BYTES
+    assert gn_noalloc(B=4096, H=8, W=4, C=64, G=32, P=2, rows=4) == WS
+    assert dpp.dpp_groupnorm_stale_workspace_bytes(2048, 4, 4, 64, 32) <= _lib.GN_NOALLOC_MAX_BYTES
