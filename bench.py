@@ -282,6 +282,8 @@ def run(args):
     value = step_flops / (wall / args.steps) / 1e12
     attn_tflops = f_attn / (attn_ms * 1e-3) / 1e12
 
+    block = time_attention_block(cfg, dpp, torch) if cfg.dtype == "bf16" else None
+
     kernels = None
     if args.kernels:
         kernels = time_kernels(cfg, layer, x_patches, gamma, beta, w, b, eps, rel, eps_c, eps_u, cfg_ws, dpp, torch)
@@ -332,6 +334,8 @@ def run(args):
             "flops_per_launch": f_attn,
         },
     }
+    if block:
+        out["attention_block_step"] = block
     if kernels:
         out["kernels"] = kernels
     if args.hbm_sweep:
@@ -341,10 +345,58 @@ def run(args):
     return out
 
 
+def time_attention_block(cfg, dpp, torch, reps=3):
+    """The attention block with its projections (GroupNorm + SiLU -> conv ->
+    q and fused K/V projections into the private buffer -> attention -> out
+    projection) of every patch, after an untimed synchronous step; HIP events
+    on the launch stream around each patch step.  Seeded weights
+    (layer_inputs, projection_inputs)."""
+    from dpp_synth import layer_inputs, projection_inputs
+    from displaced_patch_parallelism_net_amd.step import DisplacedBlock
+
+    def bf(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+
+    li, pi = layer_inputs(cfg), projection_inputs(cfg)
+    f32 = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()  # noqa: E731
+    gamma, beta, cw, cb = f32(li["gamma"]), f32(li["beta"]), bf(li["conv_w"]), f32(li["conv_b"])
+    wq, bq, wo, bo = bf(pi["w_q"]), f32(pi["b_q"]), bf(pi["w_o"]), f32(pi["b_o"])
+    wkv = bf(np.concatenate([pi["w_k"], pi["w_v"]], axis=0))
+    bkv = f32(np.concatenate([pi["b_k"], pi["b_v"]]))
+    blk = DisplacedBlock(cfg.B, cfg.H, cfg.W, cfg.C, cfg.P, cfg.G, cfg.heads, eps=cfg.gn_eps, head_dim=cfg.D)
+    blk.synchronous_step(bf(li["x_stale"]), gamma, beta, cw, cb, wkv, bkv)
+    xf = bf(li["x_fresh"])
+    xp = [blk.band(xf, p) for p in range(cfg.P)]
+    del li, pi
+    for p in range(cfg.P):
+        blk.patch_step(p, xp[p], gamma, beta, cw, cb, wq, bq, wkv, bkv, wo, bo)
+    torch.cuda.synchronize()
+    ev = []
+    for _ in range(reps):
+        for p in range(cfg.P):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            blk.patch_step(p, xp[p], gamma, beta, cw, cb, wq, bq, wkv, bkv, wo, bo)
+            e1.record()
+            ev.append((e0, e1))
+    torch.cuda.synchronize()
+    t = np.array([a.elapsed_time(b_) for a, b_ in ev])
+    f_conv, f_attn = flops(cfg)
+    f_proj = 2.0 * cfg.B * cfg.Nq * cfg.C * cfg.C * 4   # q, k, v, out
+    ms = float(np.median(t))
+    return {"median_ms": round(ms, 4), "p10_ms": round(float(np.percentile(t, 10)), 4),
+            "p90_ms": round(float(np.percentile(t, 90)), 4), "samples": int(t.size),
+            "TFLOP/s": round((f_conv + f_attn + f_proj) / (ms * 1e-3) / 1e12, 2),
+            "flops": f_conv + f_attn + f_proj,
+            "steps": "GroupNorm+SiLU -> conv -> q and fused K/V projections into the private buffer -> "
+                     "attention -> out projection, per patch"}
+
+
 def time_kernels(cfg, layer, x_patches, gamma, beta, w, b, eps, rel, eps_c, eps_u, cfg_ws, dpp, torch, reps=10):
     """Average duration of each call family over all patches (HIP events on
     the launch stream), with its algorithmic work."""
-    ev = {k: [] for k in ("groupnorm", "conv", "splice", "attention", "cfg")}
+    ev = {k: [] for k in ("groupnorm", "conv", "splice", "attention", "cfg", "conv_with_gn_partials",
+                          "groupnorm_presummed")}
 
     def timed(name, fn):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -366,6 +418,20 @@ def time_kernels(cfg, layer, x_patches, gamma, beta, w, b, eps, rel, eps_c, eps_
             timed("attention", lambda: dpp.dpp_self_attn_displaced(layer.o, layer.y2.view(cfg.B, cfg.Nq, cfg.C), kv,
                                                                    kv, cfg.heads, cfg.D, 0.0, layer.attn_ws))
         timed("cfg", lambda: dpp.dpp_cfg_combine_relmae(eps, rel, eps_c, eps_u, cfg.guidance, cfg_ws))
+    if cfg.dtype == "bf16":
+        # a GroupNorm whose input the conv wrote: the conv also emits the
+        # group partial sums, and the GroupNorm reads its input once
+        nchunk = dpp.dpp_conv3x3_halo_gn_chunks(cfg.rows, cfg.W, cfg.C)
+        part = torch.empty(cfg.B, nchunk, cfg.G, 2, dtype=torch.float32, device="cuda")
+        h = torch.empty_like(layer.y2)
+        for _ in range(reps):
+            for p in range(cfg.P):
+                r0 = p * layer.R
+                timed("conv_with_gn_partials", lambda: dpp.dpp_conv3x3_halo_gn(h, part, layer.y1, layer.a1, w, b,
+                                                                               cfg.H, r0))
+                timed("groupnorm_presummed", lambda: dpp.dpp_groupnorm_stale_presummed(
+                    layer.y1, layer.stats_next, h, part, layer.stats_prev, gamma, beta, cfg.H, cfg.G, cfg.P, p,
+                    cfg.gn_eps))
     torch.cuda.synchronize()
     es = 2 if cfg.dtype == "bf16" else 4
     f_conv, f_attn = flops(cfg)
@@ -376,9 +442,13 @@ def time_kernels(cfg, layer, x_patches, gamma, beta, w, b, eps, rel, eps_c, eps_
         "splice": (2.0 * act, "GB/s", PEAK_HBM_GBS),
         "attention": (f_attn, "TFLOP/s", PEAK_BF16_TFLOPS),
         "cfg": (3.0 * eps_c.numel() * es, "GB/s", PEAK_HBM_GBS),
+        "conv_with_gn_partials": (f_conv, "TFLOP/s", PEAK_BF16_TFLOPS),
+        "groupnorm_presummed": (2.0 * act + 2 * 4 * cfg.B * cfg.G * (cfg.P + 1), "GB/s", PEAK_HBM_GBS),
     }
     res = {}
     for k, lst in ev.items():
+        if not lst:
+            continue
         t = np.array([a.elapsed_time(b_) for a, b_ in lst])
         ms = float(np.mean(t))
         amount, unit, peak = work[k]
@@ -585,7 +655,23 @@ def hbm_sweep(cfg, dpp, torch, reps=20):
                   for _, x, y in sets]
             res.append(row("splice", "batch", B, nbytes, cold, timeit(sp)))
             res.append(row("groupnorm", "batch", B, nbytes, cold, timeit(gn)))
-            del sets, sp, gn
+            # the same GroupNorm with its input's partial sums from the
+            # producer (an out projection writing x): x is read once
+            M = R * W
+            wp = (torch.randn(C, C, device=dev) / C ** 0.5).to(torch.bfloat16)
+            nchunk = dpp.dpp_linear_gn_chunks(B, M, C)
+            parts = []
+            for _, x, _ in sets:
+                part = torch.empty(B, nchunk, G, 2, device=dev)
+                src = x.clone()
+                dpp.dpp_linear_gn(x.view(B, M, C), part, src.view(B, M, C), wp)
+                parts.append(part)
+                del src
+            gnp = [lambda x=x, y=y, pt=pt: dpp.dpp_groupnorm_stale_presummed(y, so, x, pt, st, gamma, beta, H, G, P, 3,
+                                                                           1e-5)
+                   for (_, x, y), pt in zip(sets, parts)]
+            res.append(row("groupnorm_presummed", "batch", B, nbytes, cold, timeit(gnp)))
+            del sets, sp, gn, gnp, parts
     for lg in (16, 20, 23, 26):
         n = 2 ** lg
         nbytes = 3.0 * n * 2

@@ -13,13 +13,18 @@ from ._lib import (  # noqa: F401
     dpp_cfg_combine_relmae,
     dpp_cfg_combine_workspace_bytes,
     dpp_conv3x3_halo,
+    dpp_conv3x3_halo_gn,
+    dpp_conv3x3_halo_gn_chunks,
     dpp_conv3x3_halo_workspace_bytes,
     dpp_groupnorm_silu_stale,
     dpp_groupnorm_stale,
     dpp_groupnorm_stale_noalloc,
+    dpp_groupnorm_stale_presummed,
     dpp_groupnorm_stale_workspace_bytes,
     dpp_hybrid_schedule,
     dpp_linear,
+    dpp_linear_gn,
+    dpp_linear_gn_chunks,
     dpp_self_attn_displaced,
     dpp_self_attn_workspace_bytes,
     dpp_splice_patch,

@@ -46,6 +46,13 @@ SIGNATURES = {
     "dpp_cfg_combine_workspace_bytes": (_sz, [_i64]),
     "dpp_cfg_combine_relmae": (_i, [_vp, _vp, _vp, _vp, _i64, _f, _vp, _sz, _i, _vp]),
     "dpp_hybrid_schedule": (_i, [_vp, _i64, _f, _f, _i64, _vp, _vp, _vp]),
+    "dpp_groupnorm_stale_presummed": (_i, [_vp, _vp, _vp, _vp, _i64, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64,
+                                           _i64, _i64, _i64, _f, _i, _i, _vp]),
+    "dpp_conv3x3_halo_gn_chunks": (_i64, [_i64, _i64, _i64]),
+    "dpp_conv3x3_halo_gn": (_i, [_vp, _vp, _i64, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _i64, _i64, _i,
+                                 _vp]),
+    "dpp_linear_gn_chunks": (_i64, [_i64, _i64, _i64]),
+    "dpp_linear_gn": (_i, [_vp, _vp, _i64, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _i64, _i64, _i64, _i, _vp]),
 }
 
 
@@ -201,10 +208,52 @@ def dpp_groupnorm_stale_noalloc(y, stats_out, x, stale_stats, gamma, beta, H: in
                                            _ptr(beta), B, H, W, C, G, P, p, rows, eps, _dtype(x), _stream(stream)))
 
 
-def dpp_linear(y, x, w, bias=None, stream=None):
-    """y = x w^T + bias over the last dimension.  x [M,K] or [B,M,K] and y
-    [M,N] or [B,M,N] may be strided views (last dimension contiguous), e.g. y
-    a row band of a larger K/V buffer; w [N,K] contiguous; bias [N] float32."""
+def dpp_groupnorm_stale_presummed(y, stats_out, x, partials, stale_stats, gamma, beta, H: int, G: int, P: int, p: int,
+                                  eps: float, silu: bool = False, stream=None):
+    """GroupNorm of x with the fresh sums taken from partials [B,nchunk,G,2]
+    written by the producer of x (dpp_conv3x3_halo_gn, dpp_linear_gn)."""
+    _gn_args(y, stats_out, x, stale_stats, gamma, beta, G, P)
+    _contig(partials)
+    _f32(partials)
+    B, rows, W, C = x.shape
+    if partials.dim() != 4 or tuple(partials.shape[::2]) != (B, G) or partials.shape[3] != 2:
+        raise ValueError(f"partials: shape {tuple(partials.shape)}, expected [B, nchunk, G, 2] with B = {B}, G = {G}")
+    _check("dpp_groupnorm_stale_presummed",
+           LIB.dpp_groupnorm_stale_presummed(_ptr(y), _ptr(stats_out), _ptr(x), _ptr(partials), partials.shape[1],
+                                             _ptr(stale_stats), _ptr(gamma), _ptr(beta), B, H, W, C, G, P, p, rows,
+                                             eps, 1 if silu else 0, _dtype(x), _stream(stream)))
+
+
+def dpp_conv3x3_halo_gn_chunks(rows, W, Cout) -> int:
+    return int(LIB.dpp_conv3x3_halo_gn_chunks(rows, W, Cout))
+
+
+def dpp_conv3x3_halo_gn(y, gn_partials, x, stale_full, weight, bias, H: int, row0: int, stream=None):
+    """dpp_conv3x3_halo plus the GroupNorm partial sums of y,
+    gn_partials [B, dpp_conv3x3_halo_gn_chunks(rows, W, Cout), G, 2]."""
+    _contig(y, x, stale_full, weight, bias, gn_partials)
+    _same_dtype(y, x, stale_full, weight)
+    _f32(bias, gn_partials)
+    B, rows, W, Cin = x.shape
+    Cout = weight.shape[0]
+    _shape(weight, (Cout, 3, 3, Cin), "weight")
+    _shape(y, (B, rows, W, Cout), "y")
+    _shape(stale_full, (B, H, W, Cin), "stale_full")
+    _numel(bias, Cout, "bias")
+    if gn_partials.dim() != 4:
+        raise ValueError("gn_partials must be [B, nchunk, G, 2]")
+    G = gn_partials.shape[2]
+    _shape(gn_partials, (B, dpp_conv3x3_halo_gn_chunks(rows, W, Cout), G, 2), "gn_partials")
+    _check("dpp_conv3x3_halo_gn",
+           LIB.dpp_conv3x3_halo_gn(_ptr(y), _ptr(gn_partials), G, _ptr(x), _ptr(stale_full), _ptr(weight), _ptr(bias),
+                                   B, H, W, Cin, Cout, row0, rows, _dtype(x), _stream(stream)))
+
+
+def dpp_linear_gn_chunks(B, M, N) -> int:
+    return int(LIB.dpp_linear_gn_chunks(B, M, N))
+
+
+def _lin3(y, x, w, bias):
     _contig(w, bias)
     _same_dtype(y, x, w)
     _f32(bias)
@@ -217,6 +266,29 @@ def dpp_linear(y, x, w, bias=None, stream=None):
     if x3.stride(2) != 1 or y3.stride(2) != 1:
         raise ValueError("last dimension of x and y must be contiguous")
     _numel(bias, N, "bias")
+    return x3, y3, B, M, K, N
+
+
+def dpp_linear_gn(y, gn_partials, x, w, bias=None, stream=None):
+    """dpp_linear plus the GroupNorm partial sums of y,
+    gn_partials [B, dpp_linear_gn_chunks(B, M, N), G, 2]."""
+    x3, y3, B, M, K, N = _lin3(y, x, w, bias)
+    _contig(gn_partials)
+    _f32(gn_partials)
+    if gn_partials.dim() != 4:
+        raise ValueError("gn_partials must be [B, nchunk, G, 2]")
+    G = gn_partials.shape[2]
+    _shape(gn_partials, (B, dpp_linear_gn_chunks(B, M, N), G, 2), "gn_partials")
+    _check("dpp_linear_gn", LIB.dpp_linear_gn(_ptr(y3), _ptr(gn_partials), G, _ptr(x3), _ptr(w), _ptr(bias), B, M, K,
+                                              N, x3.stride(1), x3.stride(0), y3.stride(1), y3.stride(0), _dtype(x),
+                                              _stream(stream)))
+
+
+def dpp_linear(y, x, w, bias=None, stream=None):
+    """y = x w^T + bias over the last dimension.  x [M,K] or [B,M,K] and y
+    [M,N] or [B,M,N] may be strided views (last dimension contiguous), e.g. y
+    a row band of a larger K/V buffer; w [N,K] contiguous; bias [N] float32."""
+    x3, y3, B, M, K, N = _lin3(y, x, w, bias)
     _check("dpp_linear", LIB.dpp_linear(_ptr(y3), _ptr(x3), _ptr(w), _ptr(bias), B, M, K, N, x3.stride(1),
                                         x3.stride(0), y3.stride(1), y3.stride(0), _dtype(x), _stream(stream)))
 

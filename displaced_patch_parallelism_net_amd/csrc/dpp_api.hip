@@ -123,6 +123,24 @@ int dpp_groupnorm_silu_stale(void* y, float* stats_out, const void* x, const flo
                         workspace_bytes, dtype, true, stream);
 }
 
+int dpp_groupnorm_stale_presummed(void* y, float* stats_out, const void* x, const float* partials, int64_t nchunk,
+                                  const float* stale_stats, const float* gamma, const float* beta, int64_t B,
+                                  int64_t H, int64_t W, int64_t C, int64_t G, int64_t P, int64_t p, int64_t rows,
+                                  float eps, int silu, int dtype, void* stream) {
+  const int rc = groupnorm_validate(y, stats_out, x, stale_stats, gamma, beta, B, H, W, C, G, P, p, rows, eps, dtype);
+  if (rc != DPP_OK) return rc;
+  if (!partials) return DPP_ERR_NULL;
+  if (nchunk <= 0 || nchunk > (1LL << 30)) return DPP_ERR_SHAPE;
+  const int es = esize_of(dtype);
+  const int64_t act = B * rows * W * C * es;
+  const int64_t st = B * P * G * 2 * 4;
+  const int64_t pb = B * nchunk * G * 2 * 4;
+  if (overlap(stats_out, st, partials, pb) || (y && overlap(y, act, partials, pb))) return DPP_ERR_ALIAS;
+  return launch_status(dpp::launch_groupnorm_presummed(y, stats_out, x, partials, nchunk, stale_stats, gamma, beta, B,
+                                                       H, W, C, G, P, p, rows, eps, dtype == DPP_BF16, silu != 0,
+                                                       static_cast<hipStream_t>(stream)));
+}
+
 int dpp_groupnorm_stale_noalloc(void* y, float* stats_out, const void* x, const float* stale_stats,
                                 const float* gamma, const float* beta, int64_t B, int64_t H, int64_t W, int64_t C,
                                 int64_t G, int64_t P, int64_t p, int64_t rows, float eps, int dtype, void* stream) {
@@ -150,9 +168,12 @@ int dpp_conv3x3_halo(void* y, const void* x, const void* stale_full, const void*
                              stream);
 }
 
-int dpp_conv3x3_halo_ws(void* y, const void* x, const void* stale_full, const void* weight, const float* bias,
-                        int64_t B, int64_t H, int64_t W, int64_t Cin, int64_t Cout, int64_t row0, int64_t rows,
-                        void* workspace, size_t workspace_bytes, int dtype, void* stream) {
+}  // extern "C"
+
+namespace {
+// Every check of a conv call except those of its workspace.
+int conv_validate(void* y, const void* x, const void* stale_full, const void* weight, const float* bias, int64_t B,
+                  int64_t H, int64_t W, int64_t Cin, int64_t Cout, int64_t row0, int64_t rows, int dtype) {
   if (bad_dtype(dtype)) return DPP_ERR_DTYPE;
   if (!y || !x || !weight) return DPP_ERR_NULL;
   if (B <= 0 || H <= 0 || W <= 0 || Cin <= 0 || Cout <= 0 || rows <= 0 || row0 < 0 || row0 + rows > H)
@@ -172,6 +193,19 @@ int dpp_conv3x3_halo_ws(void* y, const void* x, const void* stale_full, const vo
   if (overlap(y, ybytes, x, B * rows * W * Cin * es) || overlap(y, ybytes, weight, Cout * 9 * Cin * es) ||
       (stale_full && overlap(y, ybytes, stale_full, B * H * W * Cin * es)) || (bias && overlap(y, ybytes, bias, Cout * 4)))
     return DPP_ERR_ALIAS;
+  return DPP_OK;
+}
+}  // namespace
+
+extern "C" {
+
+int dpp_conv3x3_halo_ws(void* y, const void* x, const void* stale_full, const void* weight, const float* bias,
+                        int64_t B, int64_t H, int64_t W, int64_t Cin, int64_t Cout, int64_t row0, int64_t rows,
+                        void* workspace, size_t workspace_bytes, int dtype, void* stream) {
+  const int rc = conv_validate(y, x, stale_full, weight, bias, B, H, W, Cin, Cout, row0, rows, dtype);
+  if (rc != DPP_OK) return rc;
+  const int es = esize_of(dtype);
+  const int64_t ybytes = B * rows * W * Cout * es;
   if (workspace && workspace_bytes > 0) {
     const int64_t wb = static_cast<int64_t>(workspace_bytes);
     if (!aligned16(workspace)) return DPP_ERR_ALIGN;
@@ -183,6 +217,30 @@ int dpp_conv3x3_halo_ws(void* y, const void* x, const void* stale_full, const vo
   }
   return launch_status(dpp::launch_conv3x3(y, x, stale_full, weight, bias, B, H, W, Cin, Cout, row0, rows, workspace,
                                            workspace_bytes, dtype == DPP_BF16, static_cast<hipStream_t>(stream)));
+}
+
+int64_t dpp_conv3x3_halo_gn_chunks(int64_t rows, int64_t W, int64_t Cout) {
+  if (rows <= 0 || W <= 0 || Cout <= 0) return 0;
+  return dpp::conv_gn_chunks(rows, W, Cout);
+}
+
+int dpp_conv3x3_halo_gn(void* y, float* gn_partials, int64_t G, const void* x, const void* stale_full,
+                        const void* weight, const float* bias, int64_t B, int64_t H, int64_t W, int64_t Cin,
+                        int64_t Cout, int64_t row0, int64_t rows, int dtype, void* stream) {
+  const int rc = conv_validate(y, x, stale_full, weight, bias, B, H, W, Cin, Cout, row0, rows, dtype);
+  if (rc != DPP_OK) return rc;
+  if (!gn_partials) return DPP_ERR_NULL;
+  if (G <= 0 || Cout % G != 0) return DPP_ERR_SHAPE;
+  if (dtype != DPP_BF16) return DPP_ERR_UNSUPPORTED;
+  const int64_t pbytes = B * dpp::conv_gn_chunks(rows, W, Cout) * G * 2 * 4;
+  const int64_t ybytes = B * rows * W * Cout * 2;
+  if (overlap(gn_partials, pbytes, y, ybytes) || overlap(gn_partials, pbytes, x, B * rows * W * Cin * 2) ||
+      overlap(gn_partials, pbytes, weight, Cout * 9 * Cin * 2) ||
+      (stale_full && overlap(gn_partials, pbytes, stale_full, B * H * W * Cin * 2)) ||
+      (bias && overlap(gn_partials, pbytes, bias, Cout * 4)))
+    return DPP_ERR_ALIAS;
+  return launch_status(dpp::launch_conv3x3(y, x, stale_full, weight, bias, B, H, W, Cin, Cout, row0, rows, nullptr, 0,
+                                           true, static_cast<hipStream_t>(stream), gn_partials, static_cast<int>(G)));
 }
 
 // ------------------------------------------------------------------ a4
@@ -228,8 +286,11 @@ int dpp_self_attn_displaced(void* o, const void* q, const void* k, const void* v
 }
 
 // ------------------------------------------------------------------ projections
-int dpp_linear(void* y, const void* x, const void* w, const float* bias, int64_t B, int64_t M, int64_t K, int64_t N,
-               int64_t ld_x, int64_t bs_x, int64_t ld_y, int64_t bs_y, int dtype, void* stream) {
+}  // extern "C"
+
+namespace {
+int linear_validate(void* y, const void* x, const void* w, const float* bias, int64_t B, int64_t M, int64_t K,
+                    int64_t N, int64_t ld_x, int64_t bs_x, int64_t ld_y, int64_t bs_y, int dtype) {
   if (bad_dtype(dtype)) return DPP_ERR_DTYPE;
   if (!y || !x || !w) return DPP_ERR_NULL;
   if (B <= 0 || M <= 0 || K <= 0 || N <= 0 || ld_x < K || ld_y < N || bs_x < 0 || bs_y < 0) return DPP_ERR_SHAPE;
@@ -253,8 +314,40 @@ int dpp_linear(void* y, const void* x, const void* w, const float* bias, int64_t
   const int64_t wbytes = N * K * es;
   if (overlap(y, ybytes, x, xbytes) || overlap(y, ybytes, w, wbytes) || (bias && overlap(y, ybytes, bias, N * 4)))
     return DPP_ERR_ALIAS;
+  return DPP_OK;
+}
+}  // namespace
+
+extern "C" {
+
+int dpp_linear(void* y, const void* x, const void* w, const float* bias, int64_t B, int64_t M, int64_t K, int64_t N,
+               int64_t ld_x, int64_t bs_x, int64_t ld_y, int64_t bs_y, int dtype, void* stream) {
+  const int rc = linear_validate(y, x, w, bias, B, M, K, N, ld_x, bs_x, ld_y, bs_y, dtype);
+  if (rc != DPP_OK) return rc;
   return launch_status(dpp::launch_linear(y, x, w, bias, B, M, K, N, ld_x, bs_x, ld_y, bs_y, dtype == DPP_BF16,
                                           static_cast<hipStream_t>(stream)));
+}
+
+int64_t dpp_linear_gn_chunks(int64_t B, int64_t M, int64_t N) {
+  if (B <= 0 || M <= 0 || N <= 0) return 0;
+  return dpp::linear_gn_chunks(B, M, N);
+}
+
+int dpp_linear_gn(void* y, float* gn_partials, int64_t G, const void* x, const void* w, const float* bias, int64_t B,
+                  int64_t M, int64_t K, int64_t N, int64_t ld_x, int64_t bs_x, int64_t ld_y, int64_t bs_y, int dtype,
+                  void* stream) {
+  const int rc = linear_validate(y, x, w, bias, B, M, K, N, ld_x, bs_x, ld_y, bs_y, dtype);
+  if (rc != DPP_OK) return rc;
+  if (!gn_partials) return DPP_ERR_NULL;
+  if (G <= 0 || N % G != 0) return DPP_ERR_SHAPE;
+  if (dtype != DPP_BF16) return DPP_ERR_UNSUPPORTED;
+  const int64_t pbytes = B * dpp::linear_gn_chunks(B, M, N) * G * 2 * 4;
+  if (overlap(gn_partials, pbytes, y, ((B - 1) * bs_y + (M - 1) * ld_y + N) * 2) ||
+      overlap(gn_partials, pbytes, x, ((B - 1) * bs_x + (M - 1) * ld_x + K) * 2) ||
+      overlap(gn_partials, pbytes, w, N * K * 2) || (bias && overlap(gn_partials, pbytes, bias, N * 4)))
+    return DPP_ERR_ALIAS;
+  return launch_status(dpp::launch_linear(y, x, w, bias, B, M, K, N, ld_x, bs_x, ld_y, bs_y, true,
+                                          static_cast<hipStream_t>(stream), gn_partials, static_cast<int>(G)));
 }
 
 // ------------------------------------------------------------------ a5

@@ -98,6 +98,8 @@ struct ConvArgs {
   int tiles_c;  // column tiles per row pair
   int nsplit;   // input-channel splits (blockIdx.z = b * nsplit + split)
   int spl;      // 64-channel slices per split
+  float* gn_part;  // GroupNorm partial sums of y [B][gridDim.x * gridDim.y][G][2], or NULL (unsplit only)
+  int G;
 };
 
 // LDS row of 8 x 16-byte slots, slot index XOR-swizzled by the row index so
@@ -351,6 +353,21 @@ __global__ __launch_bounds__(kConvThreads, 1) void conv3x3_bf16_mfma_kernel(Conv
       *reinterpret_cast<uint2*>(a.y + ((static_cast<int64_t>(b) * a.rows + row) * W + col) * a.Cout + m) =
           tile[pix * kPixU2 + q];
   }
+  if (a.gn_part != nullptr) {
+    // GroupNorm partial sums of this tile's stored values, one chunk per
+    // workgroup (chunk = channel tile * pixel tiles + pixel tile); the weight
+    // buffers past the staged tile are the scratch
+    constexpr int kTileU2 = kConvTR * TC * kPixU2;
+    static_assert((kTileU2 * 8 + 4 * tile_group_sums_scratch_floats<kConvThreads, kConvBM>()) <= sizeof(wts),
+                  "statistics scratch fits after the staged tile");
+    const int64_t nchunk = static_cast<int64_t>(gridDim.x) * gridDim.y;
+    const int64_t chunk = static_cast<int64_t>(blockIdx.y) * gridDim.x + blockIdx.x;
+    float* out = a.gn_part + (static_cast<int64_t>(b) * nchunk + chunk) * a.G * 2;
+    tile_group_sums<kConvThreads, kConvTR * TC, kConvBM>(
+        reinterpret_cast<const uint16_t*>(tile), 4 * kPixU2,
+        [&](int p) { return pr0 + p / TC < a.rows && pc0 + p % TC < W; }, m0, a.Cout, a.Cout / a.G, a.G,
+        reinterpret_cast<float*>(tile + kTileU2), out);
+  }
 }
 
 // Split-K reduction: y = bf16(bias + sum over splits of the float32 partials),
@@ -424,6 +441,10 @@ static ConvSplit conv_split(int64_t B, int64_t rows, int64_t W, int64_t Cin, int
   return best;
 }
 
+int64_t conv_gn_chunks(int64_t rows, int64_t W, int64_t Cout) {
+  return ceil_div(rows, kConvTR) * ceil_div(W, 16 * conv_pick_tg(W)) * ceil_div(Cout, kConvBM);
+}
+
 size_t conv_workspace_bytes(int64_t B, int64_t rows, int64_t W, int64_t Cin, int64_t Cout) {
   const ConvSplit sp = conv_split(B, rows, W, Cin, Cout);
   if (sp.nsplit <= 1) return 0;
@@ -432,7 +453,7 @@ size_t conv_workspace_bytes(int64_t B, int64_t rows, int64_t W, int64_t Cin, int
 
 hipError_t launch_conv3x3(void* y, const void* x, const void* stale_full, const void* weight, const float* bias,
                           int64_t B, int64_t H, int64_t W, int64_t Cin, int64_t Cout, int64_t row0, int64_t rows,
-                          void* ws, size_t ws_bytes, bool bf16, hipStream_t s) {
+                          void* ws, size_t ws_bytes, bool bf16, hipStream_t s, float* gn_part, int G) {
   if (!bf16) {
     const int64_t total = B * rows * W * Cout;
     int64_t blocks = ceil_div(total, 256);
@@ -458,8 +479,10 @@ hipError_t launch_conv3x3(void* y, const void* x, const void* stale_full, const 
   a.tiles_c = static_cast<int>(ceil_div(W, 16 * tg));
   const int64_t tiles = ceil_div(rows, kConvTR) * a.tiles_c;
   ConvSplit sp = conv_split(B, rows, W, Cin, Cout);
-  if (sp.nsplit > 1 && (ws == nullptr || ws_bytes < conv_workspace_bytes(B, rows, W, Cin, Cout)))
+  if (sp.nsplit > 1 && (gn_part != nullptr || ws == nullptr || ws_bytes < conv_workspace_bytes(B, rows, W, Cin, Cout)))
     sp = ConvSplit{1, static_cast<int>(Cin / kConvKC)};
+  a.gn_part = gn_part;
+  a.G = G;
   a.nsplit = sp.nsplit;
   a.spl = sp.spl;
   a.part = sp.nsplit > 1 ? static_cast<float*>(ws) : nullptr;

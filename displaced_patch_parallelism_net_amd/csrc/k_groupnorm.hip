@@ -5,26 +5,26 @@
 // raw sums (sum x, sum x^2) from the previous step plus the own patch's fresh
 // sums (DistriFusion reading notes, Introduction, fourth paragraph).
 //
-// Three launches, all deterministic (no atomics):
+// Three launches, deterministic (no atomics):
 //   1. partial: workgroup (chunk, b) sums its pixels per channel in float32
 //      registers (each thread owns one 16-byte channel vector and walks
-//      pixels, eight loads in flight), folds channels into groups through LDS in a fixed order and
-//      writes one (s1, s2) per group to the workspace;
-//   2. finalize: one wave per (group, b) adds the chunk partials in float64
-//      (fixed order), adds the other patches' stale sums, writes the fresh
-//      sums to stats_out[b,p] and mean/rstd to the workspace;
-//   3. apply: y = x * a_c + b_c with a_c = rstd_g gamma_c, b_c = beta_c -
-//      mean_g a_c (then SiLU when asked: the GroupNorm + SiLU pair opening
-//      an SDXL residual block); one 16-byte load and one streaming store per
-//      vector.
+//      pixels, eight loads in flight), folds channels into groups through
+//      LDS in a fixed order and writes one (s1, s2) per group to the
+//      workspace;
+//   2. stats: the chunk partials of each group added in float64 in a fixed
+//      order, the fresh sums written to stats_out[b, p];
+//   3. apply: every workgroup forms mean/rstd of each group from the fresh
+//      and the other patches' stale sums in LDS and streams
+//      y = x * a_c + b_c (then SiLU when asked).
 // The second read of x (step 3) normally hits the 256 MB last-level cache.
+// When the kernel that wrote x also wrote its group partial sums (the conv
+// and projection epilogues), step 1 is skipped and x is read once.
 #include <mutex>
 
 #include "dpp_common.h"
 
-// Scratch of the allocation-free GroupNorm entry point (chunk partial sums
-// and per-group mean/rstd, exactly the workspace the other entry points take
-// from the caller).  Each GPU the library runs on holds its own copy until
+// Scratch of the allocation-free GroupNorm entry point (the chunk partial
+// sums, exactly the workspace the other entry points take from the caller).  Each GPU the library runs on holds its own copy until
 // the process ends.  Host code never uses this name as an address: the
 // device address comes from hipGetSymbolAddress, once per device.
 constexpr size_t kGnScratchBytes = size_t(1) << 20;   // DPP_GN_NOALLOC_MAX_BYTES
@@ -58,7 +58,6 @@ hipError_t gn_scratch_ptr(void** out) {
 
 constexpr int kGnMaxThreads = 256;
 constexpr int kGnStatChunks = 256;    // total partial workgroups (over B)
-constexpr int kGnApplyChunks = 1024;  // total apply workgroups (over B)
 constexpr int kGnInFlight = 8;        // 16-byte loads in flight per thread
 
 struct GnGeom {
@@ -68,7 +67,6 @@ struct GnGeom {
   int threads;  // KP * V
   int64_t npix;
   int64_t nstat, stat_ppc;    // partial chunks per b, pixels per chunk
-  int64_t napply, apply_ppc;  // apply chunks per b, pixels per chunk
 };
 
 static GnGeom gn_geom(int64_t B, int64_t rows, int64_t W, int64_t C, bool bf16) {
@@ -80,16 +78,11 @@ static GnGeom gn_geom(int64_t B, int64_t rows, int64_t W, int64_t C, bool bf16) 
   g.threads = g.KP * g.V;
   g.npix = rows * W;
   const int64_t maxc = ceil_div(g.npix, g.KP);
-  int64_t want = ceil_div(kGnStatChunks, B);
+  const int64_t want = ceil_div(kGnStatChunks, B);
   g.nstat = want < maxc ? want : maxc;
   if (g.nstat < 1) g.nstat = 1;
   g.stat_ppc = ceil_div(g.npix, g.nstat);
   g.nstat = ceil_div(g.npix, g.stat_ppc);
-  want = ceil_div(kGnApplyChunks, B);
-  g.napply = want < maxc ? want : maxc;
-  if (g.napply < 1) g.napply = 1;
-  g.apply_ppc = ceil_div(g.npix, g.napply);
-  g.napply = ceil_div(g.npix, g.apply_ppc);
   return g;
 }
 
@@ -101,7 +94,7 @@ size_t gn_workspace_bytes(int64_t B, int64_t rows, int64_t W, int64_t C, int64_t
     const int64_t nb = gn_geom(B, rows, W, C, true).nstat;
     if (nb > nstat) nstat = nb;
   }
-  return static_cast<size_t>(B * nstat * G * 2 + B * G * 2) * sizeof(float);
+  return static_cast<size_t>(B * nstat * G * 2) * sizeof(float);
 }
 
 template <typename T>
@@ -179,61 +172,51 @@ __global__ __launch_bounds__(kGnMaxThreads) void gn_partial_kernel(const T* __re
   }
 }
 
-// Finalize: one wave per (group g, batch entry b).  Lane l sums chunks l,
-// l + 64, ... of the group's partials in float64 (kGnFinLoads loads issued
-// before they are summed, then a remainder loop) and, issued with the first
-// of them, the stale sums of patches l, l + 64, ... other than p; two fixed
-// xor butterflies add the lanes (every lane ends with the same totals); lane
-// 0 writes the fresh sums and (mean, rstd).  Deterministic, no atomics.
-constexpr int kGnFinLoads = 8;
+// Fresh group sums of a patch from its chunk partials, in one fixed order: a
+// set of 16 lanes handles one (b, g); lane j adds the chunk partials j,
+// j + 16, j + 32, ... in float64 in increasing order (batches of kGnFinLoads
+// loads issued before any is used; chunks past the end read as zero, which
+// leaves the sums unchanged), and a 16-lane xor butterfly (offsets 8, 4, 2,
+// 1) joins the lanes, every lane ending with the same sums.
+constexpr int kGnFinLoads = 16;
+constexpr int kGnSet = 16;
 
-__global__ __launch_bounds__(kWave) void gn_finalize_kernel(
-    const float* __restrict__ partial, int64_t nchunk, const float* __restrict__ stale, float* __restrict__ stats_out,
-    float* __restrict__ coef, int G, int P, int p, double n, float eps) {
-  const int g = blockIdx.x, b = blockIdx.y;
-  const int l = threadIdx.x;
-  const float* base = partial + (static_cast<int64_t>(b) * nchunk * G + g) * 2;
-  double sa = 0.0, sc = 0.0;  // stale sums of the other patches
-  if (stale != nullptr && coef != nullptr)
-    for (int q = l; q < P; q += kWave)
-      if (q != p) {
-        const float2 st = *reinterpret_cast<const float2*>(stale + ((static_cast<int64_t>(b) * P + q) * G + g) * 2);
-        sa += st.x;
-        sc += st.y;
-      }
+__device__ __forceinline__ double2 gn_fresh_sums(const float* __restrict__ partial, int64_t nchunk, int G, int b,
+                                                 int g, int j) {
   double a = 0.0, c = 0.0;
-  int64_t ch = l;
-  for (; ch + (kGnFinLoads - 1) * kWave < nchunk; ch += kGnFinLoads * kWave) {
+  const float* base = partial + (static_cast<int64_t>(b) * nchunk * G + g) * 2;
+  for (int64_t ch = j; ch < nchunk; ch += kGnFinLoads * kGnSet) {
     float2 v[kGnFinLoads];
 #pragma unroll
-    for (int j = 0; j < kGnFinLoads; ++j) v[j] = *reinterpret_cast<const float2*>(base + (ch + j * kWave) * G * 2);
+    for (int i = 0; i < kGnFinLoads; ++i) {
+      const int64_t ci = ch + i * kGnSet;
+      v[i] = ci < nchunk ? *reinterpret_cast<const float2*>(base + ci * G * 2) : make_float2(0.f, 0.f);
+    }
 #pragma unroll
-    for (int j = 0; j < kGnFinLoads; ++j) { a += v[j].x; c += v[j].y; }
-  }
-  for (; ch < nchunk; ch += kWave) {
-    const float2 v = *reinterpret_cast<const float2*>(base + ch * G * 2);
-    a += v.x;
-    c += v.y;
+    for (int i = 0; i < kGnFinLoads; ++i) { a += v[i].x; c += v[i].y; }
   }
 #pragma unroll
-  for (int off = kWave / 2; off > 0; off >>= 1) {
-    a += __shfl_xor(a, off, kWave);
-    c += __shfl_xor(c, off, kWave);
-    sa += __shfl_xor(sa, off, kWave);
-    sc += __shfl_xor(sc, off, kWave);
+  for (int off = kGnSet / 2; off > 0; off >>= 1) {
+    a += __shfl_xor(a, off, kGnSet);
+    c += __shfl_xor(c, off, kGnSet);
   }
-  if (l != 0) return;
-  float* so = stats_out + ((static_cast<int64_t>(b) * P + p) * G + g) * 2;
-  so[0] = static_cast<float>(a);
-  so[1] = static_cast<float>(c);
-  if (coef == nullptr) return;
-  const double T1 = a + sa, T2 = c + sc;
-  const double mean = T1 / n;
-  double var = T2 / n - mean * mean;
-  if (var < 0.0) var = 0.0;
-  const double rstd = 1.0 / sqrt(var + static_cast<double>(eps));
-  coef[(static_cast<int64_t>(b) * G + g) * 2] = static_cast<float>(mean);
-  coef[(static_cast<int64_t>(b) * G + g) * 2 + 1] = static_cast<float>(rstd);
+  return make_double2(a, c);
+}
+
+// The fresh sums of every group to stats_out[b, p] (the next step's stale
+// sums; alone, the first half of the synchronous step): four groups per
+// 64-lane workgroup.
+__global__ __launch_bounds__(kWave) void gn_stats_kernel(const float* __restrict__ partial, int64_t nchunk,
+                                                         float* __restrict__ stats_out, int G, int P, int p) {
+  const int b = blockIdx.y;
+  const int g = blockIdx.x * (kWave / kGnSet) + threadIdx.x / kGnSet, j = threadIdx.x % kGnSet;
+  if (g >= G) return;  // uniform within each 16-lane set
+  const double2 r = gn_fresh_sums(partial, nchunk, G, b, g, j);
+  if (j == 0) {
+    float* so = stats_out + ((static_cast<int64_t>(b) * P + p) * G + g) * 2;
+    so[0] = static_cast<float>(r.x);
+    so[1] = static_cast<float>(r.y);
+  }
 }
 
 // SiLU z sigmoid(z) = z / (1 + 2^(-z log2 e)): large negative z gives
@@ -242,59 +225,143 @@ __device__ __forceinline__ float silu_f(float z) {
   return z * __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-1.4426950408889634f * z));
 }
 
+// Apply.  Each workgroup first issues its first batch of x loads, then forms
+// the mean/rstd of every group of its batch entry in LDS: the group total is
+// the sum over patches q in increasing order, in float64, of the fresh sums
+// stats[b, p] (written by gn_stats_kernel just before) for q == p and the
+// stale sums for q != p -- the same order in every workgroup.  Then it
+// streams y = x * a_c + b_c (a_c = rstd_g gamma_c, b_c = beta_c - mean_g a_c;
+// then SiLU when asked: the GroupNorm + SiLU pair opening an SDXL residual
+// block) with streaming 16-byte loads and stores.  Pixels go in grid-stride
+// order: workgroup w takes pixels w*KP .. w*KP+KP-1 of every group of
+// gridDim.x*KP consecutive pixels, so the workgroups in flight stream one
+// contiguous window of x and y (measured faster than separate ranges when x
+// comes from HBM).
+constexpr int kGnApplyThreads = 256;
+constexpr int kGnApplyWgs = 2048;     // total apply workgroups over B
+constexpr int kGnApplyInFlight = 8;   // 16-byte loads in flight per thread
+constexpr int kGnStage = 1024;        // (group, patch) sums staged in LDS per pass
+
 template <typename T, bool SILU>
-__global__ __launch_bounds__(kGnMaxThreads) void gn_apply_kernel(const T* __restrict__ x, T* __restrict__ y,
-                                                                 const float* __restrict__ coef,
-                                                                 const float* __restrict__ gamma,
-                                                                 const float* __restrict__ beta, int64_t npix, int C,
-                                                                 int G, int V, int KP, int64_t ppc) {
+__global__ __launch_bounds__(kGnApplyThreads) void gn_apply_kernel(
+    const T* __restrict__ x, T* __restrict__ y, const float* __restrict__ stats, const float* __restrict__ stale,
+    const float* __restrict__ gamma, const float* __restrict__ beta, int64_t npix, int C, int G, int V, int KP, int P,
+    int p, double n, float eps) {
   constexpr int VEC = Elem<T>::kVec;
+  __shared__ float2 stage[kGnStage];
+  __shared__ double2 tot[256];
+  __shared__ float2 coef[256];
   const int b = blockIdx.y;
-  const int t = threadIdx.x;
+  const int t = threadIdx.x, nt = blockDim.x;
   const int v = t % V, k = t / V;
-  if (k >= KP) return;
-  const int cg = C / G;
-  float a[VEC], sh[VEC];
-#pragma unroll
-  for (int j = 0; j < VEC; ++j) {
-    const int c = v * VEC + j;
-    const int g = c / cg;
-    const float mean = coef[(b * G + g) * 2], rstd = coef[(b * G + g) * 2 + 1];
-    a[j] = rstd * gamma[c];
-    sh[j] = fmaf(-mean, a[j], beta[c]);
-  }
-  const int64_t p0 = static_cast<int64_t>(blockIdx.x) * ppc;
-  const int64_t p1 = (p0 + ppc < npix) ? p0 + ppc : npix;
+  const bool active = k < KP;
   const int64_t off = static_cast<int64_t>(b) * npix * V;
   const uint4* xv = reinterpret_cast<const uint4*>(x) + off;
   uint4* yv = reinterpret_cast<uint4*>(y) + off;
-  int64_t pix = p0 + k;
-  for (; pix + (kGnInFlight - 1) * KP < p1; pix += kGnInFlight * KP) {
-    uint4 u[kGnInFlight];
+  const int64_t step = static_cast<int64_t>(gridDim.x) * KP;
+  int64_t pix = static_cast<int64_t>(blockIdx.x) * KP + k;
+  uint4 u[kGnApplyInFlight];
+  float gm[VEC], bt[VEC];
+  // the first batch and the affine parameters do not depend on the
+  // statistics: in flight while they form
+  if (active) {
 #pragma unroll
-    for (int q = 0; q < kGnInFlight; ++q) u[q] = xv[(pix + q * KP) * V + v];
+    for (int q = 0; q < kGnApplyInFlight; ++q)
+      if (pix + q * step < npix) u[q] = ld_stream(xv + (pix + q * step) * V + v);
 #pragma unroll
-    for (int q = 0; q < kGnInFlight; ++q) {
-      float f[VEC];
-      Elem<T>::unpack(u[q], f);
-#pragma unroll
-      for (int j = 0; j < VEC; ++j) {
-        f[j] = fmaf(f[j], a[j], sh[j]);
-        if (SILU) f[j] = silu_f(f[j]);
+    for (int e = 0; e < VEC; ++e) {
+      gm[e] = gamma[v * VEC + e];
+      bt[e] = beta[v * VEC + e];
+    }
+  }
+  for (int g = t; g < G; g += nt) tot[g] = make_double2(0.0, 0.0);
+  const int qb = kGnStage / G > 1 ? kGnStage / G : 1;  // patches per pass (G <= 256 <= kGnStage)
+  for (int q0 = 0; q0 < P; q0 += qb) {
+    const int nq = P - q0 < qb ? P - q0 : qb;
+    for (int i = t; i < G * nq; i += nt) {
+      const int g = i / nq, q = q0 + i % nq;
+      stage[i] = *reinterpret_cast<const float2*>((q == p ? stats : stale) +
+                                                  ((static_cast<int64_t>(b) * P + q) * G + g) * 2);
+    }
+    __syncthreads();
+    for (int g = t; g < G; g += nt) {
+      double2 a = tot[g];
+      for (int i = 0; i < nq; ++i) {
+        a.x += stage[g * nq + i].x;
+        a.y += stage[g * nq + i].y;
       }
-      st_stream(yv + (pix + q * KP) * V + v, Elem<T>::pack(f));
+      tot[g] = a;
     }
+    __syncthreads();
   }
-  for (; pix < p1; pix += KP) {
-    float f0[VEC];
-    Elem<T>::unpack(xv[pix * V + v], f0);
+  for (int g = t; g < G; g += nt) {
+    const double mean = tot[g].x / n;
+    double var = tot[g].y / n - mean * mean;
+    if (var < 0.0) var = 0.0;
+    coef[g] = make_float2(static_cast<float>(mean), static_cast<float>(1.0 / sqrt(var + static_cast<double>(eps))));
+  }
+  __syncthreads();
+  if (!active) return;
+  const int cg = C / G;
+  float ac[VEC], sh[VEC];
 #pragma unroll
-    for (int j = 0; j < VEC; ++j) {
-      f0[j] = fmaf(f0[j], a[j], sh[j]);
-      if (SILU) f0[j] = silu_f(f0[j]);
-    }
-    st_stream(yv + pix * V + v, Elem<T>::pack(f0));
+  for (int e = 0; e < VEC; ++e) {
+    const float2 mr = coef[(v * VEC + e) / cg];
+    ac[e] = mr.y * gm[e];
+    sh[e] = fmaf(-mr.x, ac[e], bt[e]);
   }
+  for (;;) {
+#pragma unroll
+    for (int q = 0; q < kGnApplyInFlight; ++q) {
+      const int64_t pq = pix + q * step;
+      if (pq < npix) {
+        float f[VEC];
+        Elem<T>::unpack(u[q], f);
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+          f[e] = fmaf(f[e], ac[e], sh[e]);
+          if (SILU) f[e] = silu_f(f[e]);
+        }
+        st_stream(yv + pq * V + v, Elem<T>::pack(f));
+      }
+    }
+    pix += kGnApplyInFlight * step;
+    if (pix >= npix) break;
+#pragma unroll
+    for (int q = 0; q < kGnApplyInFlight; ++q)
+      if (pix + q * step < npix) u[q] = ld_stream(xv + (pix + q * step) * V + v);
+  }
+}
+
+// The fresh sums to stats_out[b, p], then (y != NULL) the apply.
+template <typename T>
+static hipError_t gn_finish(T* y, float* stats_out, const T* x, const float* partial, int64_t nchunk,
+                            const float* stale, const float* gamma, const float* beta, int64_t B, int64_t H, int64_t W,
+                            int64_t C, int64_t G, int64_t P, int64_t p, int64_t rows, float eps, bool silu,
+                            hipStream_t s) {
+  hipLaunchKernelGGL(gn_stats_kernel, dim3(static_cast<unsigned>(ceil_div(G, kWave / kGnSet)),
+                                           static_cast<unsigned>(B)),
+                     dim3(kWave), 0, s, partial, nchunk, stats_out, static_cast<int>(G), static_cast<int>(P),
+                     static_cast<int>(p));
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess || y == nullptr) return err;
+  const int V = static_cast<int>(C / Elem<T>::kVec);
+  const int KP = kGnApplyThreads / V;
+  const int64_t npix = rows * W;
+  int64_t nwg = ceil_div(kGnApplyWgs, B);
+  const int64_t full = ceil_div(npix, static_cast<int64_t>(KP) * kGnApplyInFlight);  // one full batch per thread
+  if (nwg > full) nwg = full;
+  const double n = static_cast<double>(H) * static_cast<double>(W) * static_cast<double>(C / G);
+  const dim3 grid(static_cast<unsigned>(nwg), static_cast<unsigned>(B));
+  if (silu)
+    hipLaunchKernelGGL((gn_apply_kernel<T, true>), grid, dim3(KP * V), 0, s, x, y, stats_out, stale, gamma, beta, npix,
+                       static_cast<int>(C), static_cast<int>(G), V, KP, static_cast<int>(P), static_cast<int>(p), n,
+                       eps);
+  else
+    hipLaunchKernelGGL((gn_apply_kernel<T, false>), grid, dim3(KP * V), 0, s, x, y, stats_out, stale, gamma, beta, npix,
+                       static_cast<int>(C), static_cast<int>(G), V, KP, static_cast<int>(P), static_cast<int>(p), n,
+                       eps);
+  return hipGetLastError();
 }
 
 template <typename T>
@@ -303,27 +370,25 @@ static hipError_t gn_run(T* y, float* stats_out, const T* x, const float* stale,
                          int64_t p, int64_t rows, float eps, void* ws, bool silu, hipStream_t s) {
   const GnGeom g = gn_geom(B, rows, W, C, sizeof(T) == 2);
   float* partial = static_cast<float*>(ws);
-  float* coef = partial + B * g.nstat * G * 2;
   hipLaunchKernelGGL(gn_partial_kernel<T>, dim3(static_cast<unsigned>(g.nstat), static_cast<unsigned>(B)),
                      dim3(g.threads), 0, s, x, partial, g.npix, static_cast<int>(C), static_cast<int>(G), g.V, g.KP,
                      g.stat_ppc, g.nstat);
-  hipError_t err = hipGetLastError();
+  const hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  const double n = static_cast<double>(H) * static_cast<double>(W) * static_cast<double>(C / G);
-  hipLaunchKernelGGL(gn_finalize_kernel, dim3(static_cast<unsigned>(G), static_cast<unsigned>(B)), dim3(kWave), 0, s,
-                     partial, g.nstat,
-                     stale, stats_out, y ? coef : nullptr, static_cast<int>(G), static_cast<int>(P),
-                     static_cast<int>(p), n, eps);
-  err = hipGetLastError();
-  if (err != hipSuccess || y == nullptr) return err;
-  const dim3 agrid(static_cast<unsigned>(g.napply), static_cast<unsigned>(B));
-  if (silu)
-    hipLaunchKernelGGL((gn_apply_kernel<T, true>), agrid, dim3(g.threads), 0, s, x, y, coef, gamma, beta, g.npix,
-                       static_cast<int>(C), static_cast<int>(G), g.V, g.KP, g.apply_ppc);
-  else
-    hipLaunchKernelGGL((gn_apply_kernel<T, false>), agrid, dim3(g.threads), 0, s, x, y, coef, gamma, beta, g.npix,
-                       static_cast<int>(C), static_cast<int>(G), g.V, g.KP, g.apply_ppc);
-  return hipGetLastError();
+  return gn_finish(y, stats_out, x, partial, g.nstat, stale, gamma, beta, B, H, W, C, G, P, p, rows, eps, silu, s);
+}
+
+// Fresh sums from a producer's partials: one kernel (or the statistics-only
+// one), x read once.
+hipError_t launch_groupnorm_presummed(void* y, float* stats_out, const void* x, const float* partials, int64_t nchunk,
+                                      const float* stale_stats, const float* gamma, const float* beta, int64_t B,
+                                      int64_t H, int64_t W, int64_t C, int64_t G, int64_t P, int64_t p, int64_t rows,
+                                      float eps, bool bf16, bool silu, hipStream_t s) {
+  if (bf16)
+    return gn_finish(static_cast<uint16_t*>(y), stats_out, static_cast<const uint16_t*>(x), partials, nchunk,
+                     stale_stats, gamma, beta, B, H, W, C, G, P, p, rows, eps, silu, s);
+  return gn_finish(static_cast<float*>(y), stats_out, static_cast<const float*>(x), partials, nchunk, stale_stats,
+                   gamma, beta, B, H, W, C, G, P, p, rows, eps, silu, s);
 }
 
 hipError_t launch_groupnorm(void* y, float* stats_out, const void* x, const float* stale_stats, const float* gamma,

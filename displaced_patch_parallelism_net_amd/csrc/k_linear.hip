@@ -51,6 +51,8 @@ struct LinArgs {
   const float* bias;
   uint16_t* y;
   int64_t M, K, N, ld_x, bs_x, ld_y, bs_y;
+  float* gn_part;  // GroupNorm partial sums of y [B][gridDim.x * gridDim.y][G][2], or NULL
+  int G;
 };
 
 // LDS row of 8 x 16-byte slots, slot XOR-swizzled by the row index.
@@ -230,10 +232,37 @@ __global__ __launch_bounds__(kLinThreads) void linear_bf16_mfma_kernel(LinArgs a
     if (m < a.M && n < a.N)
       *reinterpret_cast<uint2*>(a.y + b * a.bs_y + m * a.ld_y + n) = tile[r * kRowU2 + q];
   }
+  if (a.gn_part != nullptr) {
+    // GroupNorm partial sums of this tile's stored values (tokens = pixels),
+    // one chunk per workgroup; the LDS past the output tile is the scratch
+    const int64_t nchunk = static_cast<int64_t>(gridDim.x) * gridDim.y;
+    const int64_t chunk = static_cast<int64_t>(blockIdx.y) * gridDim.x + blockIdx.x;
+    static_assert((kLinBM * kRowU2 * 8 + 4 * tile_group_sums_scratch_floats<kLinThreads, kLinBN>()) <= sizeof(smem),
+                  "statistics scratch fits after the staged tile");
+    tile_group_sums<kLinThreads, kLinBM, kLinBN>(
+        reinterpret_cast<const uint16_t*>(tile), 4 * kRowU2, [&](int r) { return m0 + r < a.M; },
+        static_cast<int>(n0), static_cast<int>(a.N), static_cast<int>(a.N / a.G), a.G,
+        reinterpret_cast<float*>(tile + kLinBM * kRowU2), a.gn_part + (b * nchunk + chunk) * a.G * 2);
+  }
+}
+
+// Channel tile of the bf16 kernel: the one with the fewer rounds of
+// workgroups times tile width (one workgroup per CU); ties go to the wider
+// tile (fewer loads of the token rows, one prologue instead of several).
+static bool linear_wide(int64_t B, int64_t M, int64_t N) {
+  const int64_t tm = ceil_div(M, kLinBM) * B;
+  const int64_t cost2 = ceil_div(tm * ceil_div(N, 128), 256) * 128;
+  const int64_t cost4 = ceil_div(tm * ceil_div(N, 256), 256) * 256;
+  return cost4 <= cost2;
+}
+
+int64_t linear_gn_chunks(int64_t B, int64_t M, int64_t N) {
+  return ceil_div(M, kLinBM) * ceil_div(N, linear_wide(B, M, N) ? 256 : 128);
 }
 
 hipError_t launch_linear(void* y, const void* x, const void* w, const float* bias, int64_t B, int64_t M, int64_t K,
-                         int64_t N, int64_t ld_x, int64_t bs_x, int64_t ld_y, int64_t bs_y, bool bf16, hipStream_t s) {
+                         int64_t N, int64_t ld_x, int64_t bs_x, int64_t ld_y, int64_t bs_y, bool bf16, hipStream_t s,
+                         float* gn_part, int G) {
   if (!bf16) {
     int64_t blocks = ceil_div(M * N, 256);
     if (blocks > 65535) blocks = 65535;
@@ -254,13 +283,9 @@ hipError_t launch_linear(void* y, const void* x, const void* w, const float* bia
   a.bs_x = bs_x;
   a.ld_y = ld_y;
   a.bs_y = bs_y;
-  // channel tile: the one with the fewer rounds of workgroups times tile
-  // width (one workgroup per CU); ties go to the wider tile (fewer loads of
-  // the token rows, one prologue instead of several)
-  const int64_t tm = ceil_div(M, kLinBM) * B;
-  const int64_t cost2 = ceil_div(tm * ceil_div(N, 128), 256) * 128;
-  const int64_t cost4 = ceil_div(tm * ceil_div(N, 256), 256) * 256;
-  const bool wide = cost4 <= cost2;
+  a.gn_part = gn_part;
+  a.G = G;
+  const bool wide = linear_wide(B, M, N);
   dim3 grid(static_cast<unsigned>(ceil_div(M, kLinBM)), static_cast<unsigned>(ceil_div(N, wide ? 256 : 128)),
             static_cast<unsigned>(B));
   const dim3 blk(kLinThreads);

@@ -141,16 +141,45 @@ int dpp_groupnorm_silu_stale(void* y, float* stats_out, const void* x,
                              int dtype, void* stream);
 
 /*
+ * GroupNorm with stale statistics whose fresh sums come from the kernel that
+ * produced x, so x is read once (DistriGroupNorm; DistriFusion architecture
+ * article, normalisation section).  The producers dpp_conv3x3_halo_gn and
+ * dpp_linear_gn write, besides their output, its GroupNorm partial sums:
+ *   partials [B,nchunk,G,2] float32: per chunk and group (sum y, sum y^2) of
+ *            the stored output values over the chunk's pixels and the
+ *            group's channels (zero where the chunk does not touch it).
+ * This call adds the chunks in float64, in chunk order, as the fresh sums s1,
+ * s2 of dpp_groupnorm_stale, and continues exactly as that call (stale
+ * correction, mean/var, normalisation, stats_out[b,p] = the fresh sums);
+ * silu != 0 applies SiLU to the result as dpp_groupnorm_silu_stale does.
+ *   x, y [B,rows,W,C] as dpp_groupnorm_stale (y == NULL: stats_out only);
+ *   partials as written by the producer of x for the same
+ *   B, G and shape; nchunk >= 1 its chunk count (the producer's *_gn_chunks).
+ *   The result depends on partials only through their per-group sums: with
+ *   partials of values other than x's, it normalises x with those sums.
+ *   No workspace: one launch (the group totals are formed on chip by every
+ *   workgroup, in one fixed order).  Requirements and errors otherwise as
+ *   dpp_groupnorm_stale; partials must not overlap y or stats_out.
+ */
+int dpp_groupnorm_stale_presummed(void* y, float* stats_out, const void* x,
+                                  const float* partials, int64_t nchunk,
+                                  const float* stale_stats, const float* gamma,
+                                  const float* beta, int64_t B, int64_t H,
+                                  int64_t W, int64_t C, int64_t G, int64_t P,
+                                  int64_t p, int64_t rows, float eps,
+                                  int silu, int dtype, void* stream);
+
+/*
  * dpp_groupnorm_stale without a workspace argument, for callers that cannot
  * allocate device memory: code under HIP graph capture, tight serving loops,
- * harnesses that forbid hipMalloc.  The scratch it needs (the partial sums
- * and per-group mean/rstd that dpp_groupnorm_stale keeps in its workspace)
- * lives in a static device array of DPP_GN_NOALLOC_MAX_BYTES inside the
+ * harnesses that forbid hipMalloc.  The scratch it needs (the chunk partial
+ * sums that dpp_groupnorm_stale keeps in its workspace) lives in a static
+ * device array of DPP_GN_NOALLOC_MAX_BYTES inside the
  * library; each GPU holds its own copy from the first call made with that
  * device current until the process ends.  The call allocates and frees
  * nothing.  Shapes whose scratch
  * (dpp_groupnorm_stale_workspace_bytes) exceeds DPP_GN_NOALLOC_MAX_BYTES
- * return DPP_ERR_WORKSPACE -- e.g. G = 32 fits every B <= 2048.  All calls on
+ * return DPP_ERR_WORKSPACE -- e.g. G = 32 fits every B <= 4096.  All calls on
  * one GPU share that GPU's array: calls that may overlap on one GPU (several
  * streams, several host threads without ordering) race and must be ordered
  * by the caller.  Nothing in the array needs clearing: every element a call
@@ -214,6 +243,23 @@ int dpp_conv3x3_halo_ws(void* y, const void* x, const void* stale_full,
                         size_t workspace_bytes, int dtype, void* stream);
 
 /*
+ * dpp_conv3x3_halo that also writes the GroupNorm partial sums of its output
+ * for a GroupNorm that follows (dpp_groupnorm_stale_presummed), from the
+ * stored bf16 values, one chunk per output tile:
+ *   gn_partials [B, dpp_conv3x3_halo_gn_chunks(rows, W, Cout), G, 2] float32
+ * G groups of Cout/G channels (Cout % G == 0, else DPP_ERR_SHAPE).  y is
+ * bit-identical to dpp_conv3x3_halo's; always unsplit (no workspace).  bf16
+ * only (DPP_F32: DPP_ERR_UNSUPPORTED).  gn_partials must not overlap an
+ * operand.  Everything else exactly as dpp_conv3x3_halo.
+ */
+int64_t dpp_conv3x3_halo_gn_chunks(int64_t rows, int64_t W, int64_t Cout);
+int dpp_conv3x3_halo_gn(void* y, float* gn_partials, int64_t G, const void* x,
+                        const void* stale_full, const void* weight,
+                        const float* bias, int64_t B, int64_t H, int64_t W,
+                        int64_t Cin, int64_t Cout, int64_t row0, int64_t rows,
+                        int dtype, void* stream);
+
+/*
  * a4 -- displaced self-attention (DistriSelfAttentionPP; DistriFusion
  * architecture article, attention section).  The patch's queries attend over
  * all tokens of the spliced full-image K/V buffer (fresh own rows, previous
@@ -267,6 +313,23 @@ int dpp_linear(void* y, const void* x, const void* w, const float* bias,
                int64_t B, int64_t M, int64_t K, int64_t N, int64_t ld_x,
                int64_t bs_x, int64_t ld_y, int64_t bs_y, int dtype,
                void* stream);
+
+/*
+ * dpp_linear that also writes the GroupNorm partial sums of its output (the
+ * M rows of a batch entry are the pixels, the N columns the channels) for a
+ * GroupNorm that follows, e.g. the out projection feeding the next block's
+ * GroupNorm (dpp_groupnorm_stale_presummed), from the stored bf16 values:
+ *   gn_partials [B, dpp_linear_gn_chunks(B, M, N), G, 2] float32
+ * G groups of N/G channels (N % G == 0, else DPP_ERR_SHAPE).  y is
+ * bit-identical to dpp_linear's.  bf16 only (DPP_F32:
+ * DPP_ERR_UNSUPPORTED).  gn_partials must not overlap an operand.
+ * Everything else exactly as dpp_linear.
+ */
+int64_t dpp_linear_gn_chunks(int64_t B, int64_t M, int64_t N);
+int dpp_linear_gn(void* y, float* gn_partials, int64_t G, const void* x,
+                  const void* w, const float* bias, int64_t B, int64_t M,
+                  int64_t K, int64_t N, int64_t ld_x, int64_t bs_x,
+                  int64_t ld_y, int64_t bs_y, int dtype, void* stream);
 
 /*
  * a5 -- classifier-free guidance combine and denoising discrepancy

@@ -57,6 +57,11 @@ Readings where the pages are silent (each also listed in the design notes):
   R14 component step: a component is the full-image block (P = 1) GN -> conv
       -> attention with identity projections; its input after the warm-up is
       the previous step's stored output of the component before it.
+  R15 attention block: GroupNorm + SiLU -> conv -> q projection, fresh k, v
+      projections spliced into the previous step's projected K, V -> attention
+      -> out projection; the previous step is the synchronous full-image run
+      of the same block on the stale input, whose projected K, V every patch
+      starts from.
 """
 from .dpp_oracle import (  # noqa: F401
     bf16_round,
@@ -76,4 +81,6 @@ from .dpp_oracle import (  # noqa: F401
     displaced_block,
     component_block,
     async_component_chain,
+    previous_block_state,
+    displaced_attention_block,
 )

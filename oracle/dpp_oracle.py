@@ -427,3 +427,72 @@ def async_component_chain(xs, params, G: int, heads: int, eps: float, bf16: bool
             row.append(component_block(src, p["gamma"], p["beta"], p["conv_w"], p["conv_b"], G, heads, eps, bf16))
         outs.append(row)
     return outs
+
+
+# ------------------------------------------------------------------ next-1: attention block with projections
+def previous_block_state(x_stale, gamma, beta, conv_w, conv_b, wk, bk, wv, bv, P: int, G: int, eps: float,
+                         bf16: bool):
+    """The synchronous first step of the attention block on the stale input
+    (every patch fresh, each layer the plain full-image layer; DistriFusion
+    reading notes, Introduction fourth paragraph).
+
+    Returns stale_stats [B,P,G,2] (raw sums of each patch of x_stale), a1 =
+    GroupNorm + SiLU of the whole stale image (stored), a2 = its conv
+    (stored), and the projected k, v [B,N,C] of a2 (stored): the previous
+    step's K/V buffer every patch starts from (readings R11, R12); with
+    a1_exact, a2_exact, k_exact, v_exact before storage rounding (each from
+    the previous stage's stored values)."""
+    xs = _f64(x_stale)
+    B, H, W, C = xs.shape
+    R = H // P
+    stats = np.stack([patch_sums(xs[:, q * R:(q + 1) * R], G) for q in range(P)], axis=1)
+    a1_exact = groupnorm_silu_stale(xs, None, gamma, beta, H, G, 0, eps)[0]
+    a1 = _store(a1_exact, bf16)
+    a2_exact = conv3x3_halo(a1, None, conv_w, conv_b, 0)
+    a2 = _store(a2_exact, bf16)
+    t = a2.reshape(B, H * W, C)
+    k_exact, v_exact = linear(t, wk, bk), linear(t, wv, bv)
+    return {"stale_stats": stats, "a1": a1, "a2": a2, "k": _store(k_exact, bf16), "v": _store(v_exact, bf16),
+            "a1_exact": a1_exact, "a2_exact": a2_exact, "k_exact": k_exact, "v_exact": v_exact}
+
+
+def displaced_attention_block(x_fresh, state, gamma, beta, conv_w, conv_b, wq, bq, wk, bk, wv, bv, wo, bo, P: int,
+                              p: int, G: int, heads: int, eps: float, bf16: bool, attn_rows=None):
+    """One device's share (patch p) of the attention block with its
+    projections: GroupNorm + SiLU with stale statistics -> 3x3 conv with stale
+    halos -> q projection, and the fresh k, v projections replacing the
+    patch's tokens in the previous step's projected K/V -> self-attention over
+    all tokens -> out projection (DistriGroupNorm, DistriConv2dPP and
+    DistriSelfAttentionPP around the whole attention module: DistriFusion
+    architecture article; readings R11, R12).
+
+    x_fresh [B,H,W,C] (the patch's rows are used); state from
+    previous_block_state.  Each stored stage is rounded to bf16 when bf16;
+    each *_exact value is computed from the previous stage's stored values.
+    attn_rows=(b_idx, q_idx) evaluates the attention and the out projection
+    only at those query tokens (o_rows_exact, out_rows_exact); otherwise o,
+    out and their exact values cover all query tokens."""
+    xf = _f64(x_fresh)
+    B, H, W, C = xf.shape
+    R = H // P
+    r0 = p * R
+    t0 = r0 * W
+    y1_exact, fresh = groupnorm_silu_stale(xf[:, r0:r0 + R], state["stale_stats"], gamma, beta, H, G, p, eps)
+    y1 = _store(y1_exact, bf16)
+    y2_exact = conv3x3_halo(y1, state["a1"], conv_w, conv_b, r0)
+    y2 = _store(y2_exact, bf16)
+    tok = y2.reshape(B, R * W, C)
+    res = {"y1": y1, "y2": y2, "y1_exact": y1_exact, "y2_exact": y2_exact, "stats": fresh}
+    if attn_rows is None:
+        res.update(projected_attention(tok, state["k"], state["v"], t0, wq, bq, wk, bk, wv, bv, wo, bo, heads, bf16))
+        return res
+    q_exact = linear(tok, wq, bq)
+    k_exact, v_exact = linear(tok, wk, bk), linear(tok, wv, bv)
+    q = _store(q_exact, bf16)
+    K, V = _f64(state["k"]).copy(), _f64(state["v"]).copy()
+    K[:, t0:t0 + R * W] = _store(k_exact, bf16)
+    V[:, t0:t0 + R * W] = _store(v_exact, bf16)
+    o_rows_exact = self_attn_displaced(q, K, V, heads, rows=attn_rows)
+    res.update({"q_exact": q_exact, "k_exact": k_exact, "v_exact": v_exact, "o_rows_exact": o_rows_exact,
+                "out_rows_exact": linear(_store(o_rows_exact, bf16), wo, bo)})
+    return res

@@ -38,7 +38,7 @@ def header_symbols():
 
 def test_header_symbols_exported_and_bound():
     syms = header_symbols()
-    assert len(syms) == 16, syms
+    assert len(syms) == 21, syms
     for s in syms:
         assert hasattr(L, s), s
         assert s in _lib.SIGNATURES, s
@@ -355,7 +355,47 @@ def test_groupnorm_noalloc_validation():
     assert gn_noalloc(so=Dp) == ALIAS
     assert gn_noalloc(y=Cp) == ALIAS
     # shapes whose scratch exceeds the static array: refused, nothing launched
-    need = dpp.dpp_groupnorm_stale_workspace_bytes(4096, 4, 4, 64, 32)
+    need = dpp.dpp_groupnorm_stale_workspace_bytes(4097, 4, 4, 64, 32)
     assert need > _lib.GN_NOALLOC_MAX_BYTES
-    assert gn_noalloc(B=4096, H=8, W=4, C=64, G=32, P=2, rows=4) == WS
-    assert dpp.dpp_groupnorm_stale_workspace_bytes(2048, 4, 4, 64, 32) <= _lib.GN_NOALLOC_MAX_BYTES
+    assert gn_noalloc(B=4097, H=8, W=4, C=64, G=32, P=2, rows=4) == WS
+    assert dpp.dpp_groupnorm_stale_workspace_bytes(4096, 4, 4, 64, 32) <= _lib.GN_NOALLOC_MAX_BYTES
+
+
+def test_producer_statistics_and_presummed_validation():
+    # conv with GroupNorm partials: the conv's own checks, then its own
+    assert L.dpp_conv3x3_halo_gn_chunks(30, 240, 640) == 225          # 15 row pairs x 3 column tiles x 5 channel tiles
+    assert L.dpp_linear_gn_chunks(1, 7200, 640) == 225                 # 45 token tiles x 5 channel tiles
+    assert L.dpp_linear_gn_chunks(1, 7200, 1280) == 225                # 256-channel tiles: 45 x 5
+    assert L.dpp_conv3x3_halo_gn_chunks(0, 240, 640) == 0
+
+    def cgn(y=A, part=WSP, G=32, x=Bp, st=Cp, w=Dp, bias=Ep, B=1, H=8, W=16, Cin=64, Cout=64, row0=2, rows=2,
+            dtype=BF16):
+        return _no_launch(L.dpp_conv3x3_halo_gn(y, part, G, x, st, w, bias, B, H, W, Cin, Cout, row0, rows, dtype,
+                                                None))
+    assert cgn(part=None) == NULL
+    assert cgn(G=0) == SHAPE
+    assert cgn(G=24) == SHAPE                      # Cout % G
+    assert cgn(dtype=F32, Cin=12, Cout=12, G=4) == UNSUP
+    assert cgn(part=A + 64) == ALIAS               # inside y
+    assert cgn(rows=0) == SHAPE                    # the conv's own checks first
+    assert cgn(y=None) == NULL
+
+    def lgn(y=A, part=WSP, G=32, x=Bp, w=Cp, bias=Dp, B=1, M=64, K=64, N=64, ldx=64, bsx=4096, ldy=64, bsy=4096,
+            dtype=BF16):
+        return _no_launch(L.dpp_linear_gn(y, part, G, x, w, bias, B, M, K, N, ldx, bsx, ldy, bsy, dtype, None))
+    assert lgn(part=None) == NULL
+    assert lgn(G=48) == SHAPE                      # N % G
+    assert lgn(dtype=F32) == UNSUP
+    assert lgn(part=Cp + 16) == ALIAS              # inside the weights
+    assert lgn(ldx=60) == SHAPE                    # the GEMM's own checks first
+
+    def pgn(y=A, so=Bp, x=Cp, part=WSP + (1 << 20), nchunk=5, st=Dp, gamma=Ep, beta=Ep + 4096, B=1, H=8, W=4, C=64,
+            G=8, P=2, p=0, rows=4, eps=1e-5, silu=0, dtype=BF16):
+        return _no_launch(L.dpp_groupnorm_stale_presummed(y, so, x, part, nchunk, st, gamma, beta, B, H, W, C, G, P, p,
+                                                          rows, eps, silu, dtype, None))
+    assert pgn(part=None) == NULL
+    assert pgn(nchunk=0) == SHAPE
+    assert pgn(part=Bp) == ALIAS                   # partials == stats_out
+    assert pgn(part=A + 64) == ALIAS               # partials inside y
+    assert pgn(C=60) == SHAPE                      # GroupNorm's own checks first
+    assert pgn(st=None) == NULL

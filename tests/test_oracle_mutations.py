@@ -43,6 +43,10 @@ MUTATIONS = [
     ("schedule_strict_flattening", "decline <= rho32 * fastest", "decline < rho32 * fastest"),
     ("schedule_no_hysteresis", "if d[i] > grow * lowest:", "if d[i] > lowest:"),
     ("chain_reads_this_step", "src = outs[t - 1][k - 1][\"o\"]", "src = row[k - 1][\"o\"]"),
+    ("block_kv_not_spliced", "    K[:, t0:t0 + R * W] = _store(k_exact, bf16)\n", "\n"),
+    ("block_halo_from_conv_output", "y2_exact = conv3x3_halo(y1, state[\"a1\"], conv_w, conv_b, r0)",
+     "y2_exact = conv3x3_halo(y1, state[\"a2\"], conv_w, conv_b, r0)"),
+    ("block_previous_kv_from_gn", "    t = a2.reshape(B, H * W, C)\n", "    t = a1.reshape(B, H * W, C)\n"),
 ]
 
 

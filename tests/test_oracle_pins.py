@@ -680,3 +680,102 @@ def test_async_chain_bf16_rounds_every_stored_output():
             for n in ("y1", "y2", "o"):
                 assert np.array_equal(r[n], oracle.bf16_round(r[n]))
                 assert np.abs(r[n] - r[n + "_exact"]).max() > 0
+
+
+# ----------------------------------------------------------------- attention block (R15)
+def _block_params(C, rng):
+    gamma = 1 + 0.1 * rng.standard_normal(C)
+    beta = 0.1 * rng.standard_normal(C)
+    wt = 0.2 * rng.standard_normal((C, 3, 3, C))
+    bias = 0.1 * rng.standard_normal(C)
+    proj = [x for _ in range(4) for x in (rng.standard_normal((C, C)) / np.sqrt(C), 0.1 * rng.standard_normal(C))]
+    return gamma, beta, wt, bias, proj
+
+
+def _torch_attention_block(torch, S_gn, S_conv, k_src, gamma, beta, wt, bias, proj, G, heads, eps, r0, R):
+    """The block's layers by torch float64 library calls on spliced images:
+    group_norm + silu of S_gn, conv2d of S_conv (the spliced GroupNorm+SiLU
+    image), the patch's rows projected, attention over K/V = projections of
+    k_src (the spliced conv image), out projection."""
+    F = torch.nn.functional
+    T = lambda a: torch.from_numpy(np.ascontiguousarray(a))  # noqa: E731
+    wq, bq, wk, bk, wv, bv, wo, bo = proj
+    gn = F.silu(F.group_norm(T(S_gn).permute(0, 3, 1, 2), G, T(gamma), T(beta), eps=eps))
+    cv = F.conv2d(T(S_conv).permute(0, 3, 1, 2), T(wt).permute(0, 3, 1, 2), T(bias), padding=1)
+    B, C, H, W = cv.shape
+    rows = cv.permute(0, 2, 3, 1)[:, r0:r0 + R].reshape(B, R * W, C)
+    q = F.linear(rows, T(wq), T(bq))
+    kv_in = T(k_src).reshape(B, H * W, C)
+    k, v = F.linear(kv_in, T(wk), T(bk)), F.linear(kv_in, T(wv), T(bv))
+    hd = C // heads
+    split = lambda t: t.reshape(B, t.shape[1], heads, hd).permute(0, 2, 1, 3)  # noqa: E731
+    o = F.scaled_dot_product_attention(split(q), split(k), split(v)).permute(0, 2, 1, 3).reshape(B, R * W, C)
+    out = F.linear(o, T(wo), T(bo))
+    return gn.permute(0, 2, 3, 1).numpy(), cv.permute(0, 2, 3, 1).numpy(), out.numpy()
+
+
+@pytest.mark.parametrize("P", [1, 2, 4])
+def test_attention_block_stale_equals_fresh_is_full_block(torch_cpu, P):
+    # Synchronous first step: with stale == fresh, patch p's block output is
+    # the unpatched full-image block's output on its rows.
+    torch = torch_cpu
+    B, H, W, C, G, heads = 2, 8, 5, 16, 4, 2
+    rng = np.random.default_rng(51)
+    x = rng.standard_normal((B, H, W, C))
+    gamma, beta, wt, bias, proj = _block_params(C, rng)
+    wq, bq, wk, bk, wv, bv, wo, bo = proj
+    st = oracle.previous_block_state(x, gamma, beta, wt, bias, wk, bk, wv, bv, P, G, 1e-5, bf16=False)
+    st1 = oracle.previous_block_state(x, gamma, beta, wt, bias, wk, bk, wv, bv, 1, G, 1e-5, bf16=False)
+    full = oracle.displaced_attention_block(x, st1, gamma, beta, wt, bias, *proj, 1, 0, G, heads, 1e-5, bf16=False)
+    # the unpatched block is torch's layers on the image itself
+    _, _, out_torch = _torch_attention_block(torch, x, full["y1"], full["y2"], gamma, beta, wt, bias, proj, G, heads,
+                                             1e-5, 0, H)
+    np.testing.assert_allclose(full["out_exact"], out_torch, rtol=0, atol=1e-10)
+    R = H // P
+    for p in range(P):
+        out = oracle.displaced_attention_block(x, st, gamma, beta, wt, bias, *proj, P, p, G, heads, 1e-5, bf16=False)
+        np.testing.assert_allclose(out["out_exact"], full["out_exact"][:, p * R * W:(p + 1) * R * W], rtol=0,
+                                   atol=1e-11)
+        np.testing.assert_allclose(out["k"], full["k"], rtol=0, atol=1e-11)
+
+
+@pytest.mark.parametrize("P,p", [(2, 0), (4, 1), (4, 3)])
+def test_attention_block_matches_torch_layers_on_spliced_images(torch_cpu, P, p):
+    # stale != fresh: every stage equals torch's float64 layers on the spliced
+    # images the pages' scheme defines (fresh own rows, previous step's rest)
+    torch = torch_cpu
+    B, H, W, C, G, heads = 1, 8, 6, 16, 4, 2
+    rng = np.random.default_rng(52)
+    xs = rng.standard_normal((B, H, W, C))
+    xf = xs + 0.3 * rng.standard_normal((B, H, W, C))
+    gamma, beta, wt, bias, proj = _block_params(C, rng)
+    wq, bq, wk, bk, wv, bv, wo, bo = proj
+    st = oracle.previous_block_state(xs, gamma, beta, wt, bias, wk, bk, wv, bv, P, G, 1e-5, bf16=False)
+    R = H // P
+    r0 = p * R
+    out = oracle.displaced_attention_block(xf, st, gamma, beta, wt, bias, *proj, P, p, G, heads, 1e-5, bf16=False)
+    S_gn = spliced(xs, xf[:, r0:r0 + R], r0)
+    S_conv = spliced(st["a1"], out["y1"], r0)
+    S_kv = spliced(st["a2"], out["y2"], r0)
+    gn, cv, want = _torch_attention_block(torch, S_gn, S_conv, S_kv, gamma, beta, wt, bias, proj, G, heads, 1e-5, r0,
+                                          R)
+    np.testing.assert_allclose(out["y1"], gn[:, r0:r0 + R], rtol=0, atol=1e-11)
+    np.testing.assert_allclose(out["y2"], cv[:, r0:r0 + R], rtol=0, atol=1e-10)
+    np.testing.assert_allclose(out["out_exact"], want, rtol=0, atol=1e-10)
+
+
+def test_attention_block_sampled_rows_equal_full():
+    B, H, W, C, G, heads, P, p = 2, 8, 4, 16, 4, 2, 4, 2
+    rng = np.random.default_rng(53)
+    xs = rng.standard_normal((B, H, W, C))
+    xf = xs + 0.3 * rng.standard_normal((B, H, W, C))
+    gamma, beta, wt, bias, proj = _block_params(C, rng)
+    wq, bq, wk, bk, wv, bv, wo, bo = proj
+    for bf in (False, True):
+        st = oracle.previous_block_state(xs, gamma, beta, wt, bias, wk, bk, wv, bv, P, G, 1e-5, bf16=bf)
+        full = oracle.displaced_attention_block(xf, st, gamma, beta, wt, bias, *proj, P, p, G, heads, 1e-5, bf16=bf)
+        bi, qi = np.array([0, 1, 1, 0]), np.array([0, 7, 3, 5])
+        part = oracle.displaced_attention_block(xf, st, gamma, beta, wt, bias, *proj, P, p, G, heads, 1e-5, bf16=bf,
+                                                attn_rows=(bi, qi))
+        np.testing.assert_allclose(part["out_rows_exact"], full["out_exact"][bi, qi], rtol=0, atol=1e-13)
+        np.testing.assert_allclose(part["o_rows_exact"], full["o_exact"][bi, qi], rtol=0, atol=1e-13)
