@@ -280,6 +280,15 @@ def run(args):
     f_conv, f_attn = flops(cfg)
     step_flops = cfg.P * (f_conv + f_attn)
     value = step_flops / (wall / args.steps) / 1e12
+    # The same attention calls back to back between one event pair (the
+    # step's last inputs): free of the host's launch gaps that the per-call
+    # events inside the step include at small sizes, but run under the
+    # sustained load of attention alone, which lowers the clock.
+    attn_b2b_ms = time_back_to_back(
+        [lambda p=p: dpp.dpp_self_attn_displaced(layer.o, layer.y2.view(cfg.B, cfg.Nq, cfg.C),
+                                                  layer.kv[p].view(cfg.B, cfg.N, cfg.C),
+                                                  layer.kv[p].view(cfg.B, cfg.N, cfg.C), cfg.heads, cfg.D, 0.0,
+                                                  layer.attn_ws) for p in range(cfg.P)], torch)
     attn_tflops = f_attn / (attn_ms * 1e-3) / 1e12
 
     block = time_attention_block(cfg, dpp, torch) if cfg.dtype == "bf16" else None
@@ -331,6 +340,10 @@ def run(args):
             "traffic": measured_traffic(cfg.name),
             "traffic_unit": "bytes per call (attention + split merge), FETCH_SIZE + WRITE_SIZE scaled by a plain copy",
             "avg_launch_ms": round(attn_ms, 5),
+            "avg_launch_ms_back_to_back": round(attn_b2b_ms, 5),
+            "timing": "HIP events on the launch stream around each attention call inside the timed steps "
+                      "(avg_launch_ms); around every patch's call launched back to back after the timed steps "
+                      "(avg_launch_ms_back_to_back)",
             "flops_per_launch": f_attn,
         },
     }
@@ -343,6 +356,34 @@ def run(args):
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(cfg, args.cpu_budget_s)
     return out
+
+
+def host_ahead(torch, n_calls):
+    """Hold the stream with a bounded spin kernel (about 100 us of shader
+    clock per call that follows, well above the host's cost of one binding
+    call) so the host has queued the next `n_calls` calls and their events
+    before the GPU reaches them: per-call events then time the kernels, not
+    the gaps while the host launches the next one."""
+    torch.cuda._sleep(int(min(n_calls, 4000) * 250000))
+
+
+def time_back_to_back(calls, torch, min_calls=50):
+    """Mean ms per call of `calls` launched round-robin, back to back, for at
+    least `min_calls` calls between one pair of events on the current stream
+    (after one untimed round, behind a spin that lets the host queue them
+    all first)."""
+    rounds = -(-min_calls // len(calls))
+    for fn in calls:
+        fn()
+    host_ahead(torch, rounds * len(calls))
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(rounds):
+        for fn in calls:
+            fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / (rounds * len(calls))
 
 
 def time_attention_block(cfg, dpp, torch, reps=3):
@@ -372,6 +413,7 @@ def time_attention_block(cfg, dpp, torch, reps=3):
         blk.patch_step(p, xp[p], gamma, beta, cw, cb, wq, bq, wkv, bkv, wo, bo)
     torch.cuda.synchronize()
     ev = []
+    host_ahead(torch, 8 * reps * cfg.P)
     for _ in range(reps):
         for p in range(cfg.P):
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -405,6 +447,7 @@ def time_kernels(cfg, layer, x_patches, gamma, beta, w, b, eps, rel, eps_c, eps_
         e1.record()
         ev[name].append((e0, e1))
 
+    host_ahead(torch, reps * (4 * cfg.P + 1))
     for _ in range(reps):
         for p in range(cfg.P):
             r0 = p * layer.R
@@ -424,6 +467,7 @@ def time_kernels(cfg, layer, x_patches, gamma, beta, w, b, eps, rel, eps_c, eps_
         nchunk = dpp.dpp_conv3x3_halo_gn_chunks(cfg.rows, cfg.W, cfg.C)
         part = torch.empty(cfg.B, nchunk, cfg.G, 2, dtype=torch.float32, device="cuda")
         h = torch.empty_like(layer.y2)
+        host_ahead(torch, reps * 2 * cfg.P)
         for _ in range(reps):
             for p in range(cfg.P):
                 r0 = p * layer.R
@@ -496,6 +540,7 @@ def time_projections(cfg, layer, x_patches, gamma, beta, dpp, torch, reps=10):
         e1.record()
         ev[name].append((e0, e1))
 
+    host_ahead(torch, reps * 6 * cfg.P)
     for _ in range(reps):
         for p in range(cfg.P):
             t0 = p * M
