@@ -228,6 +228,9 @@ __global__ __launch_bounds__(kAttThreads, 2) void attn_bf16_kernel(AttnArgs a) {
   // MFMA far better than the packed bf16 dot product, and the normaliser
   // then differs from the sum of the rounded weights only by their
   // independent rounding errors.
+  // The first chunk of a query block (t16 == 0) starts its partial sum
+  // instead of adding to a zero: 0 + x is not x for x = -0, so an add of
+  // zero would stay in the code.
   auto exp_chunk = [&](const f32x16 (&S)[2], int qb2, int t16, const float (&m)[2], bf16x8 (&P)[2][2], float (&ls)[2]) {
     uint32_t w[4];
     float s2[4];
@@ -238,7 +241,8 @@ __global__ __launch_bounds__(kAttThreads, 2) void attn_bf16_kernel(AttnArgs a) {
       w[e] = pack_bf16x2(p0, p1);
       s2[e] = p0 + p1;
     }
-    ls[qb2] += (s2[0] + s2[1]) + (s2[2] + s2[3]);
+    const float sum = (s2[0] + s2[1]) + (s2[2] + s2[3]);
+    ls[qb2] = t16 == 0 ? sum : ls[qb2] + sum;
     P[qb2][t16] = __builtin_bit_cast(bf16x8, make_uint4(w[0], w[1], w[2], w[3]));
   };
   // scores of a unit in the ragged last tile: keys past the range -> -inf
@@ -260,7 +264,7 @@ __global__ __launch_bounds__(kAttThreads, 2) void attn_bf16_kernel(AttnArgs a) {
     const bf16x8 kf2 = k_frag(buf_k, kh_next, 2), kf3 = k_frag(buf_k, kh_next, 3);
     const bf16x8 vf00 = v_frag(buf_v, 0, kh_prev, 0), vf01 = v_frag(buf_v, 0, kh_prev, 1);
     const bf16x8 vf10 = v_frag(buf_v, 1, kh_prev, 0), vf11 = v_frag(buf_v, 1, kh_prev, 1);
-    float ls[2] = {0.f, 0.f};
+    float ls[2];
     const float m[2] = {m_run[0], m_run[1]};
     f32x16 z;
 #pragma unroll
@@ -312,8 +316,6 @@ __global__ __launch_bounds__(kAttThreads, 2) void attn_bf16_kernel(AttnArgs a) {
 #pragma unroll
           for (int r = 0; r < 16; ++r) O[qb2][db][r] *= alpha;
       }
-      ls[0] = 0.f;
-      ls[1] = 0.f;
 #pragma unroll
       for (int qb2 = 0; qb2 < 2; ++qb2)
 #pragma unroll

@@ -224,29 +224,45 @@ __global__ __launch_bounds__(kConvThreads, 1) void conv3x3_bf16_mfma_kernel(Conv
   const int a_row0 = wn * kConvCW + pl;
   const int a_slot[2] = {(0 + kg) ^ (pl & 7), (4 + kg) ^ (pl & 7)};
 
-  // The three taps of kernel row dy on the staged weights of buffer wb.
+  // The three taps of kernel row dy on the staged weights of buffer wb: six
+  // batches n = (dx, 32-wide k step ks), each two A and TG B fragments and
+  // 2 TG MFMAs.  The fragments of batch n+1 are read from LDS before the
+  // MFMAs of batch n issue; the scheduling groups keep the compiler from
+  // sinking those reads next to their use.
+  auto frag_load = [&](int dy, int wb, int n, bf16x8 (&af)[kConvCG], bf16x8 (&bfr)[TG]) {
+    const int dx = n >> 1, ks = n & 1;
+    // B fragment rows bp = (wr + dy) * BW + dx + 16 j + pl: all fragments of
+    // a tap share (bp & 7), so one swizzled slot per k step serves all j
+    const int bp0 = (wr + dy) * BW + dx + pl;
+    const int bslot = (ks * 4 + kg) ^ (bp0 & 7);
+#pragma unroll
+    for (int i = 0; i < kConvCG; ++i)
+      af[i] = __builtin_bit_cast(bf16x8, wts[wb][dx][(a_row0 + 16 * i) * 8 + a_slot[ks]]);
+#pragma unroll
+    for (int j = 0; j < TG; ++j) bfr[j] = __builtin_bit_cast(bf16x8, band[(bp0 + 16 * j) * 8 + bslot]);
+  };
+  auto mfma_batch = [&](const bf16x8 (&af)[kConvCG], const bf16x8 (&bfr)[TG]) {
+#pragma unroll
+    for (int i = 0; i < kConvCG; ++i)
+#pragma unroll
+      for (int j = 0; j < TG; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+  };
+  constexpr int kSgDsRead = 0x100, kSgMfma = 0x008;  // sched_group_barrier masks
   auto compute = [&](int dy, int wb) {
+    bf16x8 a0[kConvCG], b0[TG], a1[kConvCG], b1[TG];
+    frag_load(dy, wb, 0, a0, b0);
+    __builtin_amdgcn_sched_group_barrier(kSgDsRead, kConvCG + TG, 0);
 #pragma unroll
-    for (int dx = 0; dx < 3; ++dx) {
-      // B fragment rows bp = (wr + dy) * BW + dx + 16 j + pl: all fragments
-      // of a tap share (bp & 7), so one swizzled slot per k step serves all j
-      const int bp0 = (wr + dy) * BW + dx + pl;
-      const int b_x = bp0 & 7;
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        bf16x8 af[kConvCG], bfr[TG];
-        const int bslot = (ks * 4 + kg) ^ b_x;
-#pragma unroll
-        for (int i = 0; i < kConvCG; ++i)
-          af[i] = __builtin_bit_cast(bf16x8, wts[wb][dx][(a_row0 + 16 * i) * 8 + a_slot[ks]]);
-#pragma unroll
-        for (int j = 0; j < TG; ++j) bfr[j] = __builtin_bit_cast(bf16x8, band[(bp0 + 16 * j) * 8 + bslot]);
-#pragma unroll
-        for (int i = 0; i < kConvCG; ++i)
-#pragma unroll
-          for (int j = 0; j < TG; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
-      }
+    for (int n = 0; n < 6; n += 2) {
+      frag_load(dy, wb, n + 1, a1, b1);
+      mfma_batch(a0, b0);
+      __builtin_amdgcn_sched_group_barrier(kSgDsRead, kConvCG + TG, 0);
+      __builtin_amdgcn_sched_group_barrier(kSgMfma, kConvCG * TG, 0);
+      if (n + 2 < 6) frag_load(dy, wb, n + 2, a0, b0);
+      mfma_batch(a1, b1);
+      if (n + 2 < 6) __builtin_amdgcn_sched_group_barrier(kSgDsRead, kConvCG + TG, 0);
+      __builtin_amdgcn_sched_group_barrier(kSgMfma, kConvCG * TG, 0);
     }
   };
   // Step st = 3 slice + dy (st & 1 == P): compute on weight buffer P, stage
