@@ -26,6 +26,28 @@ import torch
 from . import _lib as L
 
 
+def capture_graph(fn, warmup: int = 1):
+    """Record the kernel launches of `fn` -- a sequence of libdpp calls, which
+    launch on the current stream and allocate, copy and synchronise nothing --
+    into a HIP graph (torch.cuda.CUDAGraph) and return it; `graph.replay()`
+    then issues the whole sequence with one launch from the host.  `fn` runs
+    `warmup` times eagerly on a side stream first.  The graph keeps the
+    device pointers it was captured with: replays read and write the same
+    buffers, so the caller refills the input buffers in place between
+    replays.  Every libdpp kernel writes its outputs in full (no memset
+    nodes), so each replay recomputes them from the inputs."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for _ in range(warmup):
+            fn()
+    torch.cuda.current_stream().wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        fn()
+    return graph
+
+
 class DisplacedLayer:
     def __init__(self, B, H, W, C, P, G, heads, dtype, device="cuda", eps=1e-5, head_dim=64):
         if H % P:
