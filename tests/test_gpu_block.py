@@ -9,7 +9,7 @@ With projection weights N(0,1)/sqrt(C) the scores have a spread of about 2
 (not one key per query), so the softmax mixing is exercised.  Every stage is
 compared with the oracle's value computed from the previous stage's stored
 values; the 1024 px workload in full, the 3840 px workload on full
-GroupNorm/conv/projection outputs and 64 sampled attention/out rows per
+GroupNorm/conv/projection outputs and 256 sampled attention/out rows per
 patch.  Each test prints the case it runs before touching the GPU."""
 import numpy as np
 import pytest
@@ -121,4 +121,4 @@ def test_attention_block_parity_cfg_pair():
 
 def test_attention_block_parity_3840_sampled():
     cfg = CONFIGS["sdxl_3840"]
-    _block_case(cfg, (0, cfg.P - 1), n_sample=64)
+    _block_case(cfg, (0, cfg.P - 1), n_sample=256)

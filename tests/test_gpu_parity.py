@@ -546,15 +546,22 @@ def test_attention_closed_form_zero_query():
     parity(to_host(o), want, "bf16", "attn zero query")
 
 
-@pytest.mark.parametrize("name", ["sdxl_2048", "sdxl_3840"])
-def test_attention_parity_full_size_sampled(name):
-    cfg = CONFIGS[name]
-    rng = np.random.default_rng(12)
-    n = 64
-    qi = np.concatenate([[0, cfg.Nq - 1, cfg.W - 1, cfg.Nq // 2], rng.integers(0, cfg.Nq, n - 4)])
-    bi = np.zeros(n, dtype=np.int64)
+@pytest.mark.parametrize("p", [0, 7])
+def test_attention_parity_2048_full_patch(p):
+    # every query of a 2048 px patch (2048 queries x 16384 keys x 10 heads, six
+    # key splits) against the oracle: a few seconds of float64 BLAS
+    say("attention full", "sdxl_2048", "patch", p)
+    _attn_case(CONFIGS["sdxl_2048"], p)
+
+
+def test_attention_parity_full_size_sampled():
+    # 3840 px: 517 queries per patch, one in 14 plus both ends and the start
+    # of the last (partial) 256-query tile, on the first and last patch
+    cfg = CONFIGS["sdxl_3840"]
+    qi = np.unique(np.concatenate([np.arange(0, cfg.Nq, 14), [cfg.Nq - 1, cfg.W - 1, (cfg.Nq // 256) * 256]]))
+    bi = np.zeros(len(qi), dtype=np.int64)
     for p in (0, cfg.P - 1):
-        say("attention sampled", name, "patch", p)
+        say("attention sampled", cfg.name, "patch", p, "queries", len(qi))
         _attn_case(cfg, p, sample_rows=(bi, qi))
 
 
@@ -745,9 +752,9 @@ def test_block_parity_full_size_sampled():
     # The 3840 px step exactly as the benchmark runs it (DisplacedLayer with
     # its GroupNorm, conv and attention workspaces): previous-step state,
     # then patches 0 and 7.  GN, conv and the spliced K/V compared in full,
-    # the attention on 64 sampled queries per patch.
+    # the attention on 256 sampled queries per patch.
     cfg = CONFIGS["sdxl_3840"]
     rng = np.random.default_rng(13)
-    n = 64
+    n = 256
     qi = np.concatenate([[0, cfg.Nq - 1, cfg.W - 1, cfg.Nq // 2], rng.integers(0, cfg.Nq, n - 4)])
     _block_case(cfg, (0, cfg.P - 1), sample_rows=(np.zeros(n, dtype=np.int64), qi))
