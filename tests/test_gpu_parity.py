@@ -471,6 +471,36 @@ def test_attention_many_key_splits():
         parity(to_host(o), want, "bf16", f"attn {nsplit} splits {B},{nq},{nkv}")
 
 
+@pytest.mark.parametrize("vscale", [3.0e5, 1.0e-6, 0.0], ids=["above_fp16_range", "tiny", "zero"])
+def test_attention_split_partials_any_magnitude(vscale):
+    # The split path at magnitudes of V far from 1 (3e5, 1e-6) and with an
+    # all-zero V: the float32 partials and the merge keep the results at the
+    # bar, and zero stays exactly zero.
+    dpp = _dpp()
+    rng = np.random.default_rng(11)
+    from dpp_synth import f32_to_bf16_bits
+    B, nq, nkv, heads = 1, 64, 8192, 2
+    hd = heads * 64
+    say("attention split partials, V scale", vscale)
+    q = f32_to_bf16_bits(rng.standard_normal((B, nq, hd)).astype(np.float32))
+    k = f32_to_bf16_bits(rng.standard_normal((B, nkv, hd)).astype(np.float32))
+    v = f32_to_bf16_bits((vscale * rng.standard_normal((B, nkv, hd))).astype(np.float32))
+    wsb = dpp.dpp_self_attn_workspace_bytes(B, nq, nkv, heads, 64, 0)
+    assert wsb > 0
+    ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+    obase, o = guarded_empty((B, nq, hd), torch.bfloat16)
+    dpp.dpp_self_attn_displaced(o, to_dev(q, "bf16"), to_dev(k, "bf16"), to_dev(v, "bf16"), heads, 64, 0.0, ws)
+    torch.cuda.synchronize()
+    check_guards(obase, f"attn split partials V x {vscale}")
+    got = to_host(o)
+    assert np.all(np.isfinite(got))
+    if vscale == 0.0:
+        assert not np.any(got), "all-zero V must give exactly zero"
+        return
+    want = oracle.self_attn_displaced(values("bf16", q), values("bf16", k), values("bf16", v), heads)
+    parity(got, want, "bf16", f"attn split partials V x {vscale}")
+
+
 @pytest.mark.parametrize("split", [False, True])
 def test_attention_growing_scores_rescale_often(split):
     # Scores that grow along the key range (keys drift along a direction the
