@@ -366,6 +366,7 @@ def test_producer_statistics_and_presummed_validation():
     assert L.dpp_conv3x3_halo_gn_chunks(30, 240, 640) == 225          # 15 row pairs x 3 column tiles x 5 channel tiles
     assert L.dpp_linear_gn_chunks(1, 7200, 640) == 225                 # 45 token tiles x 5 channel tiles
     assert L.dpp_linear_gn_chunks(1, 7200, 1280) == 225                # 256-channel tiles: 45 x 5
+    assert L.dpp_linear_gn_chunks(1, 1024, 640) == 65                  # few tiles: 80-token tiles, 13 x 5
     assert L.dpp_conv3x3_halo_gn_chunks(0, 240, 640) == 0
 
     def cgn(y=A, part=WSP, G=32, x=Bp, st=Cp, w=Dp, bias=Ep, B=1, H=8, W=16, Cin=64, Cout=64, row0=2, rows=2,

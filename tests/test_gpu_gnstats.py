@@ -121,10 +121,12 @@ def test_linear_gn_partials(B, M, K, N, G):
     check_guards(ybase, "linear gn y")
     check_guards(pbase, "linear gn partials")
     np.testing.assert_array_equal(bits(y), bits(y_ref))
-    # chunks are (channel tile) * token tiles + token tile; the channel tile
-    # is 128 or 256 wide (the call's choice): check the sums, and that no
-    # chunk writes a group outside either width's reach
-    ptiles = -(-M // 160)
+    # chunks are (channel tile) * token tiles + token tile; the token tile is
+    # 160 tokens, or 80 when the 160-token grid has at most 128 tiles, and
+    # the channel tile 128 or 256 wide (the call's choice): check the sums,
+    # and that no chunk writes a group outside either width's reach
+    bm = 80 if -(-M // 160) * B * -(-N // 128) <= 128 else 160
+    ptiles = -(-M // bm)
     ctiles = nchunk // ptiles
     assert ctiles * ptiles == nchunk
     bn = 128 if -(-N // 128) == ctiles else 256
