@@ -1,10 +1,11 @@
 """A displaced layer step captured into a HIP graph (step.capture_graph) and
 replayed must write exactly what the eager calls write: the same kernels on
 the same inputs, bit for bit.  The step is every patch's GroupNorm -> conv ->
-splice -> attention of the 1024 px workload plus the CFG combine, as the
-benchmark runs it.  Between replays the test overwrites every output buffer
-from the host side (eager fills, synchronised), so a replay that skipped a
-kernel or left a node stale would show up; three replays are checked."""
+splice -> attention of the 1024 px and 3840 px workloads plus the CFG
+combine, as the benchmark runs it.  Between replays the test overwrites
+every output buffer from the host side (eager fills, synchronised), so a
+replay that skipped a kernel or left a node stale would show up; three
+replays are checked."""
 import numpy as np
 import pytest
 
@@ -27,10 +28,11 @@ def say(*a):
     print("[case]", *a, flush=True)
 
 
-def test_graph_replay_matches_eager_step(gpu):
+@pytest.mark.parametrize("name", ["sdxl_1024", "sdxl_3840"])
+def test_graph_replay_matches_eager_step(gpu, name):
     dpp = gpu
     from displaced_patch_parallelism_net_amd.step import DisplacedLayer, capture_graph
-    cfg = CONFIGS["sdxl_1024"]
+    cfg = CONFIGS[name]
     say("graph replay of the", cfg.name, "step: eager reference")
     li = layer_inputs(cfg)
     n_lat = 2 * cfg.H * 2 * cfg.W * 4
