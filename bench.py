@@ -239,6 +239,7 @@ def run(args):
     torch.cuda.synchronize()
 
     attn_events = []
+    conv_events = []
     patch_events = []
 
     def step(record=False):
@@ -249,7 +250,13 @@ def run(args):
                 p0.record()
             dpp.dpp_groupnorm_stale(layer.y1, layer.stats_next, x_patches[p], layer.stats_prev, gamma, beta, cfg.H,
                                     cfg.G, cfg.P, p, cfg.gn_eps, layer.gn_ws)
+            if record:
+                c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                c0.record()
             dpp.dpp_conv3x3_halo(layer.y2, layer.y1, layer.a1, w, b, cfg.H, r0, workspace=layer.conv_ws)
+            if record:
+                c1.record()
+                conv_events.append((c0, c1))
             dpp.dpp_splice_patch(layer.kv[p], layer.y2, r0)
             kv = layer.kv[p].view(cfg.B, cfg.N, cfg.C)
             if record:
@@ -290,6 +297,8 @@ def run(args):
                                                   layer.kv[p].view(cfg.B, cfg.N, cfg.C), cfg.heads, cfg.D, 0.0,
                                                   layer.attn_ws) for p in range(cfg.P)], torch)
     attn_tflops = f_attn / (attn_ms * 1e-3) / 1e12
+    conv_ms = float(np.mean([a.elapsed_time(b_) for a, b_ in conv_events]))
+    conv_tflops = f_conv / (conv_ms * 1e-3) / 1e12
 
     graph = time_graph_step(step, step_flops, torch, args.steps)
 
@@ -349,6 +358,11 @@ def run(args):
             "flops_per_launch": f_attn,
         },
     }
+    out["roofline_conv"] = {
+        "kernel": "dpp_conv3x3_halo", "bound": "mfma", "achieved": round(conv_tflops, 2), "peak": PEAK_BF16_TFLOPS,
+        "unit": "TFLOP/s", "frac": round(conv_tflops / PEAK_BF16_TFLOPS, 4), "avg_launch_ms": round(conv_ms, 5),
+        "flops_per_launch": f_conv,
+        "timing": "HIP events on the launch stream around each conv call inside the timed steps"}
     out["graph_replay"] = graph
     if block:
         out["attention_block_step"] = block
