@@ -8,17 +8,19 @@
 //
 // bf16 path: implicit GEMM on MFMA.  M = output channels (A = weights,
 // [Cout][tap][Cin] rows are K-contiguous), N = output pixels (B = input
-// pixels, channel-contiguous in NHWC), K = 9 taps x Cin.  A workgroup owns 2
-// patch rows x 16*TG columns x 128 output channels (TG chosen per width so
+// pixels, channel-contiguous in NHWC), K = 9 taps x Cin.  A workgroup owns 4
+// patch rows x 16*TG columns x 64 output channels (TG chosen per width so
 // the tiles cover the rows exactly where possible: 240 columns -> 3 tiles of
-// 80, one workgroup per CU).  For each 64-channel slice of Cin the halo band
-// (4 rows x 16*TG+2 columns, halo rows from the stale image) is staged once in
-// LDS and reused by all nine taps; one barrier step covers the three taps of
-// one kernel row, whose weights are double-buffered in LDS and fetched two
-// steps ahead into registers.  Eight waves (two per SIMD) each compute 32 channels x 16*TG
-// pixels of one tile row with v_mfma_f32_16x16x32_bf16; the accumulator's
-// lane layout gives each lane four consecutive output channels of one pixel,
-// stored as one 8-byte write.
+// 80; the 30-row band of a 240 x 240 image in 8 patches -> 240 workgroups,
+// one per CU).  For each 64-channel slice of Cin the halo band (6 rows x
+// 16*TG+2 columns, halo rows from the stale image) is staged once in LDS and
+// reused by all nine taps; one barrier step covers the three taps of one
+// kernel row, whose weights are double-buffered in LDS and fetched two steps
+// ahead into registers.  Eight waves (two per SIMD) each compute 32 channels
+// x 16*TG pixels of one tile row with v_mfma_f32_16x16x32_bf16; the
+// accumulator's lane layout gives each lane four consecutive output channels
+// of one pixel.  The kernel also has the 2-row x 128-channel tile it had
+// first (same arithmetic, same bits; more weight bytes per step).
 //
 // f32 path: one thread per output element, direct loops (small shapes).
 #include "dpp_common.h"
@@ -59,33 +61,49 @@ __global__ __launch_bounds__(256) void conv3x3_f32_kernel(float* __restrict__ y,
 }
 
 // ------------------------------------------------------------------ bf16 MFMA implicit GEMM
-// Workgroup tile: 2 patch rows x 16*TG columns of output pixels x 128 output
-// channels; 2 x kConvWN waves, wave (wr, wn) owns tile row wr and channels
-// [CW wn, CW wn + CW): TG x CW/16 accumulator tiles of 16 x 16.  The host picks TG
-// (1..5) so that the tiles cover the row width with the least waste and the
-// workgroup count fills the 256 CUs in whole rounds (e.g. 240 columns ->
-// TG 5: three tiles per row pair).
+// Workgroup tile: TR patch rows x 16*TG columns of output pixels x BM = 256/TR
+// output channels (TR = 2: 128 channels; TR = 4: 64 channels).  Eight waves;
+// wave (wr, wn) owns tile row wr and channels [32 wn, 32 wn + 32): TG x 2
+// accumulator tiles of 16 x 16.  The host picks TG (1..5) so that the tiles
+// cover the row width with the least waste (e.g. 240 columns -> TG 5: three
+// tiles per row) and TR per shape.
 //
 // K loop: step = (64-channel slice, kernel row dy), three taps (dx = 0..2)
-// each, one barrier per step.  The weights of a step (3 x 128 x 64) are
+// each, one barrier per step.  The weights of a step (3 x BM x 64) are
 // double-buffered in LDS and fetched into registers two steps ahead.  The
-// (2+2) x (16 TG + 2) halo band of a slice has one LDS buffer: step dy reads
-// band rows dy and dy+1 only, so rows 0-1 of the next slice's band are
-// written during its dy = 2 step (they were last read at dy = 1) and rows 2-3
-// during the next slice's dy = 0 step; each half is fetched into registers
-// two steps before it is written.  Every global load is unconditional (weight
-// rows past Cout read zero through the buffer resource's range check; band
-// vectors in the zero padding load a valid address and are zeroed when
-// staged), and a pair of slices is one straight-line loop body, so each wait
-// before a staging store covers only the loads it needs.
-constexpr int kConvWN = 4;                      // waves across the 128 output channels
-constexpr int kConvCW = 128 / kConvWN;          // output channels per wave
-constexpr int kConvCG = kConvCW / 16;           // 16-channel MFMA groups per wave
-constexpr int kConvThreads = 2 * kConvWN * 64;  // 2 tile rows x kConvWN
-constexpr int kConvBM = 128;  // output channels per workgroup
-constexpr int kConvKC = 64;   // input channels per slice (8 x 16-byte vectors)
-constexpr int kConvTR = 2;    // patch rows per workgroup
+// (TR+2) x (16 TG + 2) halo band of a slice is staged once and read by all
+// nine taps, in two-row pieces, each fetched into registers two steps before
+// it is written:
+//  * TR = 2: one four-row buffer.  Step dy reads band rows dy and dy+1 only,
+//    so rows 0-1 of the next slice's band are written during its dy = 2 step
+//    (they were last read at dy = 1) and rows 2-3 during the next slice's
+//    dy = 0 step.
+//  * TR = 4: a ring of eight rows; slice s's band row i sits in ring row
+//    (6s + i) mod 8.  Step dy reads rows dy .. dy+3.  Rows 4-5 of slice s are
+//    written during its dy = 0 step (into the ring rows of slice s-1's rows
+//    2-3), rows 0-1 of slice s+1 during dy = 1 (ring rows slice s does not
+//    use), rows 2-3 of slice s+1 during dy = 2 (slice s's rows 0-1, last read
+//    at dy = 1).  Each step writes two rows, and the 64-channel tile halves
+//    the weight bytes per step.
+// Every global load is unconditional (weight rows past Cout read zero
+// through the buffer resource's range check; band vectors in the zero
+// padding load a valid address and are zeroed when staged), and a pair of
+// slices is one straight-line loop body, so each wait before a staging store
+// covers only the loads it needs.
+constexpr int kConvCW = 32;                // output channels per wave
+constexpr int kConvCG = kConvCW / 16;      // 16-channel MFMA groups per wave
+constexpr int kConvThreads = 512;          // 8 waves
+constexpr int kConvKC = 64;                // input channels per slice (8 x 16-byte vectors)
 constexpr int kConvBufWord3 = 0x00020000;  // raw 32-bit buffer access, no swizzle
+
+template <int TR>
+struct ConvTile {
+  static_assert(TR == 2 || TR == 4, "two or four patch rows per workgroup");
+  static constexpr int BM = 256 / TR;             // output channels per workgroup
+  static constexpr int WN = BM / kConvCW;         // waves across the channels
+  static constexpr int RING = TR == 2 ? 4 : 8;    // band rows held in LDS
+  static constexpr int NPIECE = (TR + 2) / 2;     // two-row pieces of a slice's band
+};
 
 struct ConvArgs {
   const uint16_t* x;
@@ -95,7 +113,7 @@ struct ConvArgs {
   uint16_t* y;
   float* part;  // split-K: float32 partial outputs [nsplit][B][rows][W][Cout], else NULL
   int H, W, Cin, Cout, row0, rows;
-  int tiles_c;  // column tiles per row pair
+  int tiles_c;  // column tiles per row band
   int nsplit;   // input-channel splits (blockIdx.z = b * nsplit + split)
   int spl;      // 64-channel slices per split
   float* gn_part;  // GroupNorm partial sums of y [B][gridDim.x * gridDim.y][G][2], or NULL (unsplit only)
@@ -107,57 +125,63 @@ struct ConvArgs {
 // the banks.
 __device__ __forceinline__ int swz(int row, int slot) { return row * 8 + (slot ^ (row & 7)); }
 
-template <int TG>
+template <int TG, int TR>
 __global__ __launch_bounds__(kConvThreads, 1) void conv3x3_bf16_mfma_kernel(ConvArgs a) {
+  constexpr int BM = ConvTile<TR>::BM, WN = ConvTile<TR>::WN, RING = ConvTile<TR>::RING;
+  constexpr int NPIECE = ConvTile<TR>::NPIECE;
   constexpr int TC = 16 * TG;              // output columns per tile
   constexpr int BW = TC + 2;               // band columns
-  constexpr int HALF_VEC = 2 * BW * 8;     // 16-byte vectors in two band rows
-  constexpr int HB_ITERS = (HALF_VEC + kConvThreads - 1) / kConvThreads;
-  constexpr int W_ITERS = kConvBM * 8 / kConvThreads;
+  constexpr int PIECE_VEC = 2 * BW * 8;    // 16-byte vectors in two band rows
+  constexpr int HB_ITERS = (PIECE_VEC + kConvThreads - 1) / kConvThreads;
+  constexpr int W_ITERS = BM * 8 / kConvThreads;
+  constexpr int BAND_VEC = RING * BW * 8;
+  static_assert(NPIECE * HB_ITERS <= 32, "staging mask bits");
 
-  // band: 4 rows x BW pixels x 8 slots, plus one dummy slot that absorbs the
-  // stores of the threads past the last vector of a half
-  __shared__ uint4 band[2 * HALF_VEC + 1];
-  __shared__ uint4 wts[2][3][kConvBM * 8];
+  // band: RING rows x BW pixels x 8 slots, plus one dummy slot that absorbs
+  // the stores of the threads past the last vector of a piece
+  __shared__ uint4 band[BAND_VEC + 1];
+  __shared__ uint4 wts[2][3][BM * 8];
 
   const int tid = threadIdx.x;
   const int wave = tid / kWave, lane = tid % kWave;
-  const int wr = wave / kConvWN, wn = wave % kConvWN;
+  const int wr = wave / WN, wn = wave % WN;
   const int b = blockIdx.z / a.nsplit, split = blockIdx.z % a.nsplit;
-  const int m0 = blockIdx.y * kConvBM;
+  const int m0 = blockIdx.y * BM;
   const int tile_r = blockIdx.x / a.tiles_c, tile_c = blockIdx.x % a.tiles_c;
-  const int pr0 = tile_r * kConvTR, pc0 = tile_c * TC;  // patch-relative origin of the pixel tile
+  const int pr0 = tile_r * TR, pc0 = tile_c * TC;  // patch-relative origin of the pixel tile
   const int H = a.H, W = a.W, Cin = a.Cin;
   // this workgroup's input-channel slices: [s0, s0 + nslices)
   const int s0 = split * a.spl;
   const int nslices = min(a.spl, Cin / kConvKC - s0);
   const int nsteps = nslices * 3;
 
-  // Band staging map, fixed for the kernel: vector u of half hf (rows 2hf,
-  // 2hf+1) -> source address of the first slice (x for patch rows, the stale
-  // image for halo rows; zero padding loads x and is masked) and LDS slot.
-  const uint16_t* band_src[2][HB_ITERS];
-  int band_dst[2][HB_ITERS];
-  uint32_t band_ok = 0;  // bit hf*HB_ITERS+u: the vector is inside the image
+  // Band staging map, fixed for the kernel: vector u of piece pc (band rows
+  // 2pc, 2pc+1) -> source address of the first slice (x for patch rows, the
+  // stale image for halo rows; zero padding loads x and is masked) and its
+  // place: TR = 2 the LDS slot; TR = 4 (band row << 12 | column << 3 | slot),
+  // placed in the ring when stored; -1 past the last vector.
+  const uint16_t* band_src[NPIECE][HB_ITERS];
+  int band_pos[NPIECE][HB_ITERS];
+  uint32_t band_ok = 0;  // bit pc*HB_ITERS+u: the vector is inside the image
 #pragma unroll
-  for (int hf = 0; hf < 2; ++hf)
+  for (int pc = 0; pc < NPIECE; ++pc)
 #pragma unroll
     for (int u = 0; u < HB_ITERS; ++u) {
       const int id = tid + u * kConvThreads;
-      const int pix = hf * 2 * BW + (id >> 3), slot = id & 7;
-      const int br = pix / BW, bc = pix % BW;
+      const int lp = id >> 3, slot = id & 7;
+      const int br = 2 * pc + lp / BW, bc = lp % BW;
       const int r = pr0 - 1 + br;  // patch-relative
       const int ir = a.row0 + r;   // image row
       const int col = pc0 - 1 + bc;
-      band_src[hf][u] = a.x + slot * 8;
-      band_dst[hf][u] = 2 * HALF_VEC;
-      if (id < HALF_VEC) {
-        band_dst[hf][u] = swz(pix, slot);
+      band_src[pc][u] = a.x + slot * 8;
+      band_pos[pc][u] = TR == 2 ? BAND_VEC : -1;
+      if (id < PIECE_VEC) {
+        band_pos[pc][u] = TR == 2 ? swz(br * BW + bc, slot) : (br << 12) | (bc << 3) | slot;
         if (ir >= 0 && ir < H && col >= 0 && col < W) {
-          band_src[hf][u] = ((r >= 0 && r < a.rows) ? a.x + ((static_cast<int64_t>(b) * a.rows + r) * W + col) * Cin
+          band_src[pc][u] = ((r >= 0 && r < a.rows) ? a.x + ((static_cast<int64_t>(b) * a.rows + r) * W + col) * Cin
                                                     : a.stale + ((static_cast<int64_t>(b) * H + ir) * W + col) * Cin) +
                             slot * 8;
-          band_ok |= 1u << (hf * HB_ITERS + u);
+          band_ok |= 1u << (pc * HB_ITERS + u);
         }
       }
     }
@@ -172,22 +196,29 @@ __global__ __launch_bounds__(kConvThreads, 1) void conv3x3_bf16_mfma_kernel(Conv
     w_off[u] = ((m0 + (id >> 3)) * 9 * Cin + (id & 7) * 8) * 2;
   }
 
-  uint4 band_lo[HB_ITERS], band_hi[HB_ITERS];
+  uint4 band_ra[HB_ITERS], band_rb[HB_ITERS];  // two band pieces in flight
   uint4 w_regA[3][W_ITERS], w_regB[3][W_ITERS];  // weights of the next two steps
   // Loads never touch their results until the staging store.
-  auto load_half = [&](uint4 (&reg)[HB_ITERS], int hf, int slice) {
+  auto load_piece = [&](uint4 (&reg)[HB_ITERS], int pc, int slice) {
     const int c0 = (s0 + min(slice, nslices - 1)) * kConvKC;
 #pragma unroll
-    for (int u = 0; u < HB_ITERS; ++u) reg[u] = *reinterpret_cast<const uint4*>(band_src[hf][u] + c0);
+    for (int u = 0; u < HB_ITERS; ++u) reg[u] = *reinterpret_cast<const uint4*>(band_src[pc][u] + c0);
   };
-  auto store_half = [&](uint4 (&reg)[HB_ITERS], int hf) {
+  // piece pc into the band; TR = 4: ring row (base + band row) mod 8
+  auto store_piece = [&](uint4 (&reg)[HB_ITERS], int pc, int base) {
 #pragma unroll
     for (int u = 0; u < HB_ITERS; ++u) {
-      const uint32_t keep = 0u - ((band_ok >> (hf * HB_ITERS + u)) & 1u);
+      const uint32_t keep = 0u - ((band_ok >> (pc * HB_ITERS + u)) & 1u);
       // pins the mask here: hoisted next to the load, it would make the
       // wave wait for the load there
       asm volatile("" : "+v"(reg[u].x), "+v"(reg[u].y), "+v"(reg[u].z), "+v"(reg[u].w));
-      band[band_dst[hf][u]] = make_uint4(reg[u].x & keep, reg[u].y & keep, reg[u].z & keep, reg[u].w & keep);
+      int dst = band_pos[pc][u];
+      if constexpr (TR != 2) {
+        const int pos = dst;
+        const int prow = ((base + (pos >> 12)) & (RING - 1)) * BW + ((pos >> 3) & 511);
+        dst = pos < 0 ? BAND_VEC : swz(prow, pos & 7);
+      }
+      band[dst] = make_uint4(reg[u].x & keep, reg[u].y & keep, reg[u].z & keep, reg[u].w & keep);
     }
   };
   auto load_w = [&](uint4 (&reg)[3][W_ITERS], int step) {
@@ -229,11 +260,13 @@ __global__ __launch_bounds__(kConvThreads, 1) void conv3x3_bf16_mfma_kernel(Conv
   // 2 TG MFMAs.  The fragments of batch n+1 are read from LDS before the
   // MFMAs of batch n issue; the scheduling groups keep the compiler from
   // sinking those reads next to their use.
-  auto frag_load = [&](int dy, int wb, int n, bf16x8 (&af)[kConvCG], bf16x8 (&bfr)[TG]) {
+  auto frag_load = [&](int dy, int wb, int base, int n, bf16x8 (&af)[kConvCG], bf16x8 (&bfr)[TG]) {
     const int dx = n >> 1, ks = n & 1;
-    // B fragment rows bp = (wr + dy) * BW + dx + 16 j + pl: all fragments of
-    // a tap share (bp & 7), so one swizzled slot per k step serves all j
-    const int bp0 = (wr + dy) * BW + dx + pl;
+    // B fragment rows bp = (band row of wr + dy) * BW + dx + 16 j + pl: all
+    // fragments of a tap share (bp & 7), so one swizzled slot per k step
+    // serves all j
+    const int brow = TR == 2 ? wr + dy : (base + wr + dy) & (RING - 1);
+    const int bp0 = brow * BW + dx + pl;
     const int bslot = (ks * 4 + kg) ^ (bp0 & 7);
 #pragma unroll
     for (int i = 0; i < kConvCG; ++i)
@@ -249,57 +282,99 @@ __global__ __launch_bounds__(kConvThreads, 1) void conv3x3_bf16_mfma_kernel(Conv
         acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
   };
   constexpr int kSgDsRead = 0x100, kSgMfma = 0x008;  // sched_group_barrier masks
-  auto compute = [&](int dy, int wb) {
+  auto compute = [&](int dy, int wb, int base) {
     bf16x8 a0[kConvCG], b0[TG], a1[kConvCG], b1[TG];
-    frag_load(dy, wb, 0, a0, b0);
+    frag_load(dy, wb, base, 0, a0, b0);
     __builtin_amdgcn_sched_group_barrier(kSgDsRead, kConvCG + TG, 0);
 #pragma unroll
     for (int n = 0; n < 6; n += 2) {
-      frag_load(dy, wb, n + 1, a1, b1);
+      frag_load(dy, wb, base, n + 1, a1, b1);
       mfma_batch(a0, b0);
       __builtin_amdgcn_sched_group_barrier(kSgDsRead, kConvCG + TG, 0);
       __builtin_amdgcn_sched_group_barrier(kSgMfma, kConvCG * TG, 0);
-      if (n + 2 < 6) frag_load(dy, wb, n + 2, a0, b0);
+      if (n + 2 < 6) frag_load(dy, wb, base, n + 2, a0, b0);
       mfma_batch(a1, b1);
       if (n + 2 < 6) __builtin_amdgcn_sched_group_barrier(kSgDsRead, kConvCG + TG, 0);
       __builtin_amdgcn_sched_group_barrier(kSgMfma, kConvCG * TG, 0);
     }
   };
-  // Step st = 3 slice + dy (st & 1 == P): compute on weight buffer P, stage
+  // Step st = 3 slice + dy (st & 1 == p): compute on weight buffer p, stage
   // the weights of st+1 (held in wnext) into the other buffer, barrier, fetch
-  // the weights of st+3 into wnext.  Around it, the band halves of the next
-  // slice: loads at dy = 0 (rows 0-1) and dy = 1 (rows 2-3); rows 0-1 are
-  // staged at dy = 2, rows 2-3 at the next slice's dy = 0.
-  auto slice_steps = [&](int slice, uint4 (&w0)[3][W_ITERS], uint4 (&w1)[3][W_ITERS], int p) {
+  // the weights of st+3 into wnext.  Around it, the band pieces.
+  //  TR = 2 (lo, hi = rows 0-1, 2-3): loads of the next slice at dy = 0 (lo)
+  //  and dy = 1 (hi); lo is staged at dy = 2, hi at the next slice's dy = 0.
+  //  TR = 4 (pieces A, B, C = rows 0-1, 2-3, 4-5; e and o hold the pieces
+  //  fetched at even and odd steps): dy = 0 stages C(s) and fetches B(s+1),
+  //  dy = 1 stages A(s+1) and fetches C(s+1), dy = 2 stages B(s+1) and
+  //  fetches A(s+2).
+  auto slice_steps = [&](int slice, uint4 (&w0)[3][W_ITERS], uint4 (&w1)[3][W_ITERS], int p,
+                         uint4 (&e)[HB_ITERS], uint4 (&o)[HB_ITERS]) {
     const int st = slice * 3;
-    // dy = 0
-    store_half(band_hi, 1);
-    load_half(band_lo, 0, slice + 1);
-    compute(0, p);
-    store_w(w0, p ^ 1);
-    __syncthreads();
-    load_w(w0, st + 3);
-    // dy = 1
-    load_half(band_hi, 1, slice + 1);
-    compute(1, p ^ 1);
-    store_w(w1, p);
-    __syncthreads();
-    load_w(w1, st + 4);
-    // dy = 2
-    compute(2, p);
-    store_half(band_lo, 0);
-    store_w(w0, p ^ 1);
-    __syncthreads();
-    load_w(w0, st + 5);
+    if constexpr (TR == 2) {
+      // e = lo, o = hi (fixed roles)
+      // dy = 0
+      store_piece(o, 1, 0);
+      load_piece(e, 0, slice + 1);
+      compute(0, p, 0);
+      store_w(w0, p ^ 1);
+      __syncthreads();
+      load_w(w0, st + 3);
+      // dy = 1
+      load_piece(o, 1, slice + 1);
+      compute(1, p ^ 1, 0);
+      store_w(w1, p);
+      __syncthreads();
+      load_w(w1, st + 4);
+      // dy = 2
+      compute(2, p, 0);
+      store_piece(e, 0, 0);
+      store_w(w0, p ^ 1);
+      __syncthreads();
+      load_w(w0, st + 5);
+    } else {
+      const int base = (6 * slice) & (RING - 1), nbase = (base + 6) & (RING - 1);
+      // dy = 0
+      store_piece(e, 2, base);
+      load_piece(e, 1, slice + 1);
+      compute(0, p, base);
+      store_w(w0, p ^ 1);
+      __syncthreads();
+      load_w(w0, st + 3);
+      // dy = 1
+      store_piece(o, 0, nbase);
+      load_piece(o, 2, slice + 1);
+      compute(1, p ^ 1, base);
+      store_w(w1, p);
+      __syncthreads();
+      load_w(w1, st + 4);
+      // dy = 2
+      store_piece(e, 1, nbase);
+      load_piece(e, 0, slice + 2);
+      compute(2, p, base);
+      store_w(w0, p ^ 1);
+      __syncthreads();
+      load_w(w0, st + 5);
+    }
   };
 
-  // prologue: band rows 0-1 and the weights of step 0 staged; rows 2-3 in
-  // registers (staged at the first step); steps 1 and 2 in registers
-  load_half(band_lo, 0, 0);
-  load_half(band_hi, 1, 0);
-  load_w(w_regB, 0);
-  store_half(band_lo, 0);
-  store_w(w_regB, 0);
+  // prologue: the band rows needed by the first step and the weights of step
+  // 0 staged; the next pieces and the weights of steps 1 and 2 in registers
+  if constexpr (TR == 2) {
+    load_piece(band_ra, 0, 0);
+    load_piece(band_rb, 1, 0);
+    load_w(w_regB, 0);
+    store_piece(band_ra, 0, 0);
+    store_w(w_regB, 0);
+  } else {
+    load_piece(band_ra, 0, 0);
+    load_piece(band_rb, 1, 0);
+    load_w(w_regB, 0);
+    store_piece(band_ra, 0, 0);
+    store_piece(band_rb, 1, 0);
+    store_w(w_regB, 0);
+    load_piece(band_ra, 2, 0);  // C(0), staged at step 0
+    load_piece(band_rb, 0, 1);  // A(1), staged at step 1
+  }
   load_w(w_regA, 1);
   load_w(w_regB, 2);
   __syncthreads();
@@ -307,10 +382,13 @@ __global__ __launch_bounds__(kConvThreads, 1) void conv3x3_bf16_mfma_kernel(Conv
   // of its steps st+1, st+3 in A; st+2 in B), the second at an odd one
   int slice = 0;
   for (; slice + 1 < nslices; slice += 2) {
-    slice_steps(slice, w_regA, w_regB, 0);
-    slice_steps(slice + 1, w_regB, w_regA, 1);
+    slice_steps(slice, w_regA, w_regB, 0, band_ra, band_rb);
+    if constexpr (TR == 2)
+      slice_steps(slice + 1, w_regB, w_regA, 1, band_ra, band_rb);
+    else
+      slice_steps(slice + 1, w_regB, w_regA, 1, band_rb, band_ra);
   }
-  if (slice < nslices) slice_steps(slice, w_regA, w_regB, 0);
+  if (slice < nslices) slice_steps(slice, w_regA, w_regB, 0, band_ra, band_rb);
 
   // -------- epilogue: lane holds channels m0 + wn*CW + i*16 + 4*(lane/16) + 0..3 of one pixel
   const int r = pr0 + wr;
@@ -331,15 +409,19 @@ __global__ __launch_bounds__(kConvThreads, 1) void conv3x3_bf16_mfma_kernel(Conv
     }
     return;  // uniform over the workgroup: no barrier follows
   }
-  // bf16 output: bias added and rounded in registers, the tile (2 rows x TC
-  // pixels x 128 channels) staged in LDS ([pixel][channel]; pixels padded by
-  // 16 bytes, a stride of 4 banks mod 64, so the 16 pixels of a tile write
-  // fall on distinct banks), then stored so that each wave store
-  // writes the 256 contiguous bytes of two whole pixels instead of 32-byte
-  // pieces of 16 pixels.  The slice loop ended with a barrier, so the weight
-  // buffers are free.
-  constexpr int kPixU2 = kConvBM / 4 + 2;  // uint2 per padded LDS pixel
-  uint2* const tile = reinterpret_cast<uint2*>(&wts[0][0][0]);
+  // bf16 output: bias added and rounded in registers, the tile (TR rows x TC
+  // pixels x BM channels) staged in LDS ([pixel][channel]; pixels padded by
+  // 16 bytes, so that the 16 pixels of a tile write fall on distinct banks),
+  // then stored so that each wave store writes whole pixels (256 or 128
+  // contiguous bytes) instead of 32-byte pieces of 16 pixels.  The slice
+  // loop ended with a barrier, so the band and weight buffers are free; the
+  // tile (and the statistics scratch) goes into the larger of the two.
+  constexpr int kPixU2 = BM / 4 + 2;  // uint2 per padded LDS pixel
+  constexpr int kTileU2 = TR * TC * kPixU2;
+  constexpr size_t kEpiBytes = kTileU2 * 8 + 4 * tile_group_sums_scratch_floats<kConvThreads, BM>();
+  constexpr bool kTileInBand = sizeof(band) >= sizeof(wts);
+  static_assert(kEpiBytes <= (kTileInBand ? sizeof(band) : sizeof(wts)), "staged tile and statistics scratch fit");
+  uint2* const tile = kTileInBand ? reinterpret_cast<uint2*>(&band[0]) : reinterpret_cast<uint2*>(&wts[0][0][0]);
 #pragma unroll
   for (int i = 0; i < kConvCG; ++i) {
     const int c = wn * kConvCW + i * 16 + 4 * kg;
@@ -358,12 +440,12 @@ __global__ __launch_bounds__(kConvThreads, 1) void conv3x3_bf16_mfma_kernel(Conv
     }
   }
   __syncthreads();
-  constexpr int kChunks = kConvTR * TC * (kConvBM / 4);  // 8-byte chunks of the tile
+  constexpr int kChunks = TR * TC * (BM / 4);  // 8-byte chunks of the tile
   static_assert(kChunks % kConvThreads == 0, "whole chunks per thread");
 #pragma unroll
   for (int u = 0; u < kChunks / kConvThreads; ++u) {
     const int id = tid + u * kConvThreads;
-    const int pix = id / (kConvBM / 4), q = id % (kConvBM / 4);
+    const int pix = id / (BM / 4), q = id % (BM / 4);
     const int row = pr0 + pix / TC, col = pc0 + pix % TC, m = m0 + 4 * q;
     if (row < a.rows && col < W && m < a.Cout)
       *reinterpret_cast<uint2*>(a.y + ((static_cast<int64_t>(b) * a.rows + row) * W + col) * a.Cout + m) =
@@ -371,15 +453,12 @@ __global__ __launch_bounds__(kConvThreads, 1) void conv3x3_bf16_mfma_kernel(Conv
   }
   if (a.gn_part != nullptr) {
     // GroupNorm partial sums of this tile's stored values, one chunk per
-    // workgroup (chunk = channel tile * pixel tiles + pixel tile); the weight
-    // buffers past the staged tile are the scratch
-    constexpr int kTileU2 = kConvTR * TC * kPixU2;
-    static_assert((kTileU2 * 8 + 4 * tile_group_sums_scratch_floats<kConvThreads, kConvBM>()) <= sizeof(wts),
-                  "statistics scratch fits after the staged tile");
+    // workgroup (chunk = channel tile * pixel tiles + pixel tile); the LDS
+    // past the staged tile is the scratch
     const int64_t nchunk = static_cast<int64_t>(gridDim.x) * gridDim.y;
     const int64_t chunk = static_cast<int64_t>(blockIdx.y) * gridDim.x + blockIdx.x;
     float* out = a.gn_part + (static_cast<int64_t>(b) * nchunk + chunk) * a.G * 2;
-    tile_group_sums<kConvThreads, kConvTR * TC, kConvBM>(
+    tile_group_sums<kConvThreads, TR * TC, BM>(
         reinterpret_cast<const uint16_t*>(tile), 4 * kPixU2,
         [&](int p) { return pr0 + p / TC < a.rows && pc0 + p % TC < W; }, m0, a.Cout, a.Cout / a.G, a.G,
         reinterpret_cast<float*>(tile + kTileU2), out);
@@ -421,6 +500,21 @@ static int conv_pick_tg(int64_t W) {
   return best;
 }
 
+// Row-tile choice: four patch rows x 64 channels (half the weight bytes per
+// step, two band rows staged every step) or two rows x 128 channels.  The
+// four-row tile measured faster at every band tried (same bits): 240 x 240
+// image, 30-row band 58.6 -> 56.8 us, 15-row band 52.0 -> 50.2 us; 128 x 128,
+// 16 rows 44.5 -> 41.7 us; 64 x 64, 16 rows 43.1 -> 39.8 us (unsplit calls).
+static int conv_pick_tr(int64_t rows, int64_t W, int64_t Cout) {
+  (void)rows; (void)W; (void)Cout;
+  return 4;
+}
+
+static int64_t conv_tiles(int64_t rows, int64_t W, int64_t Cout) {
+  const int tr = conv_pick_tr(rows, W, Cout);
+  return ceil_div(rows, tr) * ceil_div(W, 16 * conv_pick_tg(W)) * ceil_div(Cout, 256 / tr);
+}
+
 struct ConvSplit {
   int nsplit, spl;
 };
@@ -437,8 +531,7 @@ struct ConvSplit {
 // 8-patch band, 20 -> 10 (54 -> 29 us); full images never split.
 static ConvSplit conv_split(int64_t B, int64_t rows, int64_t W, int64_t Cin, int64_t Cout) {
   constexpr double kSliceRoundBytes = 16e6;
-  const int tg = conv_pick_tg(W);
-  const int64_t wgs = ceil_div(rows, kConvTR) * ceil_div(W, 16 * tg) * ceil_div(Cout, kConvBM) * B;
+  const int64_t wgs = conv_tiles(rows, W, Cout) * B;
   const int64_t nsl = Cin / kConvKC;
   const double out_bytes = static_cast<double>(B) * rows * W * Cout * sizeof(float);
   ConvSplit best{1, static_cast<int>(nsl)};
@@ -458,13 +551,24 @@ static ConvSplit conv_split(int64_t B, int64_t rows, int64_t W, int64_t Cin, int
 }
 
 int64_t conv_gn_chunks(int64_t rows, int64_t W, int64_t Cout) {
-  return ceil_div(rows, kConvTR) * ceil_div(W, 16 * conv_pick_tg(W)) * ceil_div(Cout, kConvBM);
+  return conv_tiles(rows, W, Cout);
 }
 
 size_t conv_workspace_bytes(int64_t B, int64_t rows, int64_t W, int64_t Cin, int64_t Cout) {
   const ConvSplit sp = conv_split(B, rows, W, Cin, Cout);
   if (sp.nsplit <= 1) return 0;
   return static_cast<size_t>(sp.nsplit) * B * rows * W * Cout * sizeof(float);
+}
+
+template <int TR>
+static void launch_conv_tg(int tg, dim3 grid, const ConvArgs& a, hipStream_t s) {
+  switch (tg) {
+    case 1: hipLaunchKernelGGL((conv3x3_bf16_mfma_kernel<1, TR>), grid, dim3(kConvThreads), 0, s, a); break;
+    case 2: hipLaunchKernelGGL((conv3x3_bf16_mfma_kernel<2, TR>), grid, dim3(kConvThreads), 0, s, a); break;
+    case 3: hipLaunchKernelGGL((conv3x3_bf16_mfma_kernel<3, TR>), grid, dim3(kConvThreads), 0, s, a); break;
+    case 4: hipLaunchKernelGGL((conv3x3_bf16_mfma_kernel<4, TR>), grid, dim3(kConvThreads), 0, s, a); break;
+    default: hipLaunchKernelGGL((conv3x3_bf16_mfma_kernel<5, TR>), grid, dim3(kConvThreads), 0, s, a); break;
+  }
 }
 
 hipError_t launch_conv3x3(void* y, const void* x, const void* stale_full, const void* weight, const float* bias,
@@ -492,8 +596,10 @@ hipError_t launch_conv3x3(void* y, const void* x, const void* stale_full, const 
   a.row0 = static_cast<int>(row0);
   a.rows = static_cast<int>(rows);
   const int tg = conv_pick_tg(W);
+  const int tr = conv_pick_tr(rows, W, Cout);
+  const int bm = 256 / tr;
   a.tiles_c = static_cast<int>(ceil_div(W, 16 * tg));
-  const int64_t tiles = ceil_div(rows, kConvTR) * a.tiles_c;
+  const int64_t tiles = ceil_div(rows, tr) * a.tiles_c;
   ConvSplit sp = conv_split(B, rows, W, Cin, Cout);
   if (sp.nsplit > 1 && (gn_part != nullptr || ws == nullptr || ws_bytes < conv_workspace_bytes(B, rows, W, Cin, Cout)))
     sp = ConvSplit{1, static_cast<int>(Cin / kConvKC)};
@@ -502,14 +608,12 @@ hipError_t launch_conv3x3(void* y, const void* x, const void* stale_full, const 
   a.nsplit = sp.nsplit;
   a.spl = sp.spl;
   a.part = sp.nsplit > 1 ? static_cast<float*>(ws) : nullptr;
-  dim3 grid(static_cast<unsigned>(tiles), static_cast<unsigned>(ceil_div(Cout, kConvBM)),
+  dim3 grid(static_cast<unsigned>(tiles), static_cast<unsigned>(ceil_div(Cout, bm)),
             static_cast<unsigned>(B * sp.nsplit));
-  switch (tg) {
-    case 1: hipLaunchKernelGGL(conv3x3_bf16_mfma_kernel<1>, grid, dim3(kConvThreads), 0, s, a); break;
-    case 2: hipLaunchKernelGGL(conv3x3_bf16_mfma_kernel<2>, grid, dim3(kConvThreads), 0, s, a); break;
-    case 3: hipLaunchKernelGGL(conv3x3_bf16_mfma_kernel<3>, grid, dim3(kConvThreads), 0, s, a); break;
-    case 4: hipLaunchKernelGGL(conv3x3_bf16_mfma_kernel<4>, grid, dim3(kConvThreads), 0, s, a); break;
-    default: hipLaunchKernelGGL(conv3x3_bf16_mfma_kernel<5>, grid, dim3(kConvThreads), 0, s, a); break;
+  if (tr == 2) {
+    launch_conv_tg<2>(tg, grid, a, s);
+  } else {
+    launch_conv_tg<4>(tg, grid, a, s);
   }
   if (sp.nsplit > 1) {
     const hipError_t err = hipGetLastError();

@@ -363,7 +363,8 @@ def test_groupnorm_noalloc_validation():
 
 def test_producer_statistics_and_presummed_validation():
     # conv with GroupNorm partials: the conv's own checks, then its own
-    assert L.dpp_conv3x3_halo_gn_chunks(30, 240, 640) == 225          # 15 row pairs x 3 column tiles x 5 channel tiles
+    assert L.dpp_conv3x3_halo_gn_chunks(30, 240, 640) == 240          # 8 four-row tiles x 3 column tiles x 10 channel tiles
+    assert L.dpp_conv3x3_halo_gn_chunks(16, 64, 320) == 20            # 4 x 1 x 5
     assert L.dpp_linear_gn_chunks(1, 7200, 640) == 225                 # 45 token tiles x 5 channel tiles
     assert L.dpp_linear_gn_chunks(1, 7200, 1280) == 225                # 256-channel tiles: 45 x 5
     assert L.dpp_linear_gn_chunks(1, 1024, 640) == 65                  # few tiles: 80-token tiles, 13 x 5

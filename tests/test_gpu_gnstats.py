@@ -50,22 +50,33 @@ def _check_partials(part, y_vals, G, chunk_groups, what):
         assert np.all(part[:, c, others] == 0.0), f"{what}: chunk {c} wrote groups it does not touch"
 
 
-def _conv_chunk_groups(nchunk, Cout, G):
-    """Conv chunks are (channel tile of 128) * pixel tiles + pixel tile."""
-    ctiles = -(-Cout // 128)
-    ptiles = nchunk // ctiles
+def _conv_pixel_tiles(rows, W, tr):
+    """Pixel tiles of the conv: tr patch rows x 16 tg columns, tg (1..5) the
+    width that wastes the fewest columns, ties to the wider tile."""
+    tg = min(range(1, 6), key=lambda t: (-(-W // (16 * t)) * 16 * t - W, -t))
+    return -(-rows // tr) * -(-W // (16 * tg))
+
+
+def _conv_chunk_groups(nchunk, rows, W, Cout, G):
+    """Conv chunks are (channel tile) * pixel tiles + pixel tile; a tile is
+    four patch rows x 64 channels or two rows x 128 channels: the one whose
+    chunk count the call reports."""
+    shapes = [bm for bm in (64, 128) if -(-Cout // bm) * _conv_pixel_tiles(rows, W, 256 // bm) == nchunk]
+    assert shapes, f"no tile shape gives {nchunk} chunks"
+    bm = shapes[0]
+    ptiles = nchunk // -(-Cout // bm)
     cg = Cout // G
     out = []
     for c in range(nchunk):
         ct = c // ptiles
-        lo, hi = ct * 128, min(Cout, ct * 128 + 128)
+        lo, hi = ct * bm, min(Cout, ct * bm + bm)
         out.append(set(range(lo // cg, (hi - 1) // cg + 1)))
     return out
 
 
 CONV_CASES = [
     # (config, patch, G) -- G sets the channels per group: 20, 10, 6 (groups straddle
-    # 4-channel quads and 128-channel tiles), 1 (one group), C (one channel each)
+    # 4-channel quads and 64-channel tiles), 1 (one group), C (one channel each)
     (Config("gs_1024", B=1, H=64, W=64, C=640, P=4), 1, 32),
     (Config("gs_c320", B=1, H=16, W=48, C=320, P=2, G=32, heads=5, D=64), 1, 32),
     (Config("gs_w37", B=2, H=12, W=37, C=192, P=4, G=8, heads=3, D=64), 2, 32),
@@ -94,7 +105,8 @@ def test_conv_gn_partials(cfg, p, G):
     check_guards(ybase, f"conv gn {cfg.name} y")
     check_guards(pbase, f"conv gn {cfg.name} partials")
     np.testing.assert_array_equal(bits(y), bits(y_ref))
-    _check_partials(part.cpu().numpy(), to_host(y), G, _conv_chunk_groups(nchunk, cfg.C, G), f"conv gn {cfg.name}")
+    _check_partials(part.cpu().numpy(), to_host(y), G, _conv_chunk_groups(nchunk, cfg.rows, cfg.W, cfg.C, G),
+                    f"conv gn {cfg.name}")
 
 
 LIN_CASES = [(2, 300, 640, 640, 32), (1, 7200, 640, 640, 32), (1, 1024, 320, 320, 32), (1, 333, 128, 1280, 32),
@@ -237,7 +249,7 @@ def test_groupnorm_presummed_matches_plain_groupnorm():
                 to_dev(inp["conv_w"], "bf16"))
     b = torch.from_numpy(inp["conv_b"]).cuda()
     nchunk = dpp.dpp_conv3x3_halo_gn_chunks(cfg.rows, cfg.W, cfg.C)
-    assert nchunk == 225
+    assert nchunk == 240  # 8 four-row tiles x 3 column tiles x 10 channel tiles
     part = torch.empty(cfg.B, nchunk, cfg.G, 2, device="cuda")
     h = torch.empty(cfg.B, cfg.rows, cfg.W, cfg.C, dtype=torch.bfloat16, device="cuda")
     dpp.dpp_conv3x3_halo_gn(h, part, x, st, w, b, cfg.H, r0)
