@@ -61,49 +61,42 @@ __global__ __launch_bounds__(256) void conv3x3_f32_kernel(float* __restrict__ y,
 }
 
 // ------------------------------------------------------------------ bf16 MFMA implicit GEMM
-// Workgroup tile: TR patch rows x 16*TG columns of output pixels x BM = 256/TR
-// output channels (TR = 2: 128 channels; TR = 4: 64 channels).  Eight waves;
-// wave (wr, wn) owns tile row wr and channels [32 wn, 32 wn + 32): TG x 2
-// accumulator tiles of 16 x 16.  The host picks TG (1..5) so that the tiles
-// cover the row width with the least waste (e.g. 240 columns -> TG 5: three
-// tiles per row) and TR per shape.
+// Workgroup tile: 4 patch rows x 16*TG columns of output pixels x 64 output
+// channels; eight waves, wave (wr, wn) owns tile row wr and channels
+// [32 wn, 32 wn + 32): TG x 2 accumulator tiles of 16 x 16.  The host picks
+// TG (1..5) so that the tiles cover the row width with the least waste (e.g.
+// 240 columns -> TG 5: three tiles per row).
 //
 // K loop: step = (64-channel slice, kernel row dy), three taps (dx = 0..2)
-// each, one barrier per step.  The weights of a step (3 x BM x 64) are
+// each, one barrier per step.  The weights of a step (3 x 64 x 64) are
 // double-buffered in LDS and fetched into registers two steps ahead.  The
-// (TR+2) x (16 TG + 2) halo band of a slice is staged once and read by all
-// nine taps, in two-row pieces, each fetched into registers two steps before
-// it is written:
-//  * TR = 2: one four-row buffer.  Step dy reads band rows dy and dy+1 only,
-//    so rows 0-1 of the next slice's band are written during its dy = 2 step
-//    (they were last read at dy = 1) and rows 2-3 during the next slice's
-//    dy = 0 step.
-//  * TR = 4: a ring of eight rows; slice s's band row i sits in ring row
-//    (6s + i) mod 8.  Step dy reads rows dy .. dy+3.  Rows 4-5 of slice s are
-//    written during its dy = 0 step (into the ring rows of slice s-1's rows
-//    2-3), rows 0-1 of slice s+1 during dy = 1 (ring rows slice s does not
-//    use), rows 2-3 of slice s+1 during dy = 2 (slice s's rows 0-1, last read
-//    at dy = 1).  Each step writes two rows, and the 64-channel tile halves
-//    the weight bytes per step.
-// Every global load is unconditional (weight rows past Cout read zero
-// through the buffer resource's range check; band vectors in the zero
-// padding load a valid address and are zeroed when staged), and a pair of
+// 6 x (16 TG + 2) halo band of a slice is staged once and read by all nine
+// taps, from a ring of eight LDS rows: slice s's band row i sits in ring row
+// (6s + i) mod 8, and step dy reads band rows dy .. dy+3.  The band goes in
+// two-row pieces A, B, C (rows 0-1, 2-3, 4-5), each fetched into registers
+// two steps before it is written: C(s) during slice s's dy = 0 step (into the
+// ring rows of slice s-1's rows 2-3), A(s+1) during dy = 1 (ring rows slice s
+// does not use), B(s+1) during dy = 2 (slice s's rows 0-1, last read at
+// dy = 1).
+//
+// Staging loads carry no predicates: a weight row past Cout and a band
+// vector outside the image lie beyond the range of their buffer resource,
+// which returns zeros.  Each band row has one source (x for patch rows, the
+// stale image for halo rows, nothing above or below the image), so the four
+// waves that load a row use one resource based at that row's first pixel
+// at the slice's channels; a lane's offsets are fixed for the kernel, and
+// its LDS slot is the ring row's base plus a fixed column part.  A pair of
 // slices is one straight-line loop body, so each wait before a staging store
 // covers only the loads it needs.
-constexpr int kConvCW = 32;                // output channels per wave
-constexpr int kConvCG = kConvCW / 16;      // 16-channel MFMA groups per wave
-constexpr int kConvThreads = 512;          // 8 waves
-constexpr int kConvKC = 64;                // input channels per slice (8 x 16-byte vectors)
-constexpr int kConvBufWord3 = 0x00020000;  // raw 32-bit buffer access, no swizzle
-
-template <int TR>
-struct ConvTile {
-  static_assert(TR == 2 || TR == 4, "two or four patch rows per workgroup");
-  static constexpr int BM = 256 / TR;             // output channels per workgroup
-  static constexpr int WN = BM / kConvCW;         // waves across the channels
-  static constexpr int RING = TR == 2 ? 4 : 8;    // band rows held in LDS
-  static constexpr int NPIECE = (TR + 2) / 2;     // two-row pieces of a slice's band
-};
+constexpr int kConvTR = 4;                  // patch rows per workgroup
+constexpr int kConvBM = 64;                 // output channels per workgroup
+constexpr int kConvCW = 32;                 // output channels per wave
+constexpr int kConvCG = kConvCW / 16;       // 16-channel MFMA groups per wave
+constexpr int kConvWN = kConvBM / kConvCW;  // waves across the channels
+constexpr int kConvThreads = 512;           // 8 waves: 4 rows x 2 channel halves
+constexpr int kConvKC = 64;                 // input channels per slice (8 x 16-byte vectors)
+constexpr int kConvRing = 8;                // band rows held in LDS
+constexpr int kConvBufWord3 = 0x00020000;   // raw 32-bit buffer access, no swizzle
 
 struct ConvArgs {
   const uint16_t* x;
@@ -122,69 +115,59 @@ struct ConvArgs {
 
 // LDS row of 8 x 16-byte slots, slot index XOR-swizzled by the row index so
 // that 16 lanes reading the same logical slot of consecutive rows spread over
-// the banks.
+// the banks (weights: a row is an output channel; band: a row is a pixel,
+// keyed by its column, which within one ring row is the same spread).
 __device__ __forceinline__ int swz(int row, int slot) { return row * 8 + (slot ^ (row & 7)); }
 
-template <int TG, int TR>
+template <int TG>
 __global__ __launch_bounds__(kConvThreads, 1) void conv3x3_bf16_mfma_kernel(ConvArgs a) {
-  constexpr int BM = ConvTile<TR>::BM, WN = ConvTile<TR>::WN, RING = ConvTile<TR>::RING;
-  constexpr int NPIECE = ConvTile<TR>::NPIECE;
-  constexpr int TC = 16 * TG;              // output columns per tile
-  constexpr int BW = TC + 2;               // band columns
-  constexpr int PIECE_VEC = 2 * BW * 8;    // 16-byte vectors in two band rows
-  constexpr int HB_ITERS = (PIECE_VEC + kConvThreads - 1) / kConvThreads;
-  constexpr int W_ITERS = BM * 8 / kConvThreads;
-  constexpr int BAND_VEC = RING * BW * 8;
-  static_assert(NPIECE * HB_ITERS <= 32, "staging mask bits");
+  constexpr int TC = 16 * TG;                   // output columns per tile
+  constexpr int BW = TC + 2;                    // band columns
+  constexpr int ROW_VEC = BW * 8;               // 16-byte vectors in one band row
+  constexpr int RB_ITERS = (ROW_VEC + 255) / 256;  // per lane, four waves per row
+  constexpr int W_ITERS = kConvBM * 8 / kConvThreads;
+  constexpr int BAND_VEC = kConvRing * ROW_VEC;
 
-  // band: RING rows x BW pixels x 8 slots, plus one dummy slot that absorbs
-  // the stores of the threads past the last vector of a piece
-  __shared__ uint4 band[BAND_VEC + 1];
-  __shared__ uint4 wts[2][3][BM * 8];
+  __shared__ uint4 band[BAND_VEC];
+  __shared__ uint4 wts[2][3][kConvBM * 8];
 
   const int tid = threadIdx.x;
-  const int wave = tid / kWave, lane = tid % kWave;
-  const int wr = wave / WN, wn = wave % WN;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave), lane = tid % kWave;
+  const int wr = wave / kConvWN, wn = wave % kConvWN;
   const int b = blockIdx.z / a.nsplit, split = blockIdx.z % a.nsplit;
-  const int m0 = blockIdx.y * BM;
+  const int m0 = blockIdx.y * kConvBM;
   const int tile_r = blockIdx.x / a.tiles_c, tile_c = blockIdx.x % a.tiles_c;
-  const int pr0 = tile_r * TR, pc0 = tile_c * TC;  // patch-relative origin of the pixel tile
+  const int pr0 = tile_r * kConvTR, pc0 = tile_c * TC;  // patch-relative origin of the pixel tile
   const int H = a.H, W = a.W, Cin = a.Cin;
   // this workgroup's input-channel slices: [s0, s0 + nslices)
   const int s0 = split * a.spl;
   const int nslices = min(a.spl, Cin / kConvKC - s0);
   const int nsteps = nslices * 3;
 
-  // Band staging map, fixed for the kernel: vector u of piece pc (band rows
-  // 2pc, 2pc+1) -> source address of the first slice (x for patch rows, the
-  // stale image for halo rows; zero padding loads x and is masked) and its
-  // place: TR = 2 the LDS slot; TR = 4 (band row << 12 | column << 3 | slot),
-  // placed in the ring when stored; -1 past the last vector.
-  const uint16_t* band_src[NPIECE][HB_ITERS];
-  int band_pos[NPIECE][HB_ITERS];
-  uint32_t band_ok = 0;  // bit pc*HB_ITERS+u: the vector is inside the image
+  // Band staging map.  Waves 0-3 load the first row of a piece, waves 4-7
+  // the second; lane vector u -> band column bc, slot: byte offset from the
+  // row's first pixel (beyond the resource for columns outside the image and
+  // for lanes past the row) and the column part of its LDS slot.
+  const int prow = wave >> 2;  // row within a piece
+  int b_off[RB_ITERS], b_col[RB_ITERS];
 #pragma unroll
-  for (int pc = 0; pc < NPIECE; ++pc)
-#pragma unroll
-    for (int u = 0; u < HB_ITERS; ++u) {
-      const int id = tid + u * kConvThreads;
-      const int lp = id >> 3, slot = id & 7;
-      const int br = 2 * pc + lp / BW, bc = lp % BW;
-      const int r = pr0 - 1 + br;  // patch-relative
-      const int ir = a.row0 + r;   // image row
-      const int col = pc0 - 1 + bc;
-      band_src[pc][u] = a.x + slot * 8;
-      band_pos[pc][u] = TR == 2 ? BAND_VEC : -1;
-      if (id < PIECE_VEC) {
-        band_pos[pc][u] = TR == 2 ? swz(br * BW + bc, slot) : (br << 12) | (bc << 3) | slot;
-        if (ir >= 0 && ir < H && col >= 0 && col < W) {
-          band_src[pc][u] = ((r >= 0 && r < a.rows) ? a.x + ((static_cast<int64_t>(b) * a.rows + r) * W + col) * Cin
-                                                    : a.stale + ((static_cast<int64_t>(b) * H + ir) * W + col) * Cin) +
-                            slot * 8;
-          band_ok |= 1u << (pc * HB_ITERS + u);
-        }
-      }
-    }
+  for (int u = 0; u < RB_ITERS; ++u) {
+    const int id = (wave & 3) * kWave + lane + u * 256;
+    const int bc = id >> 3, slot = id & 7;
+    const int col = pc0 - 1 + bc;
+    b_off[u] = (id < ROW_VEC && col >= 0 && col < W) ? (col * Cin + slot * 8) * 2 : 0x7ffffff0;
+    b_col[u] = id < ROW_VEC ? bc * 8 + (slot ^ (bc & 7)) : -1;
+  }
+  // source row of this wave's row of piece pc (band row 2 pc + prow), or NULL
+  // above and below the image
+  auto band_row_src = [&](int pc) -> const uint16_t* {
+    const int r = pr0 - 1 + 2 * pc + prow;  // patch-relative
+    const int ir = a.row0 + r;              // image row
+    if (ir < 0 || ir >= H) return nullptr;
+    return (r >= 0 && r < a.rows) ? a.x + (static_cast<int64_t>(b) * a.rows + r) * W * Cin
+                                  : a.stale + (static_cast<int64_t>(b) * H + ir) * W * Cin;
+  };
+  const uint16_t* const row_src[3] = {band_row_src(0), band_row_src(1), band_row_src(2)};
   // Weight staging map: vector u -> byte offset of row m0 + m, slot, at tap 0
   // of slice 0; rows past Cout lie beyond the resource and read zero.
   const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
@@ -196,30 +179,24 @@ __global__ __launch_bounds__(kConvThreads, 1) void conv3x3_bf16_mfma_kernel(Conv
     w_off[u] = ((m0 + (id >> 3)) * 9 * Cin + (id & 7) * 8) * 2;
   }
 
-  uint4 band_ra[HB_ITERS], band_rb[HB_ITERS];  // two band pieces in flight
+  uint4 band_ra[RB_ITERS], band_rb[RB_ITERS];  // two band pieces in flight
   uint4 w_regA[3][W_ITERS], w_regB[3][W_ITERS];  // weights of the next two steps
   // Loads never touch their results until the staging store.
-  auto load_piece = [&](uint4 (&reg)[HB_ITERS], int pc, int slice) {
+  auto load_piece = [&](uint4 (&reg)[RB_ITERS], int pc, int slice) {
     const int c0 = (s0 + min(slice, nslices - 1)) * kConvKC;
+    const uint16_t* src = row_src[pc];
+    const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(src ? src + c0 : a.x), 0, src ? (W * Cin - c0) * 2 : 0, kConvBufWord3);
 #pragma unroll
-    for (int u = 0; u < HB_ITERS; ++u) reg[u] = *reinterpret_cast<const uint4*>(band_src[pc][u] + c0);
+    for (int u = 0; u < RB_ITERS; ++u)
+      reg[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rb, b_off[u], 0, 0));
   };
-  // piece pc into the band; TR = 4: ring row (base + band row) mod 8
-  auto store_piece = [&](uint4 (&reg)[HB_ITERS], int pc, int base) {
+  // piece pc into ring rows (base + 2 pc + prow) mod 8
+  auto store_piece = [&](const uint4 (&reg)[RB_ITERS], int pc, int base) {
+    const int row_base = ((base + 2 * pc + prow) & (kConvRing - 1)) * ROW_VEC;
 #pragma unroll
-    for (int u = 0; u < HB_ITERS; ++u) {
-      const uint32_t keep = 0u - ((band_ok >> (pc * HB_ITERS + u)) & 1u);
-      // pins the mask here: hoisted next to the load, it would make the
-      // wave wait for the load there
-      asm volatile("" : "+v"(reg[u].x), "+v"(reg[u].y), "+v"(reg[u].z), "+v"(reg[u].w));
-      int dst = band_pos[pc][u];
-      if constexpr (TR != 2) {
-        const int pos = dst;
-        const int prow = ((base + (pos >> 12)) & (RING - 1)) * BW + ((pos >> 3) & 511);
-        dst = pos < 0 ? BAND_VEC : swz(prow, pos & 7);
-      }
-      band[dst] = make_uint4(reg[u].x & keep, reg[u].y & keep, reg[u].z & keep, reg[u].w & keep);
-    }
+    for (int u = 0; u < RB_ITERS; ++u)
+      if (u + 1 < RB_ITERS || b_col[u] >= 0) band[row_base + b_col[u]] = reg[u];
   };
   auto load_w = [&](uint4 (&reg)[3][W_ITERS], int step) {
     const int st = min(step, nsteps - 1);
@@ -262,17 +239,18 @@ __global__ __launch_bounds__(kConvThreads, 1) void conv3x3_bf16_mfma_kernel(Conv
   // sinking those reads next to their use.
   auto frag_load = [&](int dy, int wb, int base, int n, bf16x8 (&af)[kConvCG], bf16x8 (&bfr)[TG]) {
     const int dx = n >> 1, ks = n & 1;
-    // B fragment rows bp = (band row of wr + dy) * BW + dx + 16 j + pl: all
-    // fragments of a tap share (bp & 7), so one swizzled slot per k step
-    // serves all j
-    const int brow = TR == 2 ? wr + dy : (base + wr + dy) & (RING - 1);
-    const int bp0 = brow * BW + dx + pl;
-    const int bslot = (ks * 4 + kg) ^ (bp0 & 7);
+    // B fragment j: band column dx + 16 j + pl of ring row (base + wr + dy)
+    // mod 8; the columns of a tap share (column & 7), so one swizzled slot per
+    // k step serves all j
+    const int brow = (base + wr + dy) & (kConvRing - 1);
+    const int col0 = dx + pl;
+    const int bslot = (ks * 4 + kg) ^ (col0 & 7);
 #pragma unroll
     for (int i = 0; i < kConvCG; ++i)
       af[i] = __builtin_bit_cast(bf16x8, wts[wb][dx][(a_row0 + 16 * i) * 8 + a_slot[ks]]);
 #pragma unroll
-    for (int j = 0; j < TG; ++j) bfr[j] = __builtin_bit_cast(bf16x8, band[(bp0 + 16 * j) * 8 + bslot]);
+    for (int j = 0; j < TG; ++j)
+      bfr[j] = __builtin_bit_cast(bf16x8, band[brow * ROW_VEC + (col0 + 16 * j) * 8 + bslot]);
   };
   auto mfma_batch = [&](const bf16x8 (&af)[kConvCG], const bf16x8 (&bfr)[TG]) {
 #pragma unroll
@@ -300,81 +278,47 @@ __global__ __launch_bounds__(kConvThreads, 1) void conv3x3_bf16_mfma_kernel(Conv
   };
   // Step st = 3 slice + dy (st & 1 == p): compute on weight buffer p, stage
   // the weights of st+1 (held in wnext) into the other buffer, barrier, fetch
-  // the weights of st+3 into wnext.  Around it, the band pieces.
-  //  TR = 2 (lo, hi = rows 0-1, 2-3): loads of the next slice at dy = 0 (lo)
-  //  and dy = 1 (hi); lo is staged at dy = 2, hi at the next slice's dy = 0.
-  //  TR = 4 (pieces A, B, C = rows 0-1, 2-3, 4-5; e and o hold the pieces
-  //  fetched at even and odd steps): dy = 0 stages C(s) and fetches B(s+1),
-  //  dy = 1 stages A(s+1) and fetches C(s+1), dy = 2 stages B(s+1) and
-  //  fetches A(s+2).
+  // the weights of st+3 into wnext.  Before it, the band pieces (e and o hold
+  // the pieces fetched at even and odd steps): dy = 0 stages C(s) and
+  // fetches B(s+1), dy = 1 stages A(s+1) and fetches C(s+1), dy = 2 stages
+  // B(s+1) and fetches A(s+2).
   auto slice_steps = [&](int slice, uint4 (&w0)[3][W_ITERS], uint4 (&w1)[3][W_ITERS], int p,
-                         uint4 (&e)[HB_ITERS], uint4 (&o)[HB_ITERS]) {
+                         uint4 (&e)[RB_ITERS], uint4 (&o)[RB_ITERS]) {
     const int st = slice * 3;
-    if constexpr (TR == 2) {
-      // e = lo, o = hi (fixed roles)
-      // dy = 0
-      store_piece(o, 1, 0);
-      load_piece(e, 0, slice + 1);
-      compute(0, p, 0);
-      store_w(w0, p ^ 1);
-      __syncthreads();
-      load_w(w0, st + 3);
-      // dy = 1
-      load_piece(o, 1, slice + 1);
-      compute(1, p ^ 1, 0);
-      store_w(w1, p);
-      __syncthreads();
-      load_w(w1, st + 4);
-      // dy = 2
-      compute(2, p, 0);
-      store_piece(e, 0, 0);
-      store_w(w0, p ^ 1);
-      __syncthreads();
-      load_w(w0, st + 5);
-    } else {
-      const int base = (6 * slice) & (RING - 1), nbase = (base + 6) & (RING - 1);
-      // dy = 0
-      store_piece(e, 2, base);
-      load_piece(e, 1, slice + 1);
-      compute(0, p, base);
-      store_w(w0, p ^ 1);
-      __syncthreads();
-      load_w(w0, st + 3);
-      // dy = 1
-      store_piece(o, 0, nbase);
-      load_piece(o, 2, slice + 1);
-      compute(1, p ^ 1, base);
-      store_w(w1, p);
-      __syncthreads();
-      load_w(w1, st + 4);
-      // dy = 2
-      store_piece(e, 1, nbase);
-      load_piece(e, 0, slice + 2);
-      compute(2, p, base);
-      store_w(w0, p ^ 1);
-      __syncthreads();
-      load_w(w0, st + 5);
-    }
+    const int base = (6 * slice) & (kConvRing - 1), nbase = (base + 6) & (kConvRing - 1);
+    // dy = 0
+    store_piece(e, 2, base);
+    load_piece(e, 1, slice + 1);
+    compute(0, p, base);
+    store_w(w0, p ^ 1);
+    __syncthreads();
+    load_w(w0, st + 3);
+    // dy = 1
+    store_piece(o, 0, nbase);
+    load_piece(o, 2, slice + 1);
+    compute(1, p ^ 1, base);
+    store_w(w1, p);
+    __syncthreads();
+    load_w(w1, st + 4);
+    // dy = 2
+    store_piece(e, 1, nbase);
+    load_piece(e, 0, slice + 2);
+    compute(2, p, base);
+    store_w(w0, p ^ 1);
+    __syncthreads();
+    load_w(w0, st + 5);
   };
 
-  // prologue: the band rows needed by the first step and the weights of step
-  // 0 staged; the next pieces and the weights of steps 1 and 2 in registers
-  if constexpr (TR == 2) {
-    load_piece(band_ra, 0, 0);
-    load_piece(band_rb, 1, 0);
-    load_w(w_regB, 0);
-    store_piece(band_ra, 0, 0);
-    store_w(w_regB, 0);
-  } else {
-    load_piece(band_ra, 0, 0);
-    load_piece(band_rb, 1, 0);
-    load_w(w_regB, 0);
-    store_piece(band_ra, 0, 0);
-    store_piece(band_rb, 1, 0);
-    store_w(w_regB, 0);
-    load_piece(band_ra, 2, 0);  // C(0), staged at step 0
-    load_piece(band_rb, 0, 1);  // A(1), staged at step 1
-  }
+  // prologue: band rows 0-3 of slice 0 and the weights of step 0 staged;
+  // C(0), A(1) and the weights of steps 1 and 2 in registers
+  load_piece(band_ra, 0, 0);
+  load_piece(band_rb, 1, 0);
+  load_w(w_regB, 0);
+  store_piece(band_ra, 0, 0);
+  store_piece(band_rb, 1, 0);
+  store_w(w_regB, 0);
+  load_piece(band_ra, 2, 0);  // C(0), staged at step 0
+  load_piece(band_rb, 0, 1);  // A(1), staged at step 1
   load_w(w_regA, 1);
   load_w(w_regB, 2);
   __syncthreads();
@@ -383,10 +327,7 @@ __global__ __launch_bounds__(kConvThreads, 1) void conv3x3_bf16_mfma_kernel(Conv
   int slice = 0;
   for (; slice + 1 < nslices; slice += 2) {
     slice_steps(slice, w_regA, w_regB, 0, band_ra, band_rb);
-    if constexpr (TR == 2)
-      slice_steps(slice + 1, w_regB, w_regA, 1, band_ra, band_rb);
-    else
-      slice_steps(slice + 1, w_regB, w_regA, 1, band_rb, band_ra);
+    slice_steps(slice + 1, w_regB, w_regA, 1, band_rb, band_ra);
   }
   if (slice < nslices) slice_steps(slice, w_regA, w_regB, 0, band_ra, band_rb);
 
@@ -409,16 +350,16 @@ __global__ __launch_bounds__(kConvThreads, 1) void conv3x3_bf16_mfma_kernel(Conv
     }
     return;  // uniform over the workgroup: no barrier follows
   }
-  // bf16 output: bias added and rounded in registers, the tile (TR rows x TC
-  // pixels x BM channels) staged in LDS ([pixel][channel]; pixels padded by
+  // bf16 output: bias added and rounded in registers, the tile (4 rows x TC
+  // pixels x 64 channels) staged in LDS ([pixel][channel]; pixels padded by
   // 16 bytes, so that the 16 pixels of a tile write fall on distinct banks),
-  // then stored so that each wave store writes whole pixels (256 or 128
-  // contiguous bytes) instead of 32-byte pieces of 16 pixels.  The slice
-  // loop ended with a barrier, so the band and weight buffers are free; the
-  // tile (and the statistics scratch) goes into the larger of the two.
-  constexpr int kPixU2 = BM / 4 + 2;  // uint2 per padded LDS pixel
-  constexpr int kTileU2 = TR * TC * kPixU2;
-  constexpr size_t kEpiBytes = kTileU2 * 8 + 4 * tile_group_sums_scratch_floats<kConvThreads, BM>();
+  // then stored so that each wave store writes four whole 128-byte pixels
+  // instead of 32-byte pieces of 16 pixels.  The slice loop ended with a
+  // barrier, so the band and weight buffers are free; the tile (and the
+  // statistics scratch) goes into the larger of the two.
+  constexpr int kPixU2 = kConvBM / 4 + 2;  // uint2 per padded LDS pixel
+  constexpr int kTileU2 = kConvTR * TC * kPixU2;
+  constexpr size_t kEpiBytes = kTileU2 * 8 + 4 * tile_group_sums_scratch_floats<kConvThreads, kConvBM>();
   constexpr bool kTileInBand = sizeof(band) >= sizeof(wts);
   static_assert(kEpiBytes <= (kTileInBand ? sizeof(band) : sizeof(wts)), "staged tile and statistics scratch fit");
   uint2* const tile = kTileInBand ? reinterpret_cast<uint2*>(&band[0]) : reinterpret_cast<uint2*>(&wts[0][0][0]);
@@ -440,12 +381,12 @@ __global__ __launch_bounds__(kConvThreads, 1) void conv3x3_bf16_mfma_kernel(Conv
     }
   }
   __syncthreads();
-  constexpr int kChunks = TR * TC * (BM / 4);  // 8-byte chunks of the tile
+  constexpr int kChunks = kConvTR * TC * (kConvBM / 4);  // 8-byte chunks of the tile
   static_assert(kChunks % kConvThreads == 0, "whole chunks per thread");
 #pragma unroll
   for (int u = 0; u < kChunks / kConvThreads; ++u) {
     const int id = tid + u * kConvThreads;
-    const int pix = id / (BM / 4), q = id % (BM / 4);
+    const int pix = id / (kConvBM / 4), q = id % (kConvBM / 4);
     const int row = pr0 + pix / TC, col = pc0 + pix % TC, m = m0 + 4 * q;
     if (row < a.rows && col < W && m < a.Cout)
       *reinterpret_cast<uint2*>(a.y + ((static_cast<int64_t>(b) * a.rows + row) * W + col) * a.Cout + m) =
@@ -458,7 +399,7 @@ __global__ __launch_bounds__(kConvThreads, 1) void conv3x3_bf16_mfma_kernel(Conv
     const int64_t nchunk = static_cast<int64_t>(gridDim.x) * gridDim.y;
     const int64_t chunk = static_cast<int64_t>(blockIdx.y) * gridDim.x + blockIdx.x;
     float* out = a.gn_part + (static_cast<int64_t>(b) * nchunk + chunk) * a.G * 2;
-    tile_group_sums<kConvThreads, TR * TC, BM>(
+    tile_group_sums<kConvThreads, kConvTR * TC, kConvBM>(
         reinterpret_cast<const uint16_t*>(tile), 4 * kPixU2,
         [&](int p) { return pr0 + p / TC < a.rows && pc0 + p % TC < W; }, m0, a.Cout, a.Cout / a.G, a.G,
         reinterpret_cast<float*>(tile + kTileU2), out);
@@ -500,19 +441,8 @@ static int conv_pick_tg(int64_t W) {
   return best;
 }
 
-// Row-tile choice: four patch rows x 64 channels (half the weight bytes per
-// step, two band rows staged every step) or two rows x 128 channels.  The
-// four-row tile measured faster at every band tried (same bits): 240 x 240
-// image, 30-row band 58.6 -> 56.8 us, 15-row band 52.0 -> 50.2 us; 128 x 128,
-// 16 rows 44.5 -> 41.7 us; 64 x 64, 16 rows 43.1 -> 39.8 us (unsplit calls).
-static int conv_pick_tr(int64_t rows, int64_t W, int64_t Cout) {
-  (void)rows; (void)W; (void)Cout;
-  return 4;
-}
-
 static int64_t conv_tiles(int64_t rows, int64_t W, int64_t Cout) {
-  const int tr = conv_pick_tr(rows, W, Cout);
-  return ceil_div(rows, tr) * ceil_div(W, 16 * conv_pick_tg(W)) * ceil_div(Cout, 256 / tr);
+  return ceil_div(rows, kConvTR) * ceil_div(W, 16 * conv_pick_tg(W)) * ceil_div(Cout, kConvBM);
 }
 
 struct ConvSplit {
@@ -560,17 +490,6 @@ size_t conv_workspace_bytes(int64_t B, int64_t rows, int64_t W, int64_t Cin, int
   return static_cast<size_t>(sp.nsplit) * B * rows * W * Cout * sizeof(float);
 }
 
-template <int TR>
-static void launch_conv_tg(int tg, dim3 grid, const ConvArgs& a, hipStream_t s) {
-  switch (tg) {
-    case 1: hipLaunchKernelGGL((conv3x3_bf16_mfma_kernel<1, TR>), grid, dim3(kConvThreads), 0, s, a); break;
-    case 2: hipLaunchKernelGGL((conv3x3_bf16_mfma_kernel<2, TR>), grid, dim3(kConvThreads), 0, s, a); break;
-    case 3: hipLaunchKernelGGL((conv3x3_bf16_mfma_kernel<3, TR>), grid, dim3(kConvThreads), 0, s, a); break;
-    case 4: hipLaunchKernelGGL((conv3x3_bf16_mfma_kernel<4, TR>), grid, dim3(kConvThreads), 0, s, a); break;
-    default: hipLaunchKernelGGL((conv3x3_bf16_mfma_kernel<5, TR>), grid, dim3(kConvThreads), 0, s, a); break;
-  }
-}
-
 hipError_t launch_conv3x3(void* y, const void* x, const void* stale_full, const void* weight, const float* bias,
                           int64_t B, int64_t H, int64_t W, int64_t Cin, int64_t Cout, int64_t row0, int64_t rows,
                           void* ws, size_t ws_bytes, bool bf16, hipStream_t s, float* gn_part, int G) {
@@ -596,10 +515,8 @@ hipError_t launch_conv3x3(void* y, const void* x, const void* stale_full, const 
   a.row0 = static_cast<int>(row0);
   a.rows = static_cast<int>(rows);
   const int tg = conv_pick_tg(W);
-  const int tr = conv_pick_tr(rows, W, Cout);
-  const int bm = 256 / tr;
   a.tiles_c = static_cast<int>(ceil_div(W, 16 * tg));
-  const int64_t tiles = ceil_div(rows, tr) * a.tiles_c;
+  const int64_t tiles = ceil_div(rows, kConvTR) * a.tiles_c;
   ConvSplit sp = conv_split(B, rows, W, Cin, Cout);
   if (sp.nsplit > 1 && (gn_part != nullptr || ws == nullptr || ws_bytes < conv_workspace_bytes(B, rows, W, Cin, Cout)))
     sp = ConvSplit{1, static_cast<int>(Cin / kConvKC)};
@@ -608,12 +525,14 @@ hipError_t launch_conv3x3(void* y, const void* x, const void* stale_full, const 
   a.nsplit = sp.nsplit;
   a.spl = sp.spl;
   a.part = sp.nsplit > 1 ? static_cast<float*>(ws) : nullptr;
-  dim3 grid(static_cast<unsigned>(tiles), static_cast<unsigned>(ceil_div(Cout, bm)),
+  dim3 grid(static_cast<unsigned>(tiles), static_cast<unsigned>(ceil_div(Cout, kConvBM)),
             static_cast<unsigned>(B * sp.nsplit));
-  if (tr == 2) {
-    launch_conv_tg<2>(tg, grid, a, s);
-  } else {
-    launch_conv_tg<4>(tg, grid, a, s);
+  switch (tg) {
+    case 1: hipLaunchKernelGGL(conv3x3_bf16_mfma_kernel<1>, grid, dim3(kConvThreads), 0, s, a); break;
+    case 2: hipLaunchKernelGGL(conv3x3_bf16_mfma_kernel<2>, grid, dim3(kConvThreads), 0, s, a); break;
+    case 3: hipLaunchKernelGGL(conv3x3_bf16_mfma_kernel<3>, grid, dim3(kConvThreads), 0, s, a); break;
+    case 4: hipLaunchKernelGGL(conv3x3_bf16_mfma_kernel<4>, grid, dim3(kConvThreads), 0, s, a); break;
+    default: hipLaunchKernelGGL(conv3x3_bf16_mfma_kernel<5>, grid, dim3(kConvThreads), 0, s, a); break;
   }
   if (sp.nsplit > 1) {
     const hipError_t err = hipGetLastError();
