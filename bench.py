@@ -238,25 +238,21 @@ def run(args):
     del inp, cin
     torch.cuda.synchronize()
 
+    # Timed steps carry one event pair per patch, around the attention call.
+    # An event record on this stack leaves the GPU idle for about 6 us (the
+    # next kernel starts that much after it), so more per-call events would
+    # slow the very steps they time: a pair around every kernel costs 1 % of
+    # the 3840 px step and 10 % of the 2048 px one (same-box A/B).  A patch-
+    # layer step is timed from one attention's end to the next's; the conv's
+    # per-call time comes from back-to-back calls after the timed steps.
     attn_events = []
-    conv_events = []
-    patch_events = []
 
     def step(record=False):
         for p in range(cfg.P):
             r0 = p * layer.R
-            if record:
-                p0 = torch.cuda.Event(enable_timing=True)
-                p0.record()
             dpp.dpp_groupnorm_stale(layer.y1, layer.stats_next, x_patches[p], layer.stats_prev, gamma, beta, cfg.H,
                                     cfg.G, cfg.P, p, cfg.gn_eps, layer.gn_ws)
-            if record:
-                c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                c0.record()
             dpp.dpp_conv3x3_halo(layer.y2, layer.y1, layer.a1, w, b, cfg.H, r0, workspace=layer.conv_ws)
-            if record:
-                c1.record()
-                conv_events.append((c0, c1))
             dpp.dpp_splice_patch(layer.kv[p], layer.y2, r0)
             kv = layer.kv[p].view(cfg.B, cfg.N, cfg.C)
             if record:
@@ -267,7 +263,6 @@ def run(args):
             if record:
                 e1.record()
                 attn_events.append((e0, e1))
-                patch_events.append((p0, e1))
         dpp.dpp_cfg_combine_relmae(eps, rel, eps_c, eps_u, cfg.guidance, cfg_ws)
 
     for _ in range(args.warmup):
@@ -281,8 +276,11 @@ def run(args):
     ms_step = wall * 1e3 / args.steps
     attn_ms = float(np.mean([a.elapsed_time(b_) for a, b_ in attn_events]))
     # one patch's GN -> conv -> splice -> attention, by events on the launch
-    # stream, over every patch and timed step
-    patch_ms = np.array([a.elapsed_time(b_) for a, b_ in patch_events])
+    # stream: from the end of patch p-1's attention to the end of patch p's,
+    # for p = 1 .. P-1 of every timed step (patch 0's interval would also hold
+    # the previous step's CFG combine)
+    patch_ms = np.array([attn_events[s * cfg.P + p - 1][1].elapsed_time(attn_events[s * cfg.P + p][1])
+                         for s in range(args.steps) for p in range(1, cfg.P)])
 
     f_conv, f_attn = flops(cfg)
     step_flops = cfg.P * (f_conv + f_attn)
@@ -297,8 +295,12 @@ def run(args):
                                                   layer.kv[p].view(cfg.B, cfg.N, cfg.C), cfg.heads, cfg.D, 0.0,
                                                   layer.attn_ws) for p in range(cfg.P)], torch)
     attn_tflops = f_attn / (attn_ms * 1e-3) / 1e12
-    conv_ms = float(np.mean([a.elapsed_time(b_) for a, b_ in conv_events]))
-    conv_tflops = f_conv / (conv_ms * 1e-3) / 1e12
+    # the conv's calls back to back, between one event pair (the attention's
+    # back-to-back figure above is taken the same way)
+    conv_b2b_ms = time_back_to_back(
+        [lambda p=p: dpp.dpp_conv3x3_halo(layer.y2, layer.y1, layer.a1, w, b, cfg.H, p * layer.R,
+                                           workspace=layer.conv_ws) for p in range(cfg.P)], torch)
+    conv_tflops = f_conv / (conv_b2b_ms * 1e-3) / 1e12
 
     graph = time_graph_step(step, step_flops, torch, args.steps)
 
@@ -360,9 +362,10 @@ def run(args):
     }
     out["roofline_conv"] = {
         "kernel": "dpp_conv3x3_halo", "bound": "mfma", "achieved": round(conv_tflops, 2), "peak": PEAK_BF16_TFLOPS,
-        "unit": "TFLOP/s", "frac": round(conv_tflops / PEAK_BF16_TFLOPS, 4), "avg_launch_ms": round(conv_ms, 5),
-        "flops_per_launch": f_conv,
-        "timing": "HIP events on the launch stream around each conv call inside the timed steps"}
+        "unit": "TFLOP/s", "frac": round(conv_tflops / PEAK_BF16_TFLOPS, 4),
+        "avg_launch_ms_back_to_back": round(conv_b2b_ms, 5), "flops_per_launch": f_conv,
+        "timing": "HIP events around every patch's conv call launched back to back after the timed steps (no "
+                  "per-call events inside the timed steps, whose records would slow them)"}
     out["graph_replay"] = graph
     if block:
         out["attention_block_step"] = block
@@ -472,49 +475,61 @@ def time_attention_block(cfg, dpp, torch, reps=3):
                      "attention -> out projection, per patch"}
 
 
+def time_rounds(families, torch, reps=10, min_calls=16):
+    """Per-call time of each call family: `reps` rounds of at least
+    `min_calls` calls of the family (its calls round-robin) back to back
+    between one pair of HIP events on the launch stream, behind a spin that
+    lets the host queue them first.  Returns {name: per-call ms of every
+    round}.  (A single call between its own event pair would also time the
+    GPU's idle gap after an event record, several us.)"""
+    out = {}
+    for name, calls in families.items():
+        n = max(min_calls, len(calls))
+        for fn in calls:
+            fn()
+        host_ahead(torch, reps * n)
+        pairs = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for i in range(n):
+                calls[i % len(calls)]()
+            e1.record()
+            pairs.append((e0, e1, n))
+        out[name] = pairs
+    torch.cuda.synchronize()
+    return {name: np.array([a.elapsed_time(b_) / n for a, b_, n in pairs]) for name, pairs in out.items()}
+
+
 def time_kernels(cfg, layer, x_patches, gamma, beta, w, b, eps, rel, eps_c, eps_u, cfg_ws, dpp, torch, reps=10):
-    """Average duration of each call family over all patches (HIP events on
-    the launch stream), with its algorithmic work."""
-    ev = {k: [] for k in ("groupnorm", "conv", "splice", "attention", "cfg", "conv_with_gn_partials",
-                          "groupnorm_presummed")}
-
-    def timed(name, fn):
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        fn()
-        e1.record()
-        ev[name].append((e0, e1))
-
-    host_ahead(torch, reps * (4 * cfg.P + 1))
-    for _ in range(reps):
-        for p in range(cfg.P):
-            r0 = p * layer.R
-            kv = layer.kv[p].view(cfg.B, cfg.N, cfg.C)
-            timed("groupnorm", lambda: dpp.dpp_groupnorm_stale(layer.y1, layer.stats_next, x_patches[p],
-                                                               layer.stats_prev, gamma, beta, cfg.H, cfg.G, cfg.P, p,
-                                                               cfg.gn_eps, layer.gn_ws))
-            timed("conv", lambda: dpp.dpp_conv3x3_halo(layer.y2, layer.y1, layer.a1, w, b, cfg.H, r0,
-                                                       workspace=layer.conv_ws))
-            timed("splice", lambda: dpp.dpp_splice_patch(layer.kv[p], layer.y2, r0))
-            timed("attention", lambda: dpp.dpp_self_attn_displaced(layer.o, layer.y2.view(cfg.B, cfg.Nq, cfg.C), kv,
-                                                                   kv, cfg.heads, cfg.D, 0.0, layer.attn_ws))
-        timed("cfg", lambda: dpp.dpp_cfg_combine_relmae(eps, rel, eps_c, eps_u, cfg.guidance, cfg_ws))
+    """Per-call duration of each call family over all patches (back-to-back
+    rounds, time_rounds), with its algorithmic work."""
+    P = cfg.P
+    fam = {
+        "groupnorm": [lambda p=p: dpp.dpp_groupnorm_stale(layer.y1, layer.stats_next, x_patches[p], layer.stats_prev,
+                                                          gamma, beta, cfg.H, cfg.G, cfg.P, p, cfg.gn_eps, layer.gn_ws)
+                      for p in range(P)],
+        "conv": [lambda p=p: dpp.dpp_conv3x3_halo(layer.y2, layer.y1, layer.a1, w, b, cfg.H, p * layer.R,
+                                                  workspace=layer.conv_ws) for p in range(P)],
+        "splice": [lambda p=p: dpp.dpp_splice_patch(layer.kv[p], layer.y2, p * layer.R) for p in range(P)],
+        "attention": [lambda p=p: dpp.dpp_self_attn_displaced(layer.o, layer.y2.view(cfg.B, cfg.Nq, cfg.C),
+                                                              layer.kv[p].view(cfg.B, cfg.N, cfg.C),
+                                                              layer.kv[p].view(cfg.B, cfg.N, cfg.C), cfg.heads, cfg.D,
+                                                              0.0, layer.attn_ws) for p in range(P)],
+        "cfg": [lambda: dpp.dpp_cfg_combine_relmae(eps, rel, eps_c, eps_u, cfg.guidance, cfg_ws)],
+    }
     if cfg.dtype == "bf16":
         # a GroupNorm whose input the conv wrote: the conv also emits the
         # group partial sums, and the GroupNorm reads its input once
         nchunk = dpp.dpp_conv3x3_halo_gn_chunks(cfg.rows, cfg.W, cfg.C)
         part = torch.empty(cfg.B, nchunk, cfg.G, 2, dtype=torch.float32, device="cuda")
         h = torch.empty_like(layer.y2)
-        host_ahead(torch, reps * 2 * cfg.P)
-        for _ in range(reps):
-            for p in range(cfg.P):
-                r0 = p * layer.R
-                timed("conv_with_gn_partials", lambda: dpp.dpp_conv3x3_halo_gn(h, part, layer.y1, layer.a1, w, b,
-                                                                               cfg.H, r0))
-                timed("groupnorm_presummed", lambda: dpp.dpp_groupnorm_stale_presummed(
-                    layer.y1, layer.stats_next, h, part, layer.stats_prev, gamma, beta, cfg.H, cfg.G, cfg.P, p,
-                    cfg.gn_eps))
-    torch.cuda.synchronize()
+        fam["conv_with_gn_partials"] = [lambda p=p: dpp.dpp_conv3x3_halo_gn(h, part, layer.y1, layer.a1, w, b, cfg.H,
+                                                                            p * layer.R) for p in range(P)]
+        fam["groupnorm_presummed"] = [lambda p=p: dpp.dpp_groupnorm_stale_presummed(
+            layer.y1, layer.stats_next, h, part, layer.stats_prev, gamma, beta, cfg.H, cfg.G, cfg.P, p, cfg.gn_eps)
+            for p in range(P)]
+    times = time_rounds(fam, torch, reps)
     es = 2 if cfg.dtype == "bf16" else 4
     f_conv, f_attn = flops(cfg)
     act = cfg.B * cfg.Nq * cfg.C * es
@@ -528,16 +543,13 @@ def time_kernels(cfg, layer, x_patches, gamma, beta, w, b, eps, rel, eps_c, eps_
         "groupnorm_presummed": (2.0 * act + 2 * 4 * cfg.B * cfg.G * (cfg.P + 1), "GB/s", PEAK_HBM_GBS),
     }
     res = {}
-    for k, lst in ev.items():
-        if not lst:
-            continue
-        t = np.array([a.elapsed_time(b_) for a, b_ in lst])
+    for k, t in times.items():
         ms = float(np.mean(t))
         amount, unit, peak = work[k]
         rate = amount / (ms * 1e-3) / (1e12 if unit == "TFLOP/s" else 1e9)
         res[k] = {"avg_ms": round(ms, 5), "median_ms": round(float(np.median(t)), 5),
                   "p10_ms": round(float(np.percentile(t, 10)), 5), "p90_ms": round(float(np.percentile(t, 90)), 5),
-                  "calls": int(t.size), unit: round(rate, 2), "frac_peak": round(rate / peak, 4), "work": amount}
+                  "rounds": int(t.size), unit: round(rate, 2), "frac_peak": round(rate / peak, 4), "work": amount}
     return res
 
 
@@ -548,7 +560,8 @@ def time_projections(cfg, layer, x_patches, gamma, beta, dpp, torch, reps=10):
     K/V buffer, out = o Wo^T + bo.  Seeded weights (projection_inputs).
     For scale, the same two products through PyTorch's own GEMM
     (torch.nn.functional.linear, hipBLASLt; bf16 bias, fresh contiguous
-    output): a library reference, not part of this path."""
+    output): a library reference, not part of this path.  Back-to-back
+    rounds (time_rounds)."""
     from dpp_synth import projection_inputs
     pi = projection_inputs(cfg)
     dev = "cuda"
@@ -556,7 +569,7 @@ def time_projections(cfg, layer, x_patches, gamma, beta, dpp, torch, reps=10):
     def bf(a):
         return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
 
-    C, M = cfg.C, cfg.Nq
+    C, M, P = cfg.C, cfg.Nq, cfg.P
     wq, wo = bf(pi["w_q"]), bf(pi["w_o"])
     wkv = bf(np.concatenate([pi["w_k"], pi["w_v"]], axis=0))
     bq, bo = torch.from_numpy(pi["b_q"]).to(dev), torch.from_numpy(pi["b_o"]).to(dev)
@@ -566,31 +579,21 @@ def time_projections(cfg, layer, x_patches, gamma, beta, dpp, torch, reps=10):
     q = torch.empty(cfg.B, M, C, dtype=torch.bfloat16, device=dev)
     out = torch.empty_like(q)
     o = layer.o.view(cfg.B, M, C)
-    ev = {k: [] for k in ("linear_q", "linear_kv_into_buffer", "linear_out", "groupnorm_silu",
-                          "library_reference_linear_q", "library_reference_linear_kv")}
     bq16, bkv16 = bq.to(torch.bfloat16), bkv.to(torch.bfloat16)
     xq2 = xq.reshape(cfg.B * M, C)   # 2-D: a plain GEMM, no batched product
-
-    def timed(name, fn):
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        fn()
-        e1.record()
-        ev[name].append((e0, e1))
-
-    host_ahead(torch, reps * 6 * cfg.P)
-    for _ in range(reps):
-        for p in range(cfg.P):
-            t0 = p * M
-            timed("groupnorm_silu", lambda: dpp.dpp_groupnorm_silu_stale(layer.y1, layer.stats_next, x_patches[p],
-                                                                         layer.stats_prev, gamma, beta, cfg.H, cfg.G,
-                                                                         cfg.P, p, cfg.gn_eps, layer.gn_ws))
-            timed("linear_q", lambda: dpp.dpp_linear(q, xq, wq, bq))
-            timed("linear_kv_into_buffer", lambda: dpp.dpp_linear(kv2[:, t0:t0 + M, :], xq, wkv, bkv))
-            timed("linear_out", lambda: dpp.dpp_linear(out, o, wo, bo))
-            timed("library_reference_linear_q", lambda: torch.nn.functional.linear(xq2, wq, bq16))
-            timed("library_reference_linear_kv", lambda: torch.nn.functional.linear(xq2, wkv, bkv16))
-    torch.cuda.synchronize()
+    fam = {
+        "groupnorm_silu": [lambda p=p: dpp.dpp_groupnorm_silu_stale(layer.y1, layer.stats_next, x_patches[p],
+                                                                    layer.stats_prev, gamma, beta, cfg.H, cfg.G,
+                                                                    cfg.P, p, cfg.gn_eps, layer.gn_ws)
+                           for p in range(P)],
+        "linear_q": [lambda: dpp.dpp_linear(q, xq, wq, bq)],
+        "linear_kv_into_buffer": [lambda p=p: dpp.dpp_linear(kv2[:, p * M:(p + 1) * M, :], xq, wkv, bkv)
+                                  for p in range(P)],
+        "linear_out": [lambda: dpp.dpp_linear(out, o, wo, bo)],
+        "library_reference_linear_q": [lambda: torch.nn.functional.linear(xq2, wq, bq16)],
+        "library_reference_linear_kv": [lambda: torch.nn.functional.linear(xq2, wkv, bkv16)],
+    }
+    times = time_rounds(fam, torch, reps)
     act = cfg.B * M * C * 2
     work = {
         "linear_q": (2.0 * cfg.B * M * C * C, "TFLOP/s", PEAK_BF16_TFLOPS),
@@ -601,8 +604,8 @@ def time_projections(cfg, layer, x_patches, gamma, beta, dpp, torch, reps=10):
         "library_reference_linear_kv": (2.0 * cfg.B * M * C * 2 * C, "TFLOP/s", PEAK_BF16_TFLOPS),
     }
     res = {}
-    for k, lst in ev.items():
-        ms = float(np.median([a.elapsed_time(b_) for a, b_ in lst]))
+    for k, t in times.items():
+        ms = float(np.median(t))
         amount, unit, peak = work[k]
         rate = amount / (ms * 1e-3) / (1e12 if unit == "TFLOP/s" else 1e9)
         res[k] = {"median_ms": round(ms, 5), unit: round(rate, 2), "frac_peak": round(rate / peak, 4), "work": amount}
