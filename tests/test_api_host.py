@@ -130,6 +130,8 @@ def test_conv_validation():
     assert conv(Cout=0) == SHAPE
     assert conv(Cin=32) == UNSUP                   # bf16 needs Cin % 64
     assert conv(Cout=24) == UNSUP                  # bf16 needs Cout % 16
+    assert conv(W=1 << 21, Cin=640) == UNSUP       # bf16 image-row byte offsets are 32-bit
+    assert conv(Cin=1 << 18, Cout=512) == UNSUP    # and so are weight byte offsets
     assert conv(x=Bp + 4) == ALIGN
     assert conv(y=Bp) == ALIAS
     assert conv(y=Cp + 256) == ALIAS               # inside the stale image
