@@ -244,9 +244,9 @@ def test_conv_parity_ragged(cfg):
 
 
 @pytest.mark.parametrize("B,H,W,Cin,Cout,r0,R", [
-    (1, 10, 19, 64, 80, 3, 4),     # Cout not a multiple of the 128-channel tile, Cin != Cout
+    (1, 10, 19, 64, 80, 3, 4),     # Cout not a multiple of the 64-channel tile, Cin != Cout, one 4-row tile
     (2, 5, 1, 128, 16, 2, 1),      # one-pixel-wide image, one-row patch, the smallest Cout
-    (1, 4, 33, 192, 272, 0, 4),    # whole image without stale rows, 3 slices, 3 Cout tiles (last 16 wide)
+    (1, 4, 33, 192, 272, 0, 4),    # whole image without stale rows, 3 slices, 5 Cout tiles (last 16 wide)
 ])
 def test_conv_ragged_cout(B, H, W, Cin, Cout, r0, R):
     dpp = _dpp()
