@@ -19,8 +19,7 @@
 // ahead into registers.  Eight waves (two per SIMD) each compute 32 channels
 // x 16*TG pixels of one tile row with v_mfma_f32_16x16x32_bf16; the
 // accumulator's lane layout gives each lane four consecutive output channels
-// of one pixel.  The kernel also has the 2-row x 128-channel tile it had
-// first (same arithmetic, same bits; more weight bytes per step).
+// of one pixel.
 //
 // f32 path: one thread per output element, direct loops (small shapes).
 #include "dpp_common.h"
