@@ -239,12 +239,14 @@ def run(args):
     torch.cuda.synchronize()
 
     # Timed steps carry one event pair per patch, around the attention call.
-    # An event record on this stack leaves the GPU idle for about 6 us (the
-    # next kernel starts that much after it), so more per-call events would
-    # slow the very steps they time: a pair around every kernel costs 1 % of
-    # the 3840 px step and 10 % of the 2048 px one (same-box A/B).  A patch-
-    # layer step is timed from one attention's end to the next's; the conv's
-    # per-call time comes from back-to-back calls after the timed steps.
+    # Events are created without the system-scope fence (FenceFreeEvent):
+    # recording one of torch's events leaves the GPU idle for about 6 us
+    # before the next kernel.  Even so each record costs a little, so a pair
+    # around every kernel would still slow the very steps it times (+0.5 % at
+    # 3840 px, +6 % at 2048 px; the attention pair alone: +0.1 % / +1 %,
+    # same-box A/B).  A patch-layer step is timed from one attention's end to
+    # the next's; the conv's per-call time comes from back-to-back calls after
+    # the timed steps.
     attn_events = []
 
     def step(record=False):
@@ -256,7 +258,7 @@ def run(args):
             dpp.dpp_splice_patch(layer.kv[p], layer.y2, r0)
             kv = layer.kv[p].view(cfg.B, cfg.N, cfg.C)
             if record:
-                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0, e1 = FenceFreeEvent(), FenceFreeEvent()
                 e0.record()
             dpp.dpp_self_attn_displaced(layer.o, layer.y2.view(cfg.B, cfg.Nq, cfg.C), kv, kv, cfg.heads, cfg.D, 0.0,
                                         layer.attn_ws)
@@ -354,9 +356,9 @@ def run(args):
             "traffic_unit": "bytes per call (attention + split merge), FETCH_SIZE + WRITE_SIZE scaled by a plain copy",
             "avg_launch_ms": round(attn_ms, 5),
             "avg_launch_ms_back_to_back": round(attn_b2b_ms, 5),
-            "timing": "HIP events on the launch stream around each attention call inside the timed steps "
-                      "(avg_launch_ms); around every patch's call launched back to back after the timed steps "
-                      "(avg_launch_ms_back_to_back)",
+            "timing": "HIP events (created without the system-scope fence) on the launch stream around each "
+                      "attention call inside the timed steps (avg_launch_ms); around every patch's call launched "
+                      "back to back after the timed steps (avg_launch_ms_back_to_back)",
             "flops_per_launch": f_attn,
         },
     }
@@ -364,8 +366,9 @@ def run(args):
         "kernel": "dpp_conv3x3_halo", "bound": "mfma", "achieved": round(conv_tflops, 2), "peak": PEAK_BF16_TFLOPS,
         "unit": "TFLOP/s", "frac": round(conv_tflops / PEAK_BF16_TFLOPS, 4),
         "avg_launch_ms_back_to_back": round(conv_b2b_ms, 5), "flops_per_launch": f_conv,
-        "timing": "HIP events around every patch's conv call launched back to back after the timed steps (no "
-                  "per-call events inside the timed steps, whose records would slow them)"}
+        "timing": "HIP events (created without the system-scope fence) around every patch's conv call launched "
+                  "back to back after the timed steps (no per-call conv events inside the timed steps: their "
+                  "records would slow them)"}
     out["graph_replay"] = graph
     if block:
         out["attention_block_step"] = block
@@ -396,6 +399,66 @@ def time_graph_step(step, step_flops, torch, steps):
             "steps": steps, "how": "the timed step captured once into a HIP graph, replayed back to back"}
 
 
+class FenceFreeEvent:
+    """A HIP timing event created with hipEventDisableSystemFence, recorded on
+    torch's current stream.  Recording one of torch's events ends with a
+    system-scope release (cache write-back and invalidate) that leaves the GPU
+    idle for about 6 us before the next kernel; this event only takes its
+    timestamp.  Uses the HIP runtime the process has already loaded (torch's),
+    so the library's launches and these events share one runtime."""
+    _hip = None
+    _FLAGS = 0x20000000  # hipEventDisableSystemFence
+
+    @classmethod
+    def _lib(cls):
+        if cls._hip is None:
+            import ctypes
+            with open("/proc/self/maps") as fh:
+                paths = sorted({ln.split()[-1] for ln in fh if "libamdhip64" in ln and ln.split()[-1].startswith("/")})
+            if not paths:
+                raise RuntimeError("the HIP runtime is not loaded in this process")
+            hip = ctypes.CDLL(paths[0])
+            hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+            hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+            hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+            hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+            for f in ("hipEventCreateWithFlags", "hipEventRecord", "hipEventElapsedTime", "hipEventDestroy"):
+                getattr(hip, f).restype = ctypes.c_int
+            cls._hip = hip
+        return cls._hip
+
+    def __init__(self):
+        import ctypes
+        self._ev = ctypes.c_void_p()
+        rc = self._lib().hipEventCreateWithFlags(ctypes.byref(self._ev), self._FLAGS)
+        if rc != 0:
+            raise RuntimeError(f"hipEventCreateWithFlags failed: {rc}")
+
+    def record(self):
+        import torch
+        rc = self._lib().hipEventRecord(self._ev, ctypes_stream(torch.cuda.current_stream().cuda_stream))
+        if rc != 0:
+            raise RuntimeError(f"hipEventRecord failed: {rc}")
+
+    def elapsed_time(self, end):
+        """ms from this event to `end`; both must have completed (synchronise first)."""
+        import ctypes
+        ms = ctypes.c_float()
+        rc = self._lib().hipEventElapsedTime(ctypes.byref(ms), self._ev, end._ev)
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed: {rc}")
+        return ms.value
+
+    def __del__(self):
+        if self._hip is not None and getattr(self, "_ev", None) is not None and self._ev.value:
+            self._hip.hipEventDestroy(self._ev)
+
+
+def ctypes_stream(handle):
+    import ctypes
+    return ctypes.c_void_p(handle)
+
+
 def host_ahead(torch, n_calls):
     """Hold the stream with a bounded spin kernel (about 100 us of shader
     clock per call that follows, well above the host's cost of one binding
@@ -417,7 +480,7 @@ def time_back_to_back(calls, torch, min_calls=50):
     for fn in calls:
         fn()
     host_ahead(torch, rounds * len(calls))
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0, e1 = FenceFreeEvent(), FenceFreeEvent()
     e0.record()
     for _ in range(rounds):
         for fn in calls:
@@ -457,7 +520,7 @@ def time_attention_block(cfg, dpp, torch, reps=3):
     host_ahead(torch, 8 * reps * cfg.P)
     for _ in range(reps):
         for p in range(cfg.P):
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0, e1 = FenceFreeEvent(), FenceFreeEvent()
             e0.record()
             blk.patch_step(p, xp[p], gamma, beta, cw, cb, wq, bq, wkv, bkv, wo, bo)
             e1.record()
@@ -481,7 +544,7 @@ def time_rounds(families, torch, reps=10, min_calls=16):
     between one pair of HIP events on the launch stream, behind a spin that
     lets the host queue them first.  Returns {name: per-call ms of every
     round}.  (A single call between its own event pair would also time the
-    GPU's idle gap after an event record, several us.)"""
+    cost of recording the events.)"""
     out = {}
     for name, calls in families.items():
         n = max(min_calls, len(calls))
@@ -490,7 +553,7 @@ def time_rounds(families, torch, reps=10, min_calls=16):
         host_ahead(torch, reps * n)
         pairs = []
         for _ in range(reps):
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0, e1 = FenceFreeEvent(), FenceFreeEvent()
             e0.record()
             for i in range(n):
                 calls[i % len(calls)]()
@@ -636,7 +699,7 @@ def time_component(dpp, torch, reps=10):
     torch.cuda.synchronize()
     ev = []
     for _ in range(reps):
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0, e1 = FenceFreeEvent(), FenceFreeEvent()
         e0.record()
         chain.step(x, params, synchronous=True)
         e1.record()
@@ -674,7 +737,7 @@ def time_conv_bands(dpp, torch, reps=20):
             call = lambda: dpp.dpp_conv3x3_halo(y, x, st, w, b, H, R, workspace=wsx)
             call()
             torch.cuda.synchronize()
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0, e1 = FenceFreeEvent(), FenceFreeEvent()
             e0.record()
             for _ in range(reps):
                 call()
@@ -707,7 +770,7 @@ def hbm_sweep(cfg, dpp, torch, reps=20):
         # one untimed call on the last set (reached again only after all others)
         calls[-1]()
         torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0, e1 = FenceFreeEvent(), FenceFreeEvent()
         e0.record()
         for i in range(reps):
             calls[i % len(calls)]()
