@@ -453,11 +453,12 @@ struct ConvSplit {
 // slices each, a slice-round being about 3.2 us on MI355X.  A split adds its
 // float32 partials, written and read back by the reduction (counted at
 // 5 TB/s, 16 MB per slice-round), and one slice-round for the reduction's
-// launch.  Gains under 10% go to fewer splits.  The model picks the measured
-// fastest split count at every shape of a forced-split sweep (B = 1-2,
-// 8-240 rows, 64-240 px wide, 320 and 640 channels): 3840 px 8-patch band,
-// 225 workgroups -> no split; 16-patch band, 120 -> 2 (60 -> 47 us); 1024 px
-// 8-patch band, 20 -> 10 (54 -> 29 us); full images never split.
+// launch.  Gains under 10% go to fewer splits.  In a forced-split sweep on
+// MI355X (seven bands of 8-240 rows, 64-240 px wide, 320 and 640 channels)
+// the model picks the measured fastest count at six shapes and one within 4 %:
+// 240 x 240 image, 30-row band, 240 workgroups -> no split; 15-row band, 120
+// -> 2 (42 -> 35 us); 64 x 64 image, 8-row band, 20 -> 10 (36 -> 19 us;
+// 5 splits: 18 us); full images never split.
 static ConvSplit conv_split(int64_t B, int64_t rows, int64_t W, int64_t Cin, int64_t Cout) {
   constexpr double kSliceRoundBytes = 16e6;
   const int64_t wgs = conv_tiles(rows, W, Cout) * B;
