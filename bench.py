@@ -41,6 +41,9 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_sdxl_3840_traffic.md")
 ATTN_SOURCES = ("displaced_patch_parallelism_net_amd/csrc/k_attn.hip",
                 "displaced_patch_parallelism_net_amd/csrc/dpp_common.h")
+CONV_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "conv_sdxl_3840_traffic.md")
+CONV_SOURCES = ("displaced_patch_parallelism_net_amd/csrc/k_conv.hip",
+                "displaced_patch_parallelism_net_amd/csrc/dpp_common.h")
 
 
 def parse():
@@ -60,19 +63,28 @@ def parse():
     return ap.parse_args()
 
 
-def attn_source_hash():
+def source_hash(sources):
     h = hashlib.sha256()
-    for f in ATTN_SOURCES:
+    for f in sources:
         with open(os.path.join(ROOT, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()
 
 
-def measured_traffic(workload):
-    """HBM bytes per attention call from the recorded counter summary, or
-    None when there is none for this workload or the kernel changed since."""
+def attn_source_hash():
+    return source_hash(ATTN_SOURCES)
+
+
+def conv_source_hash():
+    return source_hash(CONV_SOURCES)
+
+
+def measured_traffic(workload, path=TRAFFIC_FILE, sources=ATTN_SOURCES):
+    """HBM bytes per call from a recorded counter summary (the attention's
+    by default), or None when there is none for this workload or the
+    kernel's sources changed since."""
     try:
-        with open(TRAFFIC_FILE) as fh:
+        with open(path) as fh:
             text = fh.read()
     except OSError:
         return None
@@ -80,7 +92,7 @@ def measured_traffic(workload):
     if not m:
         return None
     rec = json.loads(m.group(1))
-    if rec.get("workload") != workload or rec.get("kernel_source_sha256") != attn_source_hash():
+    if rec.get("workload") != workload or rec.get("kernel_source_sha256") != source_hash(sources):
         return None
     return rec.get("traffic_bytes_per_call")
 
@@ -366,6 +378,8 @@ def run(args):
         "kernel": "dpp_conv3x3_halo", "bound": "mfma", "achieved": round(conv_tflops, 2), "peak": PEAK_BF16_TFLOPS,
         "unit": "TFLOP/s", "frac": round(conv_tflops / PEAK_BF16_TFLOPS, 4),
         "avg_launch_ms_back_to_back": round(conv_b2b_ms, 5), "flops_per_launch": f_conv,
+        "traffic": measured_traffic(cfg.name, CONV_TRAFFIC_FILE, CONV_SOURCES),
+        "traffic_unit": "bytes per call, FETCH_SIZE + WRITE_SIZE scaled by a plain copy",
         "timing": "HIP events (created without the system-scope fence) around every patch's conv call launched "
                   "back to back after the timed steps (no per-call conv events inside the timed steps: their "
                   "records would slow them)"}
