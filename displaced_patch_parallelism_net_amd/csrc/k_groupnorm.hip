@@ -5,20 +5,22 @@
 // raw sums (sum x, sum x^2) from the previous step plus the own patch's fresh
 // sums (DistriFusion reading notes, Introduction, fourth paragraph).
 //
-// Three launches, deterministic (no atomics):
+// Two launches, deterministic (no atomics):
 //   1. partial: workgroup (chunk, b) sums its pixels per channel in float32
 //      registers (each thread owns one 16-byte channel vector and walks
 //      pixels, eight loads in flight), folds channels into groups through
 //      LDS in a fixed order and writes one (s1, s2) per group to the
 //      workspace;
-//   2. stats: the chunk partials of each group added in float64 in a fixed
-//      order, the fresh sums written to stats_out[b, p];
-//   3. apply: every workgroup forms mean/rstd of each group from the fresh
-//      and the other patches' stale sums in LDS and streams
+//   2. apply: a workgroup owns 64 channels of batch entry b; it adds the
+//      chunk partials of the few groups those channels touch in float64 in
+//      a fixed order (the fresh sums, stored to stats_out[b, p]), forms
+//      mean/rstd from them and the other patches' stale sums, and streams
 //      y = x * a_c + b_c (then SiLU when asked).
-// The second read of x (step 3) normally hits the 256 MB last-level cache.
+// The second read of x (step 2) normally hits the 256 MB last-level cache.
 // When the kernel that wrote x also wrote its group partial sums (the conv
-// and projection epilogues), step 1 is skipped and x is read once.
+// and projection epilogues), step 1 is skipped and x is read once, in one
+// launch.  The statistics-only call (no y) runs the float64 sums as a
+// kernel of its own (gn_stats_kernel): the same order, the same bits.
 #include <mutex>
 
 #include "dpp_common.h"
@@ -173,13 +175,14 @@ __global__ __launch_bounds__(kGnMaxThreads) void gn_partial_kernel(const T* __re
 }
 
 // Fresh group sums of a patch from its chunk partials, in one fixed order: a
-// set of 16 lanes handles one (b, g); lane j adds the chunk partials j,
-// j + 16, j + 32, ... in float64 in increasing order (batches of kGnFinLoads
-// loads issued before any is used; chunks past the end read as zero, which
-// leaves the sums unchanged), and a 16-lane xor butterfly (offsets 8, 4, 2,
-// 1) joins the lanes, every lane ending with the same sums.
-constexpr int kGnFinLoads = 16;
-constexpr int kGnSet = 16;
+// wave handles one (b, g); lane j adds the chunk partials j, j + 64,
+// j + 128, ... in float64 in increasing order (batches of kGnFinLoads loads
+// issued before any is used; chunks past the end read as zero, which leaves
+// the sums unchanged), and a 64-lane xor butterfly (offsets 32, 16, ..., 1)
+// joins the lanes, every lane ending with the same sums.  The apply kernel
+// forms the same sums in the same order.
+constexpr int kGnFinLoads = 4;
+constexpr int kGnSet = 64;
 
 __device__ __forceinline__ double2 gn_fresh_sums(const float* __restrict__ partial, int64_t nchunk, int G, int b,
                                                  int g, int j) {
@@ -204,13 +207,13 @@ __device__ __forceinline__ double2 gn_fresh_sums(const float* __restrict__ parti
 }
 
 // The fresh sums of every group to stats_out[b, p] (the next step's stale
-// sums; alone, the first half of the synchronous step): four groups per
-// 64-lane workgroup.
+// sums; alone, the first half of the synchronous step): one group per
+// 64-lane workgroup.  Only the statistics-only call runs it.
 __global__ __launch_bounds__(kWave) void gn_stats_kernel(const float* __restrict__ partial, int64_t nchunk,
                                                          float* __restrict__ stats_out, int G, int P, int p) {
   const int b = blockIdx.y;
   const int g = blockIdx.x * (kWave / kGnSet) + threadIdx.x / kGnSet, j = threadIdx.x % kGnSet;
-  if (g >= G) return;  // uniform within each 16-lane set
+  if (g >= G) return;  // uniform within each lane set
   const double2 r = gn_fresh_sums(partial, nchunk, G, b, g, j);
   if (j == 0) {
     float* so = stats_out + ((static_cast<int64_t>(b) * P + p) * G + g) * 2;
@@ -225,36 +228,58 @@ __device__ __forceinline__ float silu_f(float z) {
   return z * __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-1.4426950408889634f * z));
 }
 
-// Apply.  Each workgroup first issues its first batch of x loads, then forms
-// the mean/rstd of every group of its batch entry in LDS: the group total is
-// the sum over patches q in increasing order, in float64, of the fresh sums
-// stats[b, p] (written by gn_stats_kernel just before) for q == p and the
-// stale sums for q != p -- the same order in every workgroup.  Then it
-// streams y = x * a_c + b_c (a_c = rstd_g gamma_c, b_c = beta_c - mean_g a_c;
-// then SiLU when asked: the GroupNorm + SiLU pair opening an SDXL residual
-// block) with streaming 16-byte loads and stores.  Pixels go in grid-stride
-// order: workgroup w takes pixels w*KP .. w*KP+KP-1 of every group of
-// gridDim.x*KP consecutive pixels, so the workgroups in flight stream one
-// contiguous window of x and y (measured faster than separate ranges when x
-// comes from HBM).
+// Apply, with the fresh sums formed in the same launch.  A workgroup owns a
+// tile of 64 channels (blockIdx.y) of batch entry b (blockIdx.z) and walks
+// pixels; it needs the statistics of only the few groups its channels
+// touch.  It first issues its first batch of x loads, then
+//  1. adds the chunk partials of those groups into their fresh sums, bit for
+//     bit as gn_stats_kernel does (task (j, g) adds chunks j, j+64, ... in
+//     float64 in increasing order, as gn_fresh_sums' lane j; the 64 lane sums
+//     are then added in the order of its xor butterfly, one LDS stage per
+//     offset 32, 16, ..., 1), rounded to float32 as stored; the workgroups of
+//     pixel block 0 store them to stats_out[b, p] (each group by the tile
+//     holding its first channel);
+//  2. forms each group's total over patches q in increasing order, in
+//     float64, from those fresh sums for q == p and the stale sums for
+//     q != p, and the mean/rstd from it -- the same values in every
+//     workgroup;
+//  3. streams y = x * a_c + b_c (a_c = rstd_g gamma_c, b_c = beta_c - mean_g
+//     a_c; then SiLU when asked: the GroupNorm + SiLU pair opening an SDXL
+//     residual block) with streaming 16-byte loads and stores.  Each wave
+//     access covers whole 128-byte runs of eight pixels.  Pixels go in
+//     grid-stride order: workgroup w takes pixels w*KP .. w*KP+KP-1 of every
+//     run of gridDim.x*KP consecutive pixels, so the workgroups in flight
+//     stream one window of x and y.
 constexpr int kGnApplyThreads = 256;
-constexpr int kGnApplyWgs = 2048;     // total apply workgroups over B
+constexpr int kGnApplyWgs = 2048;     // total apply workgroups over B and the channel tiles
 constexpr int kGnApplyInFlight = 8;   // 16-byte loads in flight per thread
-constexpr int kGnStage = 1024;        // (group, patch) sums staged in LDS per pass
+constexpr int kGnCt = 64;             // channels per workgroup tile
+constexpr int kGnCtMaxGroups = kGnCt + 1;  // groups a 64-channel tile can touch
+constexpr int kGnFreshBlock = 4;      // groups per fresh-sum block (LDS scratch 64 x 4 double2)
+constexpr int kGnQb = 16;             // patches staged per pass
 
 template <typename T, bool SILU>
 __global__ __launch_bounds__(kGnApplyThreads) void gn_apply_kernel(
-    const T* __restrict__ x, T* __restrict__ y, const float* __restrict__ stats, const float* __restrict__ stale,
-    const float* __restrict__ gamma, const float* __restrict__ beta, int64_t npix, int C, int G, int V, int KP, int P,
-    int p, double n, float eps) {
+    const T* __restrict__ x, T* __restrict__ y, const float* __restrict__ partial, int64_t nchunk,
+    float* __restrict__ stats_out, const float* __restrict__ stale, const float* __restrict__ gamma,
+    const float* __restrict__ beta, int64_t npix, int C, int G, int P, int p, double n, float eps) {
   constexpr int VEC = Elem<T>::kVec;
-  __shared__ float2 stage[kGnStage];
-  __shared__ double2 tot[256];
-  __shared__ float2 coef[256];
-  const int b = blockIdx.y;
+  constexpr int VT = kGnCt / VEC;           // vectors per pixel of the tile
+  constexpr int KP = kGnApplyThreads / VT;  // pixels per pass
+  __shared__ double2 red[kGnSet * kGnFreshBlock];
+  __shared__ float2 fresh[kGnCtMaxGroups];
+  __shared__ float2 gstat[kGnCtMaxGroups];  // (mean, rstd) per group of the tile
+  __shared__ double2 tot[kGnCtMaxGroups];
+  __shared__ float2 stage[kGnQb * kGnCtMaxGroups];
+  const int b = blockIdx.z;
   const int t = threadIdx.x, nt = blockDim.x;
-  const int v = t % V, k = t / V;
-  const bool active = k < KP;
+  const int v = t % VT, k = t / VT;
+  const int c0 = blockIdx.y * kGnCt;
+  const int cg = C / G;
+  const int g_lo = c0 / cg, g_hi = (min(c0 + kGnCt, C) - 1) / cg, ng = g_hi - g_lo + 1;
+  const int V = C / VEC;                    // vectors per pixel
+  const int vi = c0 / VEC + v;              // this thread's vector within a pixel
+  const bool active = k < KP && vi < V;
   const int64_t off = static_cast<int64_t>(b) * npix * V;
   const uint4* xv = reinterpret_cast<const uint4*>(x) + off;
   uint4* yv = reinterpret_cast<uint4*>(y) + off;
@@ -267,49 +292,88 @@ __global__ __launch_bounds__(kGnApplyThreads) void gn_apply_kernel(
   if (active) {
 #pragma unroll
     for (int q = 0; q < kGnApplyInFlight; ++q)
-      if (pix + q * step < npix) u[q] = ld_stream(xv + (pix + q * step) * V + v);
+      if (pix + q * step < npix) u[q] = ld_stream(xv + (pix + q * step) * V + vi);
 #pragma unroll
     for (int e = 0; e < VEC; ++e) {
-      gm[e] = gamma[v * VEC + e];
-      bt[e] = beta[v * VEC + e];
+      gm[e] = gamma[vi * VEC + e];
+      bt[e] = beta[vi * VEC + e];
     }
   }
-  for (int g = t; g < G; g += nt) tot[g] = make_double2(0.0, 0.0);
-  const int qb = kGnStage / G > 1 ? kGnStage / G : 1;  // patches per pass (G <= 256 <= kGnStage)
-  for (int q0 = 0; q0 < P; q0 += qb) {
-    const int nq = P - q0 < qb ? P - q0 : qb;
-    for (int i = t; i < G * nq; i += nt) {
-      const int g = i / nq, q = q0 + i % nq;
-      stage[i] = *reinterpret_cast<const float2*>((q == p ? stats : stale) +
-                                                  ((static_cast<int64_t>(b) * P + q) * G + g) * 2);
-    }
-    __syncthreads();
-    for (int g = t; g < G; g += nt) {
-      double2 a = tot[g];
-      for (int i = 0; i < nq; ++i) {
-        a.x += stage[g * nq + i].x;
-        a.y += stage[g * nq + i].y;
+  // 1. fresh sums of groups g_lo .. g_hi
+  const float* pbase = partial + static_cast<int64_t>(b) * nchunk * G * 2;
+  for (int h0 = 0; h0 < ng; h0 += kGnFreshBlock) {
+    const int gb = ng - h0 < kGnFreshBlock ? ng - h0 : kGnFreshBlock;
+    for (int q = t; q < kGnSet * gb; q += nt) {
+      const int j = q / gb, h = q % gb, g = g_lo + h0 + h;
+      double a = 0.0, c = 0.0;
+      for (int64_t ch = j; ch < nchunk; ch += kGnFinLoads * kGnSet) {
+        float2 pv[kGnFinLoads];
+#pragma unroll
+        for (int i = 0; i < kGnFinLoads; ++i) {
+          const int64_t ci = ch + i * kGnSet;
+          pv[i] = ci < nchunk ? *reinterpret_cast<const float2*>(pbase + (ci * G + g) * 2) : make_float2(0.f, 0.f);
+        }
+#pragma unroll
+        for (int i = 0; i < kGnFinLoads; ++i) { a += pv[i].x; c += pv[i].y; }
       }
-      tot[g] = a;
+      red[j * kGnFreshBlock + h] = make_double2(a, c);
+    }
+    for (int o = kGnSet / 2; o > 0; o >>= 1) {
+      __syncthreads();
+      for (int q = t; q < o * gb; q += nt) {
+        const int j = q / gb, h = q % gb;
+        const double2 r0 = red[j * kGnFreshBlock + h], r1 = red[(j + o) * kGnFreshBlock + h];
+        red[j * kGnFreshBlock + h] = make_double2(r0.x + r1.x, r0.y + r1.y);
+      }
+    }
+    __syncthreads();
+    for (int h = t; h < gb; h += nt)
+      fresh[h0 + h] = make_float2(static_cast<float>(red[h].x), static_cast<float>(red[h].y));
+    __syncthreads();
+  }
+  // 2. totals over the patches, mean and rstd; pixel block 0 stores the fresh
+  // sums.  The stale sums are staged in LDS by all threads, kGnQb patches
+  // per pass, then added per group in patch order.
+  for (int h = t; h < ng; h += nt) {
+    const int g = g_lo + h;
+    if (blockIdx.x == 0 && g * cg >= c0)
+      *reinterpret_cast<float2*>(stats_out + ((static_cast<int64_t>(b) * P + p) * G + g) * 2) = fresh[h];
+    tot[h] = make_double2(0.0, 0.0);
+  }
+  for (int q0 = 0; q0 < P; q0 += kGnQb) {
+    const int nq = P - q0 < kGnQb ? P - q0 : kGnQb;
+    for (int i = t; i < nq * ng; i += nt) {
+      const int q = q0 + i / ng, h = i % ng;
+      stage[i] = q == p ? fresh[h]
+                        : *reinterpret_cast<const float2*>(stale + ((static_cast<int64_t>(b) * P + q) * G + g_lo + h) * 2);
+    }
+    __syncthreads();
+    for (int h = t; h < ng; h += nt) {
+      double2 a = tot[h];
+      for (int i = 0; i < nq; ++i) {
+        a.x += stage[i * ng + h].x;
+        a.y += stage[i * ng + h].y;
+      }
+      tot[h] = a;
     }
     __syncthreads();
   }
-  for (int g = t; g < G; g += nt) {
-    const double mean = tot[g].x / n;
-    double var = tot[g].y / n - mean * mean;
+  for (int h = t; h < ng; h += nt) {
+    const double mean = tot[h].x / n;
+    double var = tot[h].y / n - mean * mean;
     if (var < 0.0) var = 0.0;
-    coef[g] = make_float2(static_cast<float>(mean), static_cast<float>(1.0 / sqrt(var + static_cast<double>(eps))));
+    gstat[h] = make_float2(static_cast<float>(mean), static_cast<float>(1.0 / sqrt(var + static_cast<double>(eps))));
   }
   __syncthreads();
   if (!active) return;
-  const int cg = C / G;
   float ac[VEC], sh[VEC];
 #pragma unroll
   for (int e = 0; e < VEC; ++e) {
-    const float2 mr = coef[(v * VEC + e) / cg];
+    const float2 mr = gstat[(vi * VEC + e) / cg - g_lo];
     ac[e] = mr.y * gm[e];
     sh[e] = fmaf(-mr.x, ac[e], bt[e]);
   }
+  // 3. stream
   for (;;) {
 #pragma unroll
     for (int q = 0; q < kGnApplyInFlight; ++q) {
@@ -322,45 +386,47 @@ __global__ __launch_bounds__(kGnApplyThreads) void gn_apply_kernel(
           f[e] = fmaf(f[e], ac[e], sh[e]);
           if (SILU) f[e] = silu_f(f[e]);
         }
-        st_stream(yv + pq * V + v, Elem<T>::pack(f));
+        st_stream(yv + pq * V + vi, Elem<T>::pack(f));
       }
     }
     pix += kGnApplyInFlight * step;
     if (pix >= npix) break;
 #pragma unroll
     for (int q = 0; q < kGnApplyInFlight; ++q)
-      if (pix + q * step < npix) u[q] = ld_stream(xv + (pix + q * step) * V + v);
+      if (pix + q * step < npix) u[q] = ld_stream(xv + (pix + q * step) * V + vi);
   }
 }
 
-// The fresh sums to stats_out[b, p], then (y != NULL) the apply.
+// y == NULL: the fresh sums to stats_out[b, p] (gn_stats_kernel).  Else the
+// apply, which forms the same sums itself and stores them.
 template <typename T>
 static hipError_t gn_finish(T* y, float* stats_out, const T* x, const float* partial, int64_t nchunk,
                             const float* stale, const float* gamma, const float* beta, int64_t B, int64_t H, int64_t W,
                             int64_t C, int64_t G, int64_t P, int64_t p, int64_t rows, float eps, bool silu,
                             hipStream_t s) {
-  hipLaunchKernelGGL(gn_stats_kernel, dim3(static_cast<unsigned>(ceil_div(G, kWave / kGnSet)),
-                                           static_cast<unsigned>(B)),
-                     dim3(kWave), 0, s, partial, nchunk, stats_out, static_cast<int>(G), static_cast<int>(P),
-                     static_cast<int>(p));
-  hipError_t err = hipGetLastError();
-  if (err != hipSuccess || y == nullptr) return err;
-  const int V = static_cast<int>(C / Elem<T>::kVec);
-  const int KP = kGnApplyThreads / V;
+  if (y == nullptr) {
+    hipLaunchKernelGGL(gn_stats_kernel, dim3(static_cast<unsigned>(ceil_div(G, kWave / kGnSet)),
+                                             static_cast<unsigned>(B)),
+                       dim3(kWave), 0, s, partial, nchunk, stats_out, static_cast<int>(G), static_cast<int>(P),
+                       static_cast<int>(p));
+    return hipGetLastError();
+  }
+  constexpr int KP = kGnApplyThreads / (kGnCt / Elem<T>::kVec);
   const int64_t npix = rows * W;
-  int64_t nwg = ceil_div(kGnApplyWgs, B);
+  const int64_t nct = ceil_div(C, kGnCt);
+  int64_t npb = ceil_div(kGnApplyWgs, B * nct);
   const int64_t full = ceil_div(npix, static_cast<int64_t>(KP) * kGnApplyInFlight);  // one full batch per thread
-  if (nwg > full) nwg = full;
+  if (npb > full) npb = full;
   const double n = static_cast<double>(H) * static_cast<double>(W) * static_cast<double>(C / G);
-  const dim3 grid(static_cast<unsigned>(nwg), static_cast<unsigned>(B));
+  const dim3 grid(static_cast<unsigned>(npb), static_cast<unsigned>(nct), static_cast<unsigned>(B));
   if (silu)
-    hipLaunchKernelGGL((gn_apply_kernel<T, true>), grid, dim3(KP * V), 0, s, x, y, stats_out, stale, gamma, beta, npix,
-                       static_cast<int>(C), static_cast<int>(G), V, KP, static_cast<int>(P), static_cast<int>(p), n,
-                       eps);
+    hipLaunchKernelGGL((gn_apply_kernel<T, true>), grid, dim3(kGnApplyThreads), 0, s, x, y, partial, nchunk,
+                       stats_out, stale, gamma, beta, npix, static_cast<int>(C), static_cast<int>(G),
+                       static_cast<int>(P), static_cast<int>(p), n, eps);
   else
-    hipLaunchKernelGGL((gn_apply_kernel<T, false>), grid, dim3(KP * V), 0, s, x, y, stats_out, stale, gamma, beta, npix,
-                       static_cast<int>(C), static_cast<int>(G), V, KP, static_cast<int>(P), static_cast<int>(p), n,
-                       eps);
+    hipLaunchKernelGGL((gn_apply_kernel<T, false>), grid, dim3(kGnApplyThreads), 0, s, x, y, partial, nchunk,
+                       stats_out, stale, gamma, beta, npix, static_cast<int>(C), static_cast<int>(G),
+                       static_cast<int>(P), static_cast<int>(p), n, eps);
   return hipGetLastError();
 }
 
