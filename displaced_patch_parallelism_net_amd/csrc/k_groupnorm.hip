@@ -251,7 +251,7 @@ __device__ __forceinline__ float silu_f(float z) {
 //     run of gridDim.x*KP consecutive pixels, so the workgroups in flight
 //     stream one window of x and y.
 constexpr int kGnApplyThreads = 256;
-constexpr int kGnApplyWgs = 2048;     // total apply workgroups over B and the channel tiles
+constexpr int kGnApplyWgs = 2560;     // total apply workgroups over B and the channel tiles
 constexpr int kGnApplyInFlight = 8;   // 16-byte loads in flight per thread
 constexpr int kGnCt = 64;             // channels per workgroup tile
 constexpr int kGnCtMaxGroups = kGnCt + 1;  // groups a 64-channel tile can touch
