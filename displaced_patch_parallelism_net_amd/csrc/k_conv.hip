@@ -118,6 +118,92 @@ struct ConvArgs {
 // keyed by its column, which within one ring row is the same spread).
 __device__ __forceinline__ int swz(int row, int slot) { return row * 8 + (slot ^ (row & 7)); }
 
+// Epilogue of the bf16 conv kernels.  Lane (kg = lane / 16, pl = lane % 16)
+// of the wave owning tile row `row` and channels [m0 + cw0, m0 + cw0 + 32)
+// holds, in acc[i][j], channels m0 + cw0 + 16 i + 4 kg + 0..3 of pixel column
+// pc0 + 16 j + pl.  Split-K: the float32 partials go straight to a.part (the
+// bias is added by the reduction).  Otherwise the bias is added and the
+// result rounded in registers, the TR x 16 TG pixel x 64 channel tile is
+// staged in LDS at `tile` ([pixel][channel]; pixels padded by 16 bytes, so
+// that the 16 pixels of a tile write fall on distinct banks), then stored so
+// that each wave store writes whole 128-byte pixels instead of 32-byte pieces
+// of 16 pixels; with a.gn_part the tile's GroupNorm partial sums follow, the
+// LDS past the staged tile being their scratch.
+constexpr int kConvPixU2 = kConvBM / 4 + 2;  // uint2 per padded LDS pixel
+
+template <int TR, int TG, int NT>
+constexpr size_t conv_epilogue_bytes() {
+  return static_cast<size_t>(TR * 16 * TG * kConvPixU2) * 8 + 4 * tile_group_sums_scratch_floats<NT, kConvBM>();
+}
+
+template <int TR, int TG, int NT>
+__device__ __forceinline__ void conv_epilogue(const ConvArgs& a, const f32x4 (&acc)[kConvCG][TG], uint2* tile, int b,
+                                              int split, int m0, int row, int pc0, int cw0, int pr0) {
+  constexpr int TC = 16 * TG;
+  constexpr int kTileU2 = TR * TC * kConvPixU2;
+  const int tid = threadIdx.x, lane = tid % kWave;
+  const int kg = lane >> 4, pl = lane & 15;
+  const int W = a.W;
+  if (a.part != nullptr) {  // split-K: float32 partials, bias added by the reduction
+    if (row < a.rows) {
+      const int64_t nb = gridDim.z / a.nsplit;
+#pragma unroll
+      for (int j = 0; j < TG; ++j) {
+        const int col = pc0 + j * 16 + pl;
+        if (col >= W) continue;
+        float* pp = a.part + (((static_cast<int64_t>(split) * nb + b) * a.rows + row) * W + col) * a.Cout;
+#pragma unroll
+        for (int i = 0; i < kConvCG; ++i) {
+          const int m = m0 + cw0 + i * 16 + 4 * kg;
+          if (m < a.Cout) *reinterpret_cast<f32x4*>(pp + m) = acc[i][j];
+        }
+      }
+    }
+    return;  // uniform over the workgroup: no barrier follows
+  }
+  const int trow = row - pr0;  // tile row
+#pragma unroll
+  for (int i = 0; i < kConvCG; ++i) {
+    const int c = cw0 + i * 16 + 4 * kg;
+    const int m = m0 + c;
+    float bv[4] = {0.f, 0.f, 0.f, 0.f};
+    if (a.bias && m < a.Cout) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) bv[e] = a.bias[m + e];
+    }
+#pragma unroll
+    for (int j = 0; j < TG; ++j) {
+      uint2 out;
+      out.x = pack_bf16x2(acc[i][j][0] + bv[0], acc[i][j][1] + bv[1]);
+      out.y = pack_bf16x2(acc[i][j][2] + bv[2], acc[i][j][3] + bv[3]);
+      tile[(trow * TC + j * 16 + pl) * kConvPixU2 + c / 4] = out;
+    }
+  }
+  __syncthreads();
+  constexpr int kChunks = TR * TC * (kConvBM / 4);  // 8-byte chunks of the tile
+  static_assert(kChunks % NT == 0, "whole chunks per thread");
+#pragma unroll
+  for (int u = 0; u < kChunks / NT; ++u) {
+    const int id = tid + u * NT;
+    const int pix = id / (kConvBM / 4), q = id % (kConvBM / 4);
+    const int r = pr0 + pix / TC, col = pc0 + pix % TC, m = m0 + 4 * q;
+    if (r < a.rows && col < W && m < a.Cout)
+      *reinterpret_cast<uint2*>(a.y + ((static_cast<int64_t>(b) * a.rows + r) * W + col) * a.Cout + m) =
+          tile[pix * kConvPixU2 + q];
+  }
+  if (a.gn_part != nullptr) {
+    // GroupNorm partial sums of this tile's stored values, one chunk per
+    // workgroup (chunk = channel tile * pixel tiles + pixel tile)
+    const int64_t nchunk = static_cast<int64_t>(gridDim.x) * gridDim.y;
+    const int64_t chunk = static_cast<int64_t>(blockIdx.y) * gridDim.x + blockIdx.x;
+    float* out = a.gn_part + (static_cast<int64_t>(b) * nchunk + chunk) * a.G * 2;
+    tile_group_sums<NT, TR * TC, kConvBM>(
+        reinterpret_cast<const uint16_t*>(tile), 4 * kConvPixU2,
+        [&](int p) { return pr0 + p / TC < a.rows && pc0 + p % TC < W; }, m0, a.Cout, a.Cout / a.G, a.G,
+        reinterpret_cast<float*>(tile + kTileU2), out);
+  }
+}
+
 template <int TG>
 __global__ __launch_bounds__(kConvThreads, 1) void conv3x3_bf16_mfma_kernel(ConvArgs a) {
   constexpr int TC = 16 * TG;                   // output columns per tile
@@ -330,79 +416,236 @@ __global__ __launch_bounds__(kConvThreads, 1) void conv3x3_bf16_mfma_kernel(Conv
   }
   if (slice < nslices) slice_steps(slice, w_regA, w_regB, 0, band_ra, band_rb);
 
-  // -------- epilogue: lane holds channels m0 + wn*CW + i*16 + 4*(lane/16) + 0..3 of one pixel
-  const int r = pr0 + wr;
-  if (a.part != nullptr) {  // split-K: float32 partials, bias added by the reduction
-    if (r < a.rows) {
-      const int64_t nb = gridDim.z / a.nsplit;
-#pragma unroll
-      for (int j = 0; j < TG; ++j) {
-        const int col = pc0 + j * 16 + pl;
-        if (col >= W) continue;
-        float* pp = a.part + (((static_cast<int64_t>(split) * nb + b) * a.rows + r) * W + col) * a.Cout;
-#pragma unroll
-        for (int i = 0; i < kConvCG; ++i) {
-          const int m = m0 + wn * kConvCW + i * 16 + 4 * kg;
-          if (m < a.Cout) *reinterpret_cast<f32x4*>(pp + m) = acc[i][j];
-        }
-      }
-    }
-    return;  // uniform over the workgroup: no barrier follows
-  }
-  // bf16 output: bias added and rounded in registers, the tile (4 rows x TC
-  // pixels x 64 channels) staged in LDS ([pixel][channel]; pixels padded by
-  // 16 bytes, so that the 16 pixels of a tile write fall on distinct banks),
-  // then stored so that each wave store writes four whole 128-byte pixels
-  // instead of 32-byte pieces of 16 pixels.  The slice loop ended with a
-  // barrier, so the band and weight buffers are free; the tile (and the
-  // statistics scratch) goes into the larger of the two.
-  constexpr int kPixU2 = kConvBM / 4 + 2;  // uint2 per padded LDS pixel
-  constexpr int kTileU2 = kConvTR * TC * kPixU2;
-  constexpr size_t kEpiBytes = kTileU2 * 8 + 4 * tile_group_sums_scratch_floats<kConvThreads, kConvBM>();
+  // -------- epilogue (the slice loop ended with a barrier: the band and
+  // weight buffers are free; the staged tile and the statistics scratch go
+  // into the larger of the two)
   constexpr bool kTileInBand = sizeof(band) >= sizeof(wts);
-  static_assert(kEpiBytes <= (kTileInBand ? sizeof(band) : sizeof(wts)), "staged tile and statistics scratch fit");
+  static_assert(conv_epilogue_bytes<kConvTR, TG, kConvThreads>() <= (kTileInBand ? sizeof(band) : sizeof(wts)),
+                "staged tile and statistics scratch fit");
   uint2* const tile = kTileInBand ? reinterpret_cast<uint2*>(&band[0]) : reinterpret_cast<uint2*>(&wts[0][0][0]);
+  conv_epilogue<kConvTR, TG, kConvThreads>(a, acc, tile, b, split, m0, pr0 + wr, pc0, wn * kConvCW, pr0);
+}
+
+// Six-row tile: 6 patch rows x 16*TG columns x 64 output channels, twelve
+// waves (three per SIMD), wave (wr, wn) owning tile row wr and channels
+// [32 wn, 32 wn + 32): TG x 2 accumulator tiles.  Chosen where it covers the
+// band exactly (rows a multiple of 6, width a multiple of 48, TG = 3): the
+// 30-row x 240-column band is 5 x 5 x 10 = 250 workgroups of 288 pixels
+// instead of 240 of 320 (the last four-row tile half empty), and three waves
+// per SIMD hide more of the LDS and barrier latency than two.
+//
+// Same K loop as the four-row kernel (one barrier step per 64-channel slice
+// and kernel row; weights double-buffered in LDS, fetched two steps ahead),
+// but the slice's halo band is 8 rows: the band is double-buffered (two
+// halves of 8 LDS rows, slice s in half s & 1), and slice s+1's band is
+// staged during slice s in three pieces -- rows 0-2, 3-5 and 6-7, one per
+// step dy -- each fetched into registers two steps before it is stored.
+// Waves 4k .. 4k+3 load and store row k of a piece; the last piece has two
+// rows, so waves 8-11 skip it.
+constexpr int kConv6TR = 6;
+constexpr int kConv6Threads = 768;  // 12 waves: 6 rows x 2 channel halves
+constexpr int kConv6Half = 8;       // band rows per slice
+
+template <int TG>
+__global__ __launch_bounds__(kConv6Threads, 1) void conv3x3_bf16_mfma6_kernel(ConvArgs a) {
+  constexpr int TC = 16 * TG;                      // output columns per tile
+  constexpr int BW = TC + 2;                       // band columns
+  constexpr int ROW_VEC = BW * 8;                  // 16-byte vectors in one band row
+  constexpr int RB_ITERS = (ROW_VEC + 255) / 256;  // per lane, four waves per row
+  constexpr int W_VEC = 3 * kConvBM * 8;           // weight vectors of one step (3 taps)
+  constexpr int W_ITERS = W_VEC / kConv6Threads;
+  static_assert(W_VEC % kConv6Threads == 0, "whole weight vectors per thread");
+
+  __shared__ uint4 band[2 * kConv6Half * ROW_VEC];
+  __shared__ uint4 wts[2][3][kConvBM * 8];
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave), lane = tid % kWave;
+  const int wr = wave / kConvWN, wn = wave % kConvWN;
+  const int b = blockIdx.z / a.nsplit, split = blockIdx.z % a.nsplit;
+  const int m0 = blockIdx.y * kConvBM;
+  const int tile_r = blockIdx.x / a.tiles_c, tile_c = blockIdx.x % a.tiles_c;
+  const int pr0 = tile_r * kConv6TR, pc0 = tile_c * TC;
+  const int H = a.H, W = a.W, Cin = a.Cin;
+  const int s0 = split * a.spl;
+  const int nslices = min(a.spl, Cin / kConvKC - s0);
+  const int nsteps = nslices * 3;
+
+  // Band staging map (as in the four-row kernel): lane vector u -> byte
+  // offset from its row's first pixel (beyond the resource outside the image
+  // and past the row) and the column part of its LDS slot.
+  const int prow = wave >> 2;  // row within a piece: 0..2
+  int b_off[RB_ITERS], b_col[RB_ITERS];
 #pragma unroll
-  for (int i = 0; i < kConvCG; ++i) {
-    const int c = wn * kConvCW + i * 16 + 4 * kg;
-    const int m = m0 + c;
-    float bv[4] = {0.f, 0.f, 0.f, 0.f};
-    if (a.bias && m < a.Cout) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) bv[e] = a.bias[m + e];
-    }
-#pragma unroll
-    for (int j = 0; j < TG; ++j) {
-      uint2 out;
-      out.x = pack_bf16x2(acc[i][j][0] + bv[0], acc[i][j][1] + bv[1]);
-      out.y = pack_bf16x2(acc[i][j][2] + bv[2], acc[i][j][3] + bv[3]);
-      tile[(wr * TC + j * 16 + pl) * kPixU2 + c / 4] = out;
-    }
+  for (int u = 0; u < RB_ITERS; ++u) {
+    const int id = (wave & 3) * kWave + lane + u * 256;
+    const int bc = id >> 3, slot = id & 7;
+    const int col = pc0 - 1 + bc;
+    b_off[u] = (id < ROW_VEC && col >= 0 && col < W) ? (col * Cin + slot * 8) * 2 : 0x7ffffff0;
+    b_col[u] = id < ROW_VEC ? bc * 8 + (slot ^ (bc & 7)) : -1;
   }
+  // source of this wave's row of piece pc (band row 3 pc + prow), or NULL
+  // above and below the image and for the missing third row of piece 2
+  auto band_row_src = [&](int pc) -> const uint16_t* {
+    const int br = 3 * pc + prow;
+    if (br >= kConv6Half) return nullptr;
+    const int r = pr0 - 1 + br;  // patch-relative
+    const int ir = a.row0 + r;   // image row
+    if (ir < 0 || ir >= H) return nullptr;
+    return (r >= 0 && r < a.rows) ? a.x + (static_cast<int64_t>(b) * a.rows + r) * W * Cin
+                                  : a.stale + (static_cast<int64_t>(b) * H + ir) * W * Cin;
+  };
+  const uint16_t* const row_src[3] = {band_row_src(0), band_row_src(1), band_row_src(2)};
+  // Weight staging map: vector u -> tap dx, output-channel row m and slot of
+  // the step's 3 x 64 x 64 block; rows past Cout read zero.
+  const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(a.w), 0, a.Cout * 9 * Cin * 2, kConvBufWord3);
+  int w_off[W_ITERS], w_dst[W_ITERS];
+#pragma unroll
+  for (int u = 0; u < W_ITERS; ++u) {
+    const int id = tid + u * kConv6Threads;
+    const int dx = id / (kConvBM * 8), r = id % (kConvBM * 8);
+    w_off[u] = ((m0 + (r >> 3)) * 9 * Cin + dx * Cin + (r & 7) * 8) * 2;
+    w_dst[u] = dx * (kConvBM * 8) + swz(r >> 3, r & 7);
+  }
+
+  uint4 band_ra[RB_ITERS], band_rb[RB_ITERS];
+  uint4 w_regA[W_ITERS], w_regB[W_ITERS];
+  auto load_piece = [&](uint4 (&reg)[RB_ITERS], int pc, int slice) {
+    const int c0 = (s0 + min(slice, nslices - 1)) * kConvKC;
+    const uint16_t* src = row_src[pc];
+    const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(src ? src + c0 : a.x), 0, src ? (W * Cin - c0) * 2 : 0, kConvBufWord3);
+#pragma unroll
+    for (int u = 0; u < RB_ITERS; ++u)
+      reg[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rb, b_off[u], 0, 0));
+  };
+  // piece pc of a slice into band half `half` (wave-uniform skip for the
+  // missing row of piece 2)
+  auto store_piece = [&](const uint4 (&reg)[RB_ITERS], int pc, int half) {
+    if (3 * pc + prow >= kConv6Half) return;
+    const int row_base = (half * kConv6Half + 3 * pc + prow) * ROW_VEC;
+#pragma unroll
+    for (int u = 0; u < RB_ITERS; ++u)
+      if (u + 1 < RB_ITERS || b_col[u] >= 0) band[row_base + b_col[u]] = reg[u];
+  };
+  auto load_w = [&](uint4 (&reg)[W_ITERS], int step) {
+    const int st = min(step, nsteps - 1);
+    const int sl = st / 3, dy = st - sl * 3;
+    const int soff = (dy * 3 * Cin + (s0 + sl) * kConvKC) * 2;
+#pragma unroll
+    for (int u = 0; u < W_ITERS; ++u)
+      reg[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rw, w_off[u] + soff, 0, 0));
+  };
+  auto store_w = [&](const uint4 (&reg)[W_ITERS], int buf) {
+#pragma unroll
+    for (int u = 0; u < W_ITERS; ++u) (&wts[buf][0][0])[w_dst[u]] = reg[u];
+  };
+
+  f32x4 acc[kConvCG][TG];
+#pragma unroll
+  for (int i = 0; i < kConvCG; ++i)
+#pragma unroll
+    for (int j = 0; j < TG; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int kg = lane >> 4, pl = lane & 15;
+  const int a_row0 = wn * kConvCW + pl;
+  const int a_slot[2] = {(0 + kg) ^ (pl & 7), (4 + kg) ^ (pl & 7)};
+  auto frag_load = [&](int dy, int wb, int half, int n, bf16x8 (&af)[kConvCG], bf16x8 (&bfr)[TG]) {
+    const int dx = n >> 1, ks = n & 1;
+    const int brow = half * kConv6Half + wr + dy;
+    const int col0 = dx + pl;
+    const int bslot = (ks * 4 + kg) ^ (col0 & 7);
+#pragma unroll
+    for (int i = 0; i < kConvCG; ++i)
+      af[i] = __builtin_bit_cast(bf16x8, wts[wb][dx][(a_row0 + 16 * i) * 8 + a_slot[ks]]);
+#pragma unroll
+    for (int j = 0; j < TG; ++j)
+      bfr[j] = __builtin_bit_cast(bf16x8, band[brow * ROW_VEC + (col0 + 16 * j) * 8 + bslot]);
+  };
+  auto mfma_batch = [&](const bf16x8 (&af)[kConvCG], const bf16x8 (&bfr)[TG]) {
+#pragma unroll
+    for (int i = 0; i < kConvCG; ++i)
+#pragma unroll
+      for (int j = 0; j < TG; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+  };
+  constexpr int kSgDsRead = 0x100, kSgMfma = 0x008;  // sched_group_barrier masks
+  auto compute = [&](int dy, int wb, int half) {
+    bf16x8 a0[kConvCG], b0[TG], a1[kConvCG], b1[TG];
+    frag_load(dy, wb, half, 0, a0, b0);
+    __builtin_amdgcn_sched_group_barrier(kSgDsRead, kConvCG + TG, 0);
+#pragma unroll
+    for (int n = 0; n < 6; n += 2) {
+      frag_load(dy, wb, half, n + 1, a1, b1);
+      mfma_batch(a0, b0);
+      __builtin_amdgcn_sched_group_barrier(kSgDsRead, kConvCG + TG, 0);
+      __builtin_amdgcn_sched_group_barrier(kSgMfma, kConvCG * TG, 0);
+      if (n + 2 < 6) frag_load(dy, wb, half, n + 2, a0, b0);
+      mfma_batch(a1, b1);
+      if (n + 2 < 6) __builtin_amdgcn_sched_group_barrier(kSgDsRead, kConvCG + TG, 0);
+      __builtin_amdgcn_sched_group_barrier(kSgMfma, kConvCG * TG, 0);
+    }
+  };
+  // Step st = 3 slice + dy (st & 1 == p): store piece dy of slice+1 (fetched
+  // two steps ago, in e at even and o at odd steps... passed as cur) into
+  // the other band half, fetch the piece stored two steps later, compute on
+  // weight buffer p and band half slice & 1, stage the weights of st+1 into
+  // the other weight buffer, barrier, fetch the weights of st+3.
+  auto slice_steps = [&](int slice, uint4 (&w0)[W_ITERS], uint4 (&w1)[W_ITERS], int p, uint4 (&e)[RB_ITERS],
+                         uint4 (&o)[RB_ITERS]) {
+    const int st = slice * 3;
+    const int half = slice & 1, nhalf = half ^ 1;
+    // dy = 0: store piece 0 of slice+1, fetch piece 2 of slice+1
+    store_piece(e, 0, nhalf);
+    load_piece(e, 2, slice + 1);
+    compute(0, p, half);
+    store_w(w0, p ^ 1);
+    __syncthreads();
+    load_w(w0, st + 3);
+    // dy = 1: store piece 1 of slice+1, fetch piece 0 of slice+2
+    store_piece(o, 1, nhalf);
+    load_piece(o, 0, slice + 2);
+    compute(1, p ^ 1, half);
+    store_w(w1, p);
+    __syncthreads();
+    load_w(w1, st + 4);
+    // dy = 2: store piece 2 of slice+1, fetch piece 1 of slice+2
+    store_piece(e, 2, nhalf);
+    load_piece(e, 1, slice + 2);
+    compute(2, p, half);
+    store_w(w0, p ^ 1);
+    __syncthreads();
+    load_w(w0, st + 5);
+  };
+
+  // prologue: slice 0's band in half 0 and the weights of step 0 staged;
+  // pieces 0 and 1 of slice 1 and the weights of steps 1 and 2 in registers
+  load_piece(band_ra, 0, 0);
+  load_piece(band_rb, 1, 0);
+  load_w(w_regB, 0);
+  store_piece(band_ra, 0, 0);
+  store_piece(band_rb, 1, 0);
+  store_w(w_regB, 0);
+  load_piece(band_ra, 2, 0);
+  store_piece(band_ra, 2, 0);
+  load_piece(band_ra, 0, 1);  // stored at step 0
+  load_piece(band_rb, 1, 1);  // stored at step 1
+  load_w(w_regA, 1);
+  load_w(w_regB, 2);
   __syncthreads();
-  constexpr int kChunks = kConvTR * TC * (kConvBM / 4);  // 8-byte chunks of the tile
-  static_assert(kChunks % kConvThreads == 0, "whole chunks per thread");
-#pragma unroll
-  for (int u = 0; u < kChunks / kConvThreads; ++u) {
-    const int id = tid + u * kConvThreads;
-    const int pix = id / (kConvBM / 4), q = id % (kConvBM / 4);
-    const int row = pr0 + pix / TC, col = pc0 + pix % TC, m = m0 + 4 * q;
-    if (row < a.rows && col < W && m < a.Cout)
-      *reinterpret_cast<uint2*>(a.y + ((static_cast<int64_t>(b) * a.rows + row) * W + col) * a.Cout + m) =
-          tile[pix * kPixU2 + q];
+  int slice = 0;
+  for (; slice + 1 < nslices; slice += 2) {
+    slice_steps(slice, w_regA, w_regB, 0, band_ra, band_rb);
+    slice_steps(slice + 1, w_regB, w_regA, 1, band_rb, band_ra);
   }
-  if (a.gn_part != nullptr) {
-    // GroupNorm partial sums of this tile's stored values, one chunk per
-    // workgroup (chunk = channel tile * pixel tiles + pixel tile); the LDS
-    // past the staged tile is the scratch
-    const int64_t nchunk = static_cast<int64_t>(gridDim.x) * gridDim.y;
-    const int64_t chunk = static_cast<int64_t>(blockIdx.y) * gridDim.x + blockIdx.x;
-    float* out = a.gn_part + (static_cast<int64_t>(b) * nchunk + chunk) * a.G * 2;
-    tile_group_sums<kConvThreads, kConvTR * TC, kConvBM>(
-        reinterpret_cast<const uint16_t*>(tile), 4 * kPixU2,
-        [&](int p) { return pr0 + p / TC < a.rows && pc0 + p % TC < W; }, m0, a.Cout, a.Cout / a.G, a.G,
-        reinterpret_cast<float*>(tile + kTileU2), out);
-  }
+  if (slice < nslices) slice_steps(slice, w_regA, w_regB, 0, band_ra, band_rb);
+
+  // -------- epilogue (the slice loop ended with a barrier)
+  static_assert(conv_epilogue_bytes<kConv6TR, TG, kConv6Threads>() <= sizeof(band),
+                "staged tile and statistics scratch fit in the band");
+  conv_epilogue<kConv6TR, TG, kConv6Threads>(a, acc, reinterpret_cast<uint2*>(&band[0]), b, split, m0, pr0 + wr, pc0,
+                                             wn * kConvCW, pr0);
 }
 
 // Split-K reduction: y = bf16(bias + sum over splits of the float32 partials),
@@ -480,8 +723,27 @@ static ConvSplit conv_split(int64_t B, int64_t rows, int64_t W, int64_t Cin, int
   return best;
 }
 
+// Six-row tiles (48 columns) where they cover the band exactly and take fewer
+// pixel-rounds than the four-row tiles: ceil(workgroups / 256) rounds of the
+// tile's pixels, the six-row tile's pixels counted at 0.9 for its third wave
+// per SIMD (an LDS-fed MFMA probe with the conv's fragment ratios: 74 % of the
+// matrix pipe busy against 67 %).  Depends on the shape of one batch entry
+// only, so that the GroupNorm chunk count does too.  (The 30 x 240 band:
+// 250 six-row tiles against 240 four-row ones, the last row of those half
+// empty.)
+static int64_t conv_tiles6(int64_t rows, int64_t W, int64_t Cout) {
+  return rows / kConv6TR * (W / 48) * ceil_div(Cout, kConvBM);
+}
+
+static bool conv_six_rows(int64_t rows, int64_t W, int64_t Cout) {
+  if (rows % kConv6TR != 0 || W % 48 != 0) return false;
+  const double cost4 = static_cast<double>(ceil_div(conv_tiles(rows, W, Cout), 256) * kConvTR * 16 * conv_pick_tg(W));
+  const double cost6 = 0.9 * static_cast<double>(ceil_div(conv_tiles6(rows, W, Cout), 256) * kConv6TR * 48);
+  return cost6 < cost4;
+}
+
 int64_t conv_gn_chunks(int64_t rows, int64_t W, int64_t Cout) {
-  return conv_tiles(rows, W, Cout);
+  return conv_six_rows(rows, W, Cout) ? conv_tiles6(rows, W, Cout) : conv_tiles(rows, W, Cout);
 }
 
 size_t conv_workspace_bytes(int64_t B, int64_t rows, int64_t W, int64_t Cin, int64_t Cout) {
@@ -525,6 +787,13 @@ hipError_t launch_conv3x3(void* y, const void* x, const void* stale_full, const 
   a.nsplit = sp.nsplit;
   a.spl = sp.spl;
   a.part = sp.nsplit > 1 ? static_cast<float*>(ws) : nullptr;
+  if (sp.nsplit == 1 && conv_six_rows(rows, W, Cout)) {
+    a.tiles_c = static_cast<int>(W / 48);
+    const dim3 grid6(static_cast<unsigned>(conv_tiles6(rows, W, Cout) / ceil_div(Cout, kConvBM)),
+                     static_cast<unsigned>(ceil_div(Cout, kConvBM)), static_cast<unsigned>(B));
+    hipLaunchKernelGGL(conv3x3_bf16_mfma6_kernel<3>, grid6, dim3(kConv6Threads), 0, s, a);
+    return hipGetLastError();
+  }
   dim3 grid(static_cast<unsigned>(tiles), static_cast<unsigned>(ceil_div(Cout, kConvBM)),
             static_cast<unsigned>(B * sp.nsplit));
   switch (tg) {

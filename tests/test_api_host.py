@@ -365,7 +365,10 @@ def test_groupnorm_noalloc_validation():
 
 def test_producer_statistics_and_presummed_validation():
     # conv with GroupNorm partials: the conv's own checks, then its own
-    assert L.dpp_conv3x3_halo_gn_chunks(30, 240, 640) == 240          # 8 four-row tiles x 3 column tiles x 10 channel tiles
+    assert L.dpp_conv3x3_halo_gn_chunks(30, 240, 640) == 250          # 5 six-row tiles x 5 48-column tiles x 10 channel tiles
+    assert L.dpp_conv3x3_halo_gn_chunks(240, 240, 640) == 2000        # six-row tiles: 40 x 5 x 10 (8 rounds of 288 px)
+    assert L.dpp_conv3x3_halo_gn_chunks(6, 48, 64) == 2               # six rows fit, but two four-row tiles finish first
+    assert L.dpp_conv3x3_halo_gn_chunks(28, 240, 640) == 210          # 7 four-row tiles x 3 x 10
     assert L.dpp_conv3x3_halo_gn_chunks(16, 64, 320) == 20            # 4 x 1 x 5
     assert L.dpp_linear_gn_chunks(1, 7200, 640) == 225                 # 45 token tiles x 5 channel tiles
     assert L.dpp_linear_gn_chunks(1, 7200, 1280) == 225                # 256-channel tiles: 45 x 5

@@ -50,26 +50,28 @@ def _check_partials(part, y_vals, G, chunk_groups, what):
         assert np.all(part[:, c, others] == 0.0), f"{what}: chunk {c} wrote groups it does not touch"
 
 
-def _conv_pixel_tiles(rows, W, tr):
-    """Pixel tiles of the conv: tr patch rows x 16 tg columns, tg (1..5) the
-    width that wastes the fewest columns, ties to the wider tile."""
+def _conv_pixel_tiles(rows, W):
+    """Pixel tiles of the conv: four patch rows x 16 tg columns, tg (1..5) the
+    width that wastes the fewest columns, ties to the wider tile; or six rows
+    x 48 columns where those cover the band exactly."""
     tg = min(range(1, 6), key=lambda t: (-(-W // (16 * t)) * 16 * t - W, -t))
-    return -(-rows // tr) * -(-W // (16 * tg))
+    four = -(-rows // 4) * -(-W // (16 * tg))
+    six = rows // 6 * (W // 48) if rows % 6 == 0 and W % 48 == 0 else None
+    return four, six
 
 
 def _conv_chunk_groups(nchunk, rows, W, Cout, G):
-    """Conv chunks are (channel tile) * pixel tiles + pixel tile; a tile is
-    four patch rows x 64 channels or two rows x 128 channels: the one whose
-    chunk count the call reports."""
-    shapes = [bm for bm in (64, 128) if -(-Cout // bm) * _conv_pixel_tiles(rows, W, 256 // bm) == nchunk]
-    assert shapes, f"no tile shape gives {nchunk} chunks"
-    bm = shapes[0]
-    ptiles = nchunk // -(-Cout // bm)
+    """Conv chunks are (channel tile) * pixel tiles + pixel tile, with
+    64-channel tiles and one of the two pixel tilings: the one whose chunk
+    count the call reports."""
+    ctiles = -(-Cout // 64)
+    assert nchunk in [ctiles * t for t in _conv_pixel_tiles(rows, W) if t], f"no tiling gives {nchunk} chunks"
+    ptiles = nchunk // ctiles
     cg = Cout // G
     out = []
     for c in range(nchunk):
         ct = c // ptiles
-        lo, hi = ct * bm, min(Cout, ct * bm + bm)
+        lo, hi = ct * 64, min(Cout, ct * 64 + 64)
         out.append(set(range(lo // cg, (hi - 1) // cg + 1)))
     return out
 
@@ -82,6 +84,7 @@ CONV_CASES = [
     (Config("gs_w37", B=2, H=12, W=37, C=192, P=4, G=8, heads=3, D=64), 2, 32),
     (Config("gs_g1", B=1, H=9, W=20, C=128, P=3, G=1, heads=2, D=64), 0, 1),
     (Config("gs_gc", B=1, H=6, W=19, C=64, P=2, G=64, heads=1, D=64), 1, 64),
+    (Config("gs_r6", B=1, H=24, W=240, C=128, P=2, G=16, heads=2, D=64), 1, 16),   # six-row tiles
 ]
 
 
@@ -249,7 +252,7 @@ def test_groupnorm_presummed_matches_plain_groupnorm():
                 to_dev(inp["conv_w"], "bf16"))
     b = torch.from_numpy(inp["conv_b"]).cuda()
     nchunk = dpp.dpp_conv3x3_halo_gn_chunks(cfg.rows, cfg.W, cfg.C)
-    assert nchunk == 240  # 8 four-row tiles x 3 column tiles x 10 channel tiles
+    assert nchunk == 250  # 5 six-row tiles x 5 48-column tiles x 10 channel tiles
     part = torch.empty(cfg.B, nchunk, cfg.G, 2, device="cuda")
     h = torch.empty(cfg.B, cfg.rows, cfg.W, cfg.C, dtype=torch.bfloat16, device="cuda")
     dpp.dpp_conv3x3_halo_gn(h, part, x, st, w, b, cfg.H, r0)

@@ -268,6 +268,35 @@ def test_conv_ragged_cout(B, H, W, Cin, Cout, r0, R):
     parity(to_host(y), want, "bf16", "conv ragged cout")
 
 
+@pytest.mark.parametrize("B,H,W,Cin,Cout,r0,R", [
+    (1, 12, 240, 64, 80, 6, 6),     # one input slice, bottom patch: stale halo above, image edge below, 2 Cout tiles
+    (2, 18, 240, 192, 64, 6, 6),    # three slices (odd), stale halo rows on both sides, two batch entries
+    (1, 12, 240, 128, 272, 0, 12),  # whole image, two row tiles, five Cout tiles (the last 16 wide)
+    (1, 6, 240, 320, 64, 0, 6),     # five slices, one row tile
+])
+def test_conv_six_row_tiles(B, H, W, Cin, Cout, r0, R):
+    # 240-wide bands whose rows are a multiple of six run the six-row x
+    # 48-column tile kernel (twelve waves, double-buffered band)
+    dpp = _dpp()
+    from displaced_patch_parallelism_net_amd import _lib as L
+    assert L.dpp_conv3x3_halo_gn_chunks(R, W, Cout) == R // 6 * (W // 48) * -(-Cout // 64), "six-row tiling expected"
+    rng = np.random.default_rng(13)
+    say("conv six-row tiles", B, H, W, Cin, Cout, r0, R)
+    from dpp_synth import f32_to_bf16_bits
+    xs = f32_to_bf16_bits(rng.standard_normal((B, H, W, Cin)).astype(np.float32))
+    xp = f32_to_bf16_bits(rng.standard_normal((B, R, W, Cin)).astype(np.float32))
+    wt = f32_to_bf16_bits((0.05 * rng.standard_normal((Cout, 3, 3, Cin))).astype(np.float32))
+    bias = (0.1 * rng.standard_normal(Cout)).astype(np.float32)
+    whole = r0 == 0 and R == H
+    ybase, y = guarded_empty((B, R, W, Cout), torch.bfloat16)
+    dpp.dpp_conv3x3_halo(y, to_dev(xp, "bf16"), None if whole else to_dev(xs, "bf16"), to_dev(wt, "bf16"),
+                         torch.from_numpy(bias).cuda(), H, r0)
+    torch.cuda.synchronize()
+    check_guards(ybase, "conv six-row tiles")
+    want = oracle.conv3x3_halo(values("bf16", xp), None if whole else values("bf16", xs), values("bf16", wt), bias, r0)
+    parity(to_host(y), want, "bf16", "conv six-row tiles")
+
+
 @pytest.mark.parametrize("name,p", [("sdxl_1024", 1), ("sdxl_2048", 3), ("cfg_pair_1024", 2)])
 def test_conv_split_k_parity(name, p):
     # small patches split the input channels across workgroups (float32

@@ -98,6 +98,7 @@ def check(got_bits, exact, what, need_near=True):
     (1, 6, 40, 64, 2, 2, False),         # patch with both halo rows, one workgroup
     (2, 5, 37, 128, 0, 5, False),        # whole image, ragged width
     (1, 64, 64, 640, 16, 16, True),      # the 1024 px band: input channels split 5 ways
+    (1, 18, 240, 128, 6, 6, False),      # six-row x 48-column tiles (the kernel of the 240-wide bands)
 ])
 def test_conv_unit_weight_rounds_to_nearest_even(B, H, W, C, row0, rows, split):
     import displaced_patch_parallelism_net_amd as dpp
