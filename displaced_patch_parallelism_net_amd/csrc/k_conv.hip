@@ -108,7 +108,7 @@ struct ConvArgs {
   int tiles_c;  // column tiles per row band
   int nsplit;   // input-channel splits (blockIdx.z = b * nsplit + split)
   int spl;      // 64-channel slices per split
-  float* gn_part;  // GroupNorm partial sums of y [B][gridDim.x * gridDim.y][G][2], or NULL (unsplit only)
+  float* gn_part;  // GroupNorm partial sums of y [B][conv_gn_chunks][G][2], or NULL (unsplit only)
   int G;
 };
 
@@ -127,8 +127,9 @@ __device__ __forceinline__ int swz(int row, int slot) { return row * 8 + (slot ^
 // staged in LDS at `tile` ([pixel][channel]; pixels padded by 16 bytes, so
 // that the 16 pixels of a tile write fall on distinct banks), then stored so
 // that each wave store writes whole 128-byte pixels instead of 32-byte pieces
-// of 16 pixels; with a.gn_part the tile's GroupNorm partial sums follow, the
-// LDS past the staged tile being their scratch.
+// of 16 pixels; with a.gn_part the tile's GroupNorm partial sums follow as
+// chunk `chunk` of `nchunk` per batch entry, the LDS past the staged tile
+// being their scratch.
 constexpr int kConvPixU2 = kConvBM / 4 + 2;  // uint2 per padded LDS pixel
 
 template <int TR, int TG, int NT>
@@ -138,7 +139,8 @@ constexpr size_t conv_epilogue_bytes() {
 
 template <int TR, int TG, int NT>
 __device__ __forceinline__ void conv_epilogue(const ConvArgs& a, const f32x4 (&acc)[kConvCG][TG], uint2* tile, int b,
-                                              int split, int m0, int row, int pc0, int cw0, int pr0) {
+                                              int split, int m0, int row, int pc0, int cw0, int pr0, int64_t chunk,
+                                              int64_t nchunk) {
   constexpr int TC = 16 * TG;
   constexpr int kTileU2 = TR * TC * kConvPixU2;
   const int tid = threadIdx.x, lane = tid % kWave;
@@ -193,9 +195,7 @@ __device__ __forceinline__ void conv_epilogue(const ConvArgs& a, const f32x4 (&a
   }
   if (a.gn_part != nullptr) {
     // GroupNorm partial sums of this tile's stored values, one chunk per
-    // workgroup (chunk = channel tile * pixel tiles + pixel tile)
-    const int64_t nchunk = static_cast<int64_t>(gridDim.x) * gridDim.y;
-    const int64_t chunk = static_cast<int64_t>(blockIdx.y) * gridDim.x + blockIdx.x;
+    // tile (chunk = channel tile * pixel tiles + pixel tile)
     float* out = a.gn_part + (static_cast<int64_t>(b) * nchunk + chunk) * a.G * 2;
     tile_group_sums<NT, TR * TC, kConvBM>(
         reinterpret_cast<const uint16_t*>(tile), 4 * kConvPixU2,
@@ -423,7 +423,9 @@ __global__ __launch_bounds__(kConvThreads, 1) void conv3x3_bf16_mfma_kernel(Conv
   static_assert(conv_epilogue_bytes<kConvTR, TG, kConvThreads>() <= (kTileInBand ? sizeof(band) : sizeof(wts)),
                 "staged tile and statistics scratch fit");
   uint2* const tile = kTileInBand ? reinterpret_cast<uint2*>(&band[0]) : reinterpret_cast<uint2*>(&wts[0][0][0]);
-  conv_epilogue<kConvTR, TG, kConvThreads>(a, acc, tile, b, split, m0, pr0 + wr, pc0, wn * kConvCW, pr0);
+  conv_epilogue<kConvTR, TG, kConvThreads>(a, acc, tile, b, split, m0, pr0 + wr, pc0, wn * kConvCW, pr0,
+                                           static_cast<int64_t>(blockIdx.y) * gridDim.x + blockIdx.x,
+                                           static_cast<int64_t>(gridDim.x) * gridDim.y);
 }
 
 // Six-row tile: 6 patch rows x 16*TG columns x 64 output channels, twelve
@@ -462,12 +464,21 @@ __global__ __launch_bounds__(kConv6Threads, 1) void conv3x3_bf16_mfma6_kernel(Co
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave), lane = tid % kWave;
   const int wr = wave / kConvWN, wn = wave % kConvWN;
-  const int b = blockIdx.z / a.nsplit, split = blockIdx.z % a.nsplit;
-  const int m0 = blockIdx.y * kConvBM;
-  const int tile_r = blockIdx.x / a.tiles_c, tile_c = blockIdx.x % a.tiles_c;
+  // 1-D grid over (b, pixel tile, channel tile).  Workgroup ids are dealt
+  // round-robin to the 8 XCDs; each XCD takes a contiguous range of tiles,
+  // channel tile fastest, so the channel tiles of a pixel tile (which read
+  // the same band rows) share an L2.
+  const int nct = (a.Cout + kConvBM - 1) / kConvBM;
+  const int npt = a.tiles_c * (a.rows / kConv6TR);
+  const int ntot = gridDim.x, xcd = blockIdx.x % 8, per = ntot / 8, rem = ntot % 8;
+  const int logical = xcd * per + min(xcd, rem) + static_cast<int>(blockIdx.x) / 8;
+  const int b = logical / (npt * nct), split = 0;
+  const int ptile = logical % (npt * nct) / nct, ctile = logical % nct;
+  const int m0 = ctile * kConvBM;
+  const int tile_r = ptile / a.tiles_c, tile_c = ptile % a.tiles_c;
   const int pr0 = tile_r * kConv6TR, pc0 = tile_c * TC;
   const int H = a.H, W = a.W, Cin = a.Cin;
-  const int s0 = split * a.spl;
+  const int s0 = 0;
   const int nslices = min(a.spl, Cin / kConvKC - s0);
   const int nsteps = nslices * 3;
 
@@ -645,7 +656,8 @@ __global__ __launch_bounds__(kConv6Threads, 1) void conv3x3_bf16_mfma6_kernel(Co
   static_assert(conv_epilogue_bytes<kConv6TR, TG, kConv6Threads>() <= sizeof(band),
                 "staged tile and statistics scratch fit in the band");
   conv_epilogue<kConv6TR, TG, kConv6Threads>(a, acc, reinterpret_cast<uint2*>(&band[0]), b, split, m0, pr0 + wr, pc0,
-                                             wn * kConvCW, pr0);
+                                             wn * kConvCW, pr0, static_cast<int64_t>(ctile) * npt + ptile,
+                                             static_cast<int64_t>(npt) * nct);
 }
 
 // Split-K reduction: y = bf16(bias + sum over splits of the float32 partials),
@@ -789,9 +801,8 @@ hipError_t launch_conv3x3(void* y, const void* x, const void* stale_full, const 
   a.part = sp.nsplit > 1 ? static_cast<float*>(ws) : nullptr;
   if (sp.nsplit == 1 && conv_six_rows(rows, W, Cout)) {
     a.tiles_c = static_cast<int>(W / 48);
-    const dim3 grid6(static_cast<unsigned>(conv_tiles6(rows, W, Cout) / ceil_div(Cout, kConvBM)),
-                     static_cast<unsigned>(ceil_div(Cout, kConvBM)), static_cast<unsigned>(B));
-    hipLaunchKernelGGL(conv3x3_bf16_mfma6_kernel<3>, grid6, dim3(kConv6Threads), 0, s, a);
+    hipLaunchKernelGGL(conv3x3_bf16_mfma6_kernel<3>, dim3(static_cast<unsigned>(B * conv_tiles6(rows, W, Cout))),
+                       dim3(kConv6Threads), 0, s, a);
     return hipGetLastError();
   }
   dim3 grid(static_cast<unsigned>(tiles), static_cast<unsigned>(ceil_div(Cout, kConvBM)),
