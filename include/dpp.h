@@ -148,8 +148,10 @@ int dpp_groupnorm_silu_stale(void* y, float* stats_out, const void* x,
  *   partials [B,nchunk,G,2] float32: per chunk and group (sum y, sum y^2) of
  *            the stored output values over the chunk's pixels and the
  *            group's channels (zero where the chunk does not touch it).
- * This call adds the chunks in float64, in chunk order, as the fresh sums s1,
- * s2 of dpp_groupnorm_stale, and continues exactly as that call (stale
+ * This call adds the chunks in float64 in one fixed order (64 lanes, lane j
+ * adding chunks j, j+64, j+128, ... in increasing order, then the 64 lane
+ * sums pairwise at offsets 32, 16, ..., 1) as the fresh sums s1, s2 of
+ * dpp_groupnorm_stale, and continues exactly as that call (stale
  * correction, mean/var, normalisation, stats_out[b,p] = the fresh sums);
  * silu != 0 applies SiLU to the result as dpp_groupnorm_silu_stale does.
  *   x, y [B,rows,W,C] as dpp_groupnorm_stale (y == NULL: stats_out only);
