@@ -598,10 +598,11 @@ __global__ __launch_bounds__(kConv6Threads, 1) void conv3x3_bf16_mfma6_kernel(Co
       __builtin_amdgcn_sched_group_barrier(kSgMfma, kConvCG * TG, 0);
     }
   };
-  // Step st = 3 slice + dy (st & 1 == p): store piece dy of slice+1 (fetched
-  // two steps ago, in e at even and o at odd steps... passed as cur) into
-  // the other band half, fetch the piece stored two steps later, compute on
-  // weight buffer p and band half slice & 1, stage the weights of st+1 into
+  // Step st = 3 slice + dy: store piece dy of slice+1 (fetched two steps
+  // earlier) into the other band half and fetch the piece stored two steps
+  // later into the same registers (e at the slice's dy = 0 and 2, o at
+  // dy = 1; the caller swaps e and o for odd slices), compute on weight
+  // buffer st & 1 and band half slice & 1, stage the weights of st+1 into
   // the other weight buffer, barrier, fetch the weights of st+3.
   auto slice_steps = [&](int slice, uint4 (&w0)[W_ITERS], uint4 (&w1)[W_ITERS], int p, uint4 (&e)[RB_ITERS],
                          uint4 (&o)[RB_ITERS]) {
