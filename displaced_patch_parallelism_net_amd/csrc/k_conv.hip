@@ -8,18 +8,20 @@
 //
 // bf16 path: implicit GEMM on MFMA.  M = output channels (A = weights,
 // [Cout][tap][Cin] rows are K-contiguous), N = output pixels (B = input
-// pixels, channel-contiguous in NHWC), K = 9 taps x Cin.  A workgroup owns 4
-// patch rows x 16*TG columns x 64 output channels (TG chosen per width so
-// the tiles cover the rows exactly where possible: 240 columns -> 3 tiles of
-// 80; the 30-row band of a 240 x 240 image in 8 patches -> 240 workgroups,
-// one per CU).  For each 64-channel slice of Cin the halo band (6 rows x
-// 16*TG+2 columns, halo rows from the stale image) is staged once in LDS and
-// reused by all nine taps; one barrier step covers the three taps of one
-// kernel row, whose weights are double-buffered in LDS and fetched two steps
-// ahead into registers.  Eight waves (two per SIMD) each compute 32 channels
-// x 16*TG pixels of one tile row with v_mfma_f32_16x16x32_bf16; the
-// accumulator's lane layout gives each lane four consecutive output channels
-// of one pixel.
+// pixels, channel-contiguous in NHWC), K = 9 taps x Cin.  Two tile kernels
+// share the K loop's structure and the epilogue.  The four-row kernel's
+// workgroup owns 4 patch rows x 16*TG columns x 64 output channels (TG
+// chosen per width so the tiles cover the rows exactly where possible: 240
+// columns -> 3 tiles of 80), eight waves (two per SIMD) each computing 32
+// channels x 16*TG pixels of one tile row.  The six-row kernel's workgroup
+// owns 6 rows x 48 columns x 64 channels with twelve waves (three per SIMD);
+// it covers the 30-row band of a 240 x 240 image in 8 patches exactly (250
+// workgroups, one per CU).  For each 64-channel slice of Cin the halo band
+// (halo rows from the stale image) is staged once in LDS and reused by all
+// nine taps; one barrier step covers the three taps of one kernel row,
+// whose weights are double-buffered in LDS and fetched two steps ahead into
+// registers.  MFMA v_mfma_f32_16x16x32_bf16; the accumulator's lane layout
+// gives each lane four consecutive output channels of one pixel.
 //
 // f32 path: one thread per output element, direct loops (small shapes).
 #include "dpp_common.h"
@@ -712,7 +714,7 @@ struct ConvSplit {
 // launch.  Gains under 10% go to fewer splits.  In a forced-split sweep on
 // MI355X (seven bands of 8-240 rows, 64-240 px wide, 320 and 640 channels)
 // the model picks the measured fastest count at six shapes and one within 4 %:
-// 240 x 240 image, 30-row band, 240 workgroups -> no split; 15-row band, 120
+// 240 x 240 image, 30-row band, 240 four-row workgroups -> no split; 15-row band, 120
 // -> 2 (42 -> 35 us); 64 x 64 image, 8-row band, 20 -> 10 (36 -> 19 us;
 // 5 splits: 18 us); full images never split.
 static ConvSplit conv_split(int64_t B, int64_t rows, int64_t W, int64_t Cin, int64_t Cout) {
